@@ -1,0 +1,258 @@
+"""CPU oracle for PagedAttention decode (test infrastructure).
+
+This module is test infrastructure. Only ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` may import it; the product path
+never does. It shares no code with the HIP library and imports nothing from
+the ``paged_kv_cache_220_amd`` package: it takes plain NumPy arrays holding
+the exact storage bits the GPU receives.
+
+What is computed (all in float64):
+
+  For every sequence s and query head h, with L = seq_lens[s] and
+  kv head g = h // (num_heads // num_kv_heads):
+      token t (0 <= t < L) lives in physical block block_tables[s, t // bs]
+      at slot t % bs;  K_t = K_cache[block, g, :, slot],  V_t likewise;
+      out[s, h] = sum_t softmax_t(scale * q[s,h] . K_t) * V_t ,
+  and out[s, h] = 0 when L == 0.
+
+Sources on the pages:
+  * "vLLM e PagedAttention: serving high-throughput", PagedAttention kernel
+    pseudocode: the argument layouts (Q [seqs, heads, head_dim];
+    K/V cache [blocks, heads, head_dim, block_size]; block_tables
+    [seqs, max_blocks]; seq_lens), the loop over ceil(seq_len / block_size)
+    logical blocks through the block table, the score q . K_block / sqrt(d),
+    and the online-softmax update (running max m, running sum l, rescaled o)
+    ending in output = o / l.
+  * "Optimização da inferência", step 2 (attention with the KV cache): the
+    dense max-subtracted softmax attention; with one query row no mask applies.
+  * Same page, "PagedAttention": logical sequence positions map through a page
+    table to fixed-size pages anywhere in memory; pages of a shared prefix are
+    stored once and referenced by many requests.
+  * Same page, "Caches de KV": the cache is sized by the number of KV heads
+    (grouped-query attention: 64 query heads share 8 KV heads for Llama 3 70B).
+  * "Continuous Batching e PagedAttention no vLLM", section 3: physical blocks
+    need not be consecutive, and the last block may be partly unused.
+  * The fp8-e5m2 KV option appears only as the flag name ``fp8_e5m2`` on the
+    vLLM page; its decoding follows the OCP 8-bit floating point format
+    (1 sign, 5 exponent bits with bias 15, 2 mantissa bits, IEEE-style
+    subnormals, infinities and NaNs).
+
+Readings where the pages are silent (each is also listed with the design notes):
+  * tail slots of the last block (t >= L) do not exist and take no part in
+    the softmax or in P.V; the pseudocode's whole-block sums are read this way;
+  * query head h uses KV head h // G (consecutive query heads share a KV head);
+  * the scale is an argument (the pages fix 1/sqrt(head_dim)); the oracle uses
+    the float32 value the GPU receives, widened to float64;
+  * L == 0 gives a zero output row;
+  * fp8 values are checked against the stored bytes decoded exactly, times the
+    per-tensor scales k_scale / v_scale.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "decode_bits", "e5m2_value", "logical_kv", "paged_decode", "paged_decode_rows",
+    "online_decode", "merge_partials", "dense_attention",
+]
+
+
+# ----------------------------------------------------------------------------
+# storage decoding (exact)
+# ----------------------------------------------------------------------------
+
+def e5m2_value(code: int) -> float:
+    """Exact value of one OCP E5M2 byte from its bit fields."""
+    sign = -1.0 if (code >> 7) & 1 else 1.0
+    exp = (code >> 2) & 0x1F
+    man = code & 0x3
+    if exp == 0x1F:
+        return sign * math.inf if man == 0 else math.nan
+    if exp == 0:
+        return sign * (man / 4.0) * 2.0 ** (1 - 15)
+    return sign * (1.0 + man / 4.0) * 2.0 ** (exp - 15)
+
+
+_E5M2_TABLE = np.array([e5m2_value(c) for c in range(256)], dtype=np.float64)
+
+
+def decode_bits(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Storage bits -> float64 values, exactly."""
+    if dtype == "f32":
+        return np.asarray(bits, dtype=np.float32).astype(np.float64)
+    if dtype == "bf16":
+        b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+        with np.errstate(invalid="ignore"):
+            return b.view(np.float32).astype(np.float64)
+    if dtype == "e5m2":
+        return _E5M2_TABLE[np.asarray(bits, dtype=np.uint8)]
+    raise ValueError(dtype)
+
+
+# ----------------------------------------------------------------------------
+# logical reassembly through the block table
+# ----------------------------------------------------------------------------
+
+def logical_kv(cache_bits: np.ndarray, block_tables: np.ndarray, s: int, L: int, kvh: int,
+               dtype: str, elem_scale: float = 1.0) -> np.ndarray:
+    """K or V of sequence s, KV head kvh, in logical token order: float64 [L, D].
+
+    Token t is read from physical block block_tables[s, t // bs], slot t % bs.
+    Only the ceil(L / bs) table entries that hold tokens are read.
+    """
+    bs = cache_bits.shape[3]
+    D = cache_bits.shape[2]
+    if L == 0:
+        return np.zeros((0, D), dtype=np.float64)
+    nblk = (L + bs - 1) // bs
+    ids = np.asarray(block_tables[s, :nblk], dtype=np.int64)
+    tiles = cache_bits[ids, kvh]                      # [nblk, D, bs]
+    tokens = np.transpose(tiles, (0, 2, 1)).reshape(nblk * bs, D)[:L]
+    out = decode_bits(tokens, dtype)
+    if elem_scale != 1.0:
+        out = out * float(elem_scale)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# plain definition: two-pass softmax attention over the reassembled sequence
+# ----------------------------------------------------------------------------
+
+def dense_attention(qv: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+    """One query row against L keys/values: max-subtracted softmax, then weights @ V."""
+    L = K.shape[0]
+    if L == 0:
+        return np.zeros(V.shape[1], dtype=np.float64)
+    sc = scale * (K @ qv)
+    w = np.exp(sc - np.max(sc))
+    return (w @ V) / np.sum(w)
+
+
+def _check_shapes(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads):
+    S, H, D = q.shape
+    if H % num_kv_heads:
+        raise ValueError("num_heads must be a multiple of num_kv_heads")
+    if k_cache.shape != v_cache.shape or k_cache.shape[1] != num_kv_heads or k_cache.shape[2] != D:
+        raise ValueError("cache shape mismatch")
+    if block_tables.shape[0] != S or len(seq_lens) != S:
+        raise ValueError("table / seq_lens shape mismatch")
+    return S, H, D, H // num_kv_heads
+
+
+def paged_decode_rows(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale,
+                      q_dtype: str, kv_dtype: str, rows: Iterable[Tuple[int, int]],
+                      k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
+    """out[s, h, :] for the listed (s, h) pairs only: float64 [len(rows), D]."""
+    S, H, D, G = _check_shapes(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads)
+    sc64 = float(np.float32(scale))
+    rows = list(rows)
+    out = np.zeros((len(rows), D), dtype=np.float64)
+    cache = {}
+    for i, (s, h) in enumerate(rows):
+        g = h // G
+        key = (s, g)
+        if key not in cache:
+            cache.clear()
+            L = int(seq_lens[s])
+            cache[key] = (logical_kv(k_cache, block_tables, s, L, g, kv_dtype, k_scale),
+                          logical_kv(v_cache, block_tables, s, L, g, kv_dtype, v_scale))
+        K, V = cache[key]
+        out[i] = dense_attention(decode_bits(q[s, h], q_dtype), K, V, sc64)
+    return out
+
+
+def paged_decode(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale,
+                 q_dtype: str, kv_dtype: str, k_scale: float = 1.0, v_scale: float = 1.0,
+                 seqs: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Full output float64 [S, H, D] (rows of sequences not in `seqs` stay zero).
+
+    All query heads of one KV head are done together: scores [G, L] = q_g @ K^T.
+    """
+    S, H, D, G = _check_shapes(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads)
+    sc64 = float(np.float32(scale))
+    out = np.zeros((S, H, D), dtype=np.float64)
+    for s in (range(S) if seqs is None else seqs):
+        L = int(seq_lens[s])
+        if L == 0:
+            continue
+        for g in range(num_kv_heads):
+            K = logical_kv(k_cache, block_tables, s, L, g, kv_dtype, k_scale)
+            V = logical_kv(v_cache, block_tables, s, L, g, kv_dtype, v_scale)
+            qg = decode_bits(q[s, g * G:(g + 1) * G], q_dtype)          # [G, D]
+            sc = sc64 * (qg @ K.T)                                        # [G, L]
+            w = np.exp(sc - sc.max(axis=1, keepdims=True))
+            out[s, g * G:(g + 1) * G] = (w @ V) / w.sum(axis=1, keepdims=True)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# second implementation: the pages' block-by-block online softmax
+# ----------------------------------------------------------------------------
+
+def _online_partition(qv, k_cache, v_cache, table_row, L, g, first_block, last_block, bs,
+                      kv_dtype, scale, k_scale, v_scale):
+    """Online softmax over logical blocks [first_block, last_block) of one sequence.
+
+    Per block: scores = scale * q . K_block; m_new = max(m, max scores);
+    l = e^(m - m_new) l + sum e^(scores - m_new); o = e^(m - m_new) o + V_block e^(scores - m_new).
+    Tokens past L in the last block are left out. Returns (m, l, o) unnormalised.
+    """
+    D = qv.shape[0]
+    m, l, o = -math.inf, 0.0, np.zeros(D, dtype=np.float64)
+    for j in range(first_block, last_block):
+        b = int(table_row[j])
+        n_valid = min(bs, L - j * bs)
+        if n_valid <= 0:
+            break
+        Kb = decode_bits(k_cache[b, g][:, :n_valid], kv_dtype) * k_scale    # [D, n]
+        Vb = decode_bits(v_cache[b, g][:, :n_valid], kv_dtype) * v_scale
+        scores = scale * (qv @ Kb)
+        m_new = max(m, float(scores.max()))
+        alpha = math.exp(m - m_new) if m != -math.inf else 0.0
+        p = np.exp(scores - m_new)
+        l = alpha * l + float(p.sum())
+        o = alpha * o + Vb @ p
+        m = m_new
+    return m, l, o
+
+
+def merge_partials(parts: List[Tuple[float, float, np.ndarray]]) -> np.ndarray:
+    """Combine per-partition (m, l, o) states into o_total / l_total.
+
+    The same rescaling the per-block update applies, taken across partitions:
+    M = max m_p, l = sum e^(m_p - M) l_p, o = sum e^(m_p - M) o_p.
+    """
+    live = [(m, l, o) for (m, l, o) in parts if m != -math.inf]
+    if not live:
+        return np.zeros_like(parts[0][2]) if parts else np.zeros(0)
+    M = max(m for m, _, _ in live)
+    lt = sum(math.exp(m - M) * l for m, l, _ in live)
+    ot = sum(math.exp(m - M) * o for m, _, o in live)
+    return ot / lt
+
+
+def online_decode(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale,
+                  q_dtype: str, kv_dtype: str, partition_blocks: Optional[int] = None,
+                  k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
+    """Block-by-block online softmax, optionally split into partitions of
+    `partition_blocks` logical blocks whose states are merged at the end."""
+    S, H, D, G = _check_shapes(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads)
+    bs = k_cache.shape[3]
+    sc64 = float(np.float32(scale))
+    out = np.zeros((S, H, D), dtype=np.float64)
+    for s in range(S):
+        L = int(seq_lens[s])
+        nblk = (L + bs - 1) // bs
+        step = partition_blocks or max(nblk, 1)
+        for h in range(H):
+            g = h // G
+            qv = decode_bits(q[s, h], q_dtype)
+            parts = [_online_partition(qv, k_cache, v_cache, block_tables[s], L, g, b0,
+                                       min(nblk, b0 + step), bs, kv_dtype, sc64, k_scale, v_scale)
+                     for b0 in range(0, nblk, step)]
+            out[s, h] = merge_partials(parts) if parts else 0.0
+    return out
