@@ -1,0 +1,152 @@
+/*
+ * pa_decode.h - PagedAttention decode on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (vLLM e PagedAttention page, PagedAttention kernel pseudocode;
+ * "Optimização da inferência" page, step 2, attention with the KV cache):
+ *
+ *   for every sequence s and query head h, with L = seq_lens[s] and
+ *   KV head g = h / (num_heads / num_kv_heads):
+ *       token t < L of sequence s is stored in physical block
+ *       block_tables[s][t / block_size], slot t % block_size;
+ *       out[s][h][:] = sum_t softmax_t(scale * q[s][h] . K_t) * V_t
+ *   and out[s][h][:] = 0 when L == 0.
+ *
+ * The kernels accumulate the softmax online (running max, running sum,
+ * rescaled output) over whole physical blocks, split long sequences into
+ * context partitions and merge the partitions in a second kernel.
+ *
+ * Layouts (all row-major, contiguous, every pointer 16-byte aligned):
+ *   q, out        [num_seqs][num_heads][head_dim]                  element type q_dtype
+ *   k_cache       [num_blocks][num_kv_heads][head_dim][block_size] element type kv_dtype
+ *   v_cache       same as k_cache
+ *   block_tables  [num_seqs][max_blocks_per_seq]                   int32 physical block ids
+ *   seq_lens      [num_seqs]                                       int32
+ * (the cache layout is the one in the kernel pseudocode; its head axis counts
+ *  KV heads, as the KV-cache size formula on the inference page does.)
+ *
+ * Ownership: every data pointer is caller-owned device memory. The library
+ * never frees it, keeps no reference after the call returns, and never
+ * synchronises the device or the stream. Work is enqueued on `stream` (a
+ * hipStream_t passed as void*, NULL = the default stream); inputs must stay
+ * alive, and `out` untouched, until the stream reaches that point. q, the
+ * caches, the tables and seq_lens are only read; out is only written.
+ *
+ * Errors: every call returns a pa_status_t. Argument validation happens on
+ * the host before any HIP call, so a rejected call enqueues nothing. There is
+ * no global error state; pa_status_str() names a status.
+ *
+ * Device-side preconditions (not checked, the data lives on the device):
+ *   0 <= seq_lens[s] <= min(max_seq_len, max_blocks_per_seq * block_size)
+ *   0 <= block_tables[s][j] < num_blocks for j < ceil(seq_lens[s] / block_size)
+ * Table entries past ceil(seq_lens[s] / block_size), and cache slots past
+ * seq_lens[s] in the last block, are never read. Several sequences may map
+ * to the same physical block (shared prefixes).
+ */
+#ifndef PA_DECODE_H
+#define PA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,        /* a required pointer is NULL                              */
+  PA_ERR_SHAPE = 2,       /* non-positive size, num_heads % num_kv_heads != 0, ...   */
+  PA_ERR_UNSUPPORTED = 3, /* head_dim / block_size / group / dtype combination       */
+  PA_ERR_ALIGN = 4,       /* a data pointer is not 16-byte aligned                   */
+  PA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than pa_decode_workspace_bytes */
+  PA_ERR_HIP = 6          /* a HIP runtime call or kernel launch failed              */
+} pa_status_t;
+
+typedef enum pa_dtype {
+  PA_DTYPE_F32 = 0,
+  PA_DTYPE_BF16 = 1,      /* bfloat16; outputs rounded to nearest even              */
+  PA_DTYPE_FP8_E5M2 = 2   /* OCP E5M2 (bias 15, IEEE-style inf/NaN); KV cache only  */
+} pa_dtype_t;
+
+typedef enum pa_kernel {
+  PA_KERNEL_AUTO = 0,     /* matrix-core kernel where supported, else vector kernel  */
+  PA_KERNEL_VALU = 1,     /* vector-ALU kernel (every supported shape)               */
+  PA_KERNEL_MFMA = 2      /* matrix-core kernel: head_dim 128, block 16, group <= 16,
+                             q bf16 with KV bf16 or fp8-e5m2                         */
+} pa_kernel_t;
+
+/* Sizes and types of one call. Supported: block_size 16; head_dim 64 or 128;
+ * group = num_heads / num_kv_heads in {1, 2, 4, 8, 16}; (q_dtype, kv_dtype) in
+ * {(F32, F32), (BF16, BF16), (BF16, FP8_E5M2)}. */
+typedef struct pa_dims {
+  int32_t num_seqs;
+  int32_t num_heads;           /* query heads                                         */
+  int32_t head_dim;
+  int32_t num_blocks;          /* physical blocks in each cache                        */
+  int32_t block_size;          /* tokens per block                                     */
+  int32_t max_blocks_per_seq;  /* block_tables row length                              */
+  int32_t q_dtype;             /* pa_dtype_t of q and out                              */
+  int32_t kv_dtype;            /* pa_dtype_t of k_cache and v_cache                    */
+  float k_scale;               /* per-tensor dequantisation scales (1.0f unless fp8)   */
+  float v_scale;
+  int32_t max_seq_len;         /* host upper bound on seq_lens, sizes the split grid;
+                                  0 means max_blocks_per_seq * block_size             */
+  int32_t partition_tokens;    /* context-partition length; 0 = chosen by the library,
+                                  else a positive multiple of 64                      */
+  int32_t kernel;              /* pa_kernel_t                                          */
+} pa_dims_t;
+
+/* Decode with a workspace the library takes from the stream-ordered allocator
+ * (hipMallocAsync / hipFreeAsync on `stream`) when the plan needs one. */
+int pa_decode(const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* seq_lens,
+              int32_t num_kv_heads, float scale, void* out,
+              const pa_dims_t* dims, void* stream);
+
+/* Bytes of device workspace pa_decode_ws needs for these sizes (0 if none).
+ * Returns 0 and sets *status (if non-NULL) on invalid arguments. */
+size_t pa_decode_workspace_bytes(const pa_dims_t* dims, int32_t num_kv_heads, int* status);
+
+/* Decode with a caller-owned device workspace of at least
+ * pa_decode_workspace_bytes() bytes, 256-byte aligned. The workspace holds the
+ * per-partition softmax states between the two kernels; it may be reused by
+ * the next call on the same stream. */
+int pa_decode_ws(const void* q, const void* k_cache, const void* v_cache,
+                 const int32_t* block_tables, const int32_t* seq_lens,
+                 int32_t num_kv_heads, float scale, void* out,
+                 const pa_dims_t* dims, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+/* pa_decode_ws that also records three caller-created HIP events (hipEvent_t
+ * as void*) on `stream`: before the partition kernel, between the partition
+ * and reduce kernels, and after the reduce kernel. Any event may be NULL. */
+int pa_decode_ws_timed(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* seq_lens,
+                       int32_t num_kv_heads, float scale, void* out,
+                       const pa_dims_t* dims, void* workspace, size_t workspace_bytes,
+                       void* stream, void* ev_start, void* ev_mid, void* ev_end);
+
+/* The launch plan the library would use for these sizes (host only). */
+typedef struct pa_plan {
+  int32_t kernel;              /* pa_kernel_t actually used (never AUTO)              */
+  int32_t partition_tokens;    /* tokens per context partition                         */
+  int32_t max_partitions;      /* partitions of the longest allowed sequence           */
+  int32_t grid_workgroups;     /* workgroups of the partition kernel                   */
+  int32_t reduce_workgroups;   /* workgroups of the reduce kernel (0 = not launched)   */
+  int32_t pad;
+  size_t workspace_bytes;
+} pa_plan_t;
+
+int pa_decode_plan(const pa_dims_t* dims, int32_t num_kv_heads, pa_plan_t* plan);
+
+/* Static description of a status code. */
+const char* pa_status_str(int status);
+
+/* Library version, (major << 16) | minor. */
+int pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_DECODE_H */

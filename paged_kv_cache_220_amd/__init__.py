@@ -1,0 +1,8 @@
+"""PagedAttention decode for AMD Instinct MI355X (gfx950).
+
+The decode itself runs in the HIP library ``libpadecode.so`` (C ABI declared
+in ``include/pa_decode.h``); ``pa_decode`` below is its ctypes binding.
+"""
+
+from .binding import (PagedAttentionError, alloc_workspace, load_library, make_dims, pa_decode,  # noqa: F401
+                      plan, status_str, workspace_bytes)

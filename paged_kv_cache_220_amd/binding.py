@@ -1,0 +1,200 @@
+"""Python binding of libpadecode.so (ctypes): argument marshalling only.
+
+Every step of the decode runs in the HIP library; this module reads shapes
+and dtypes off torch tensors, fills ``pa_dims_t`` and calls the C ABI on the
+current torch stream. There is no fallback: a missing library or a non-zero
+status raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpadecode.so")
+
+PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_ALIGN, PA_ERR_WORKSPACE, PA_ERR_HIP = range(7)
+PA_DTYPE_F32, PA_DTYPE_BF16, PA_DTYPE_FP8_E5M2 = 0, 1, 2
+KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
+KERNEL_NAMES = {v: k for k, v in KERNELS.items()}
+
+# Symbols declared in include/pa_decode.h.
+EXPORTED = ("pa_decode", "pa_decode_ws", "pa_decode_ws_timed", "pa_decode_workspace_bytes",
+            "pa_decode_plan", "pa_status_str", "pa_version")
+
+
+class PaDims(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("max_blocks_per_seq", ctypes.c_int32), ("q_dtype", ctypes.c_int32),
+                ("kv_dtype", ctypes.c_int32), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
+                ("max_seq_len", ctypes.c_int32), ("partition_tokens", ctypes.c_int32),
+                ("kernel", ctypes.c_int32)]
+
+
+class PaPlan(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("partition_tokens", ctypes.c_int32),
+                ("max_partitions", ctypes.c_int32), ("grid_workgroups", ctypes.c_int32),
+                ("reduce_workgroups", ctypes.c_int32), ("pad", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+class PagedAttentionError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load the HIP library (built by ``python -m paged_kv_cache_220_amd.build``)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build the HIP library first "
+                           f"(python -m paged_kv_cache_220_amd.build); there is no CPU fallback")
+    lib = ctypes.CDLL(p)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    dims_p = ctypes.POINTER(PaDims)
+    common = [vp, vp, vp, vp, vp, i32, f32, vp, dims_p]
+    lib.pa_decode.argtypes = common + [vp]
+    lib.pa_decode.restype = ctypes.c_int
+    lib.pa_decode_ws.argtypes = common + [vp, sz, vp]
+    lib.pa_decode_ws.restype = ctypes.c_int
+    lib.pa_decode_ws_timed.argtypes = common + [vp, sz, vp, vp, vp, vp]
+    lib.pa_decode_ws_timed.restype = ctypes.c_int
+    lib.pa_decode_workspace_bytes.argtypes = [dims_p, i32, ctypes.POINTER(ctypes.c_int)]
+    lib.pa_decode_workspace_bytes.restype = sz
+    lib.pa_decode_plan.argtypes = [dims_p, i32, ctypes.POINTER(PaPlan)]
+    lib.pa_decode_plan.restype = ctypes.c_int
+    lib.pa_status_str.argtypes = [ctypes.c_int]
+    lib.pa_status_str.restype = ctypes.c_char_p
+    lib.pa_version.argtypes = []
+    lib.pa_version.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load_library().pa_status_str(status).decode()
+
+
+def _check(rc: int):
+    if rc != PA_OK:
+        raise PagedAttentionError(rc, status_str(rc))
+
+
+_TORCH_DTYPES = {torch.float32: PA_DTYPE_F32, torch.bfloat16: PA_DTYPE_BF16}
+_KV_NAMES = {"f32": PA_DTYPE_F32, "bf16": PA_DTYPE_BF16, "e5m2": PA_DTYPE_FP8_E5M2}
+
+
+def _kv_dtype_code(t: torch.Tensor, kv_dtype: Optional[str]) -> int:
+    if kv_dtype is not None:
+        return _KV_NAMES[kv_dtype]
+    if t.dtype == torch.float8_e5m2:
+        return PA_DTYPE_FP8_E5M2
+    if t.dtype in _TORCH_DTYPES:
+        return _TORCH_DTYPES[t.dtype]
+    raise TypeError(f"unsupported KV cache dtype {t.dtype}; pass kv_dtype for raw byte views")
+
+
+def make_dims(q: torch.Tensor, k_cache: torch.Tensor, block_tables: torch.Tensor, *,
+              kv_dtype: Optional[str] = None, max_seq_len: int = 0, partition_tokens: int = 0,
+              kernel: str = "auto", k_scale: float = 1.0, v_scale: float = 1.0) -> PaDims:
+    if q.dim() != 3 or k_cache.dim() != 4 or block_tables.dim() != 2:
+        raise ValueError("q [S,H,D], k_cache [NB,Hkv,D,bs], block_tables [S,max_blocks] expected")
+    if q.dtype not in _TORCH_DTYPES:
+        raise TypeError(f"unsupported q dtype {q.dtype}")
+    S, H, D = q.shape
+    NB, _, _, bs = k_cache.shape
+    return PaDims(num_seqs=S, num_heads=H, head_dim=D, num_blocks=NB, block_size=bs,
+                  max_blocks_per_seq=block_tables.shape[1], q_dtype=_TORCH_DTYPES[q.dtype],
+                  kv_dtype=_kv_dtype_code(k_cache, kv_dtype), k_scale=k_scale, v_scale=v_scale,
+                  max_seq_len=max_seq_len, partition_tokens=partition_tokens, kernel=KERNELS[kernel])
+
+
+def plan(dims: PaDims, num_kv_heads: int) -> dict:
+    p = PaPlan()
+    _check(load_library().pa_decode_plan(ctypes.byref(dims), num_kv_heads, ctypes.byref(p)))
+    return dict(kernel=KERNEL_NAMES[p.kernel], partition_tokens=p.partition_tokens,
+                max_partitions=p.max_partitions, grid_workgroups=p.grid_workgroups,
+                reduce_workgroups=p.reduce_workgroups, workspace_bytes=p.workspace_bytes)
+
+
+def workspace_bytes(dims: PaDims, num_kv_heads: int) -> int:
+    st = ctypes.c_int(0)
+    n = load_library().pa_decode_workspace_bytes(ctypes.byref(dims), num_kv_heads, ctypes.byref(st))
+    _check(st.value)
+    return int(n)
+
+
+def _validate_tensors(q, k_cache, v_cache, block_tables, seq_lens, out):
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("pa_decode runs on the GPU: q must be a cuda tensor")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("block_tables", block_tables),
+                    ("seq_lens", seq_lens), ("out", out)):
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, q on {dev}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_tables and seq_lens must be int32")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must have q's shape and dtype")
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("v_cache must match k_cache")
+
+
+def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+              seq_lens: torch.Tensor, num_kv_heads: int, scale: float, out: Optional[torch.Tensor] = None, *,
+              kv_dtype: Optional[str] = None, max_seq_len: int = 0, partition_tokens: int = 0,
+              kernel: str = "auto", k_scale: float = 1.0, v_scale: float = 1.0,
+              workspace: Optional[torch.Tensor] = None, events=None) -> torch.Tensor:
+    """PagedAttention decode through the C ABI; returns `out`.
+
+    `workspace` (uint8 cuda tensor) selects ``pa_decode_ws``; without it the
+    library takes its workspace from the stream-ordered allocator.
+    `events` = (start, mid, end) raw hipEvent_t handles selects ``pa_decode_ws_timed``.
+    """
+    if out is None:
+        out = torch.empty_like(q)
+    _validate_tensors(q, k_cache, v_cache, block_tables, seq_lens, out)
+    dims = make_dims(q, k_cache, block_tables, kv_dtype=kv_dtype, max_seq_len=max_seq_len,
+                     partition_tokens=partition_tokens, kernel=kernel, k_scale=k_scale, v_scale=v_scale)
+    lib = load_library()
+    stream = ctypes.c_void_p(torch.cuda.current_stream(q.device).cuda_stream)
+    args = (ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_cache.data_ptr()),
+            ctypes.c_void_p(v_cache.data_ptr()), ctypes.c_void_p(block_tables.data_ptr()),
+            ctypes.c_void_p(seq_lens.data_ptr()), ctypes.c_int32(num_kv_heads), ctypes.c_float(scale),
+            ctypes.c_void_p(out.data_ptr()), ctypes.byref(dims))
+    if workspace is None and events is None:
+        rc = lib.pa_decode(*args, stream)
+    else:
+        if workspace is None:
+            raise ValueError("events need a caller workspace")
+        if workspace.device != q.device or workspace.dtype != torch.uint8:
+            raise ValueError("workspace must be a uint8 tensor on q's device")
+        ws = (ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(workspace.numel()))
+        if events is None:
+            rc = lib.pa_decode_ws(*args, *ws, stream)
+        else:
+            ev = [ctypes.c_void_p(e) if e else None for e in events]
+            rc = lib.pa_decode_ws_timed(*args, *ws, stream, *ev)
+    _check(rc)
+    return out
+
+
+def alloc_workspace(dims: PaDims, num_kv_heads: int, device) -> torch.Tensor:
+    n = workspace_bytes(dims, num_kv_heads)
+    # torch's caching allocator hands out 512-byte aligned blocks
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)

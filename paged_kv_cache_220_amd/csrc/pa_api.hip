@@ -1,0 +1,213 @@
+// C ABI of the PagedAttention decode library: argument validation, launch
+// planning (context partitions, workspace layout) and kernel launches.
+// Validation runs entirely on the host before any HIP call.
+
+#include <math.h>
+#include <string.h>
+
+#include "pa_internal.h"
+
+namespace {
+
+using pa::Args;
+
+constexpr int kVersionMajor = 0;
+constexpr int kVersionMinor = 1;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Plan {
+  int kernel = PA_KERNEL_VALU;
+  int group = 1;
+  int max_len = 0;
+  int partition_tokens = 0;
+  int max_parts = 1;
+  size_t off_m = 0, off_l = 0, ws_bytes = 0;
+  long long grid = 0, reduce_grid = 0;
+};
+
+int check_dims(const pa_dims_t* d, int32_t hkv) {
+  if (d == nullptr) return PA_ERR_NULL;
+  if (d->num_seqs <= 0 || d->num_heads <= 0 || d->head_dim <= 0 || d->num_blocks <= 0 ||
+      d->block_size <= 0 || d->max_blocks_per_seq <= 0 || hkv <= 0)
+    return PA_ERR_SHAPE;
+  if (d->num_heads % hkv != 0) return PA_ERR_SHAPE;
+  if (d->max_seq_len < 0 || d->partition_tokens < 0) return PA_ERR_SHAPE;
+  if ((long long)d->max_seq_len > (long long)d->max_blocks_per_seq * d->block_size) return PA_ERR_SHAPE;
+  if (d->partition_tokens % pa::kTileTokens != 0) return PA_ERR_SHAPE;
+  if (!isfinite(d->k_scale) || !isfinite(d->v_scale)) return PA_ERR_SHAPE;
+  if (d->kernel < PA_KERNEL_AUTO || d->kernel > PA_KERNEL_MFMA) return PA_ERR_UNSUPPORTED;
+  if (d->block_size != pa::kBlockSize) return PA_ERR_UNSUPPORTED;
+  if (d->num_seqs > 65535 || hkv > 65535) return PA_ERR_UNSUPPORTED;  // grid y / z limits
+  const int group = d->num_heads / hkv;
+  if (!pa::valu_supported(d->q_dtype, d->kv_dtype, d->head_dim, group)) return PA_ERR_UNSUPPORTED;
+  if (d->kernel == PA_KERNEL_MFMA &&
+      !pa::mfma_supported(d->q_dtype, d->kv_dtype, d->head_dim, group, d->block_size))
+    return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
+  const int st = check_dims(d, hkv);
+  if (st != PA_OK) return st;
+  p->group = d->num_heads / hkv;
+  if (d->kernel == PA_KERNEL_AUTO) {
+    p->kernel = pa::mfma_supported(d->q_dtype, d->kv_dtype, d->head_dim, p->group, d->block_size)
+                    ? PA_KERNEL_MFMA
+                    : PA_KERNEL_VALU;
+  } else {
+    p->kernel = d->kernel;
+  }
+  p->max_len = d->max_seq_len > 0 ? d->max_seq_len : d->max_blocks_per_seq * d->block_size;
+  int P = d->partition_tokens;
+  if (P == 0) {
+    // Long contexts are split so that the grid holds enough independent
+    // (sequence, KV head, partition) items to keep every CU streaming.
+    const long long units = (long long)d->num_seqs * hkv;
+    P = 512;
+    while (P > 128 && units * ((p->max_len + P - 1) / P) < 2048) P /= 2;
+  }
+  p->partition_tokens = P;
+  p->max_parts = p->max_len > 0 ? (p->max_len + P - 1) / P : 1;
+  if (p->max_parts < 1) p->max_parts = 1;
+  p->grid = (long long)p->max_parts * hkv * d->num_seqs;
+  p->reduce_grid = p->max_parts > 1 ? (long long)d->num_heads * d->num_seqs : 0;
+  if (p->max_parts > 1) {
+    const size_t items = (size_t)d->num_seqs * hkv * p->max_parts * p->group;
+    const size_t o_bytes = items * d->head_dim * sizeof(float);
+    p->off_m = align_up(o_bytes, kAlign);
+    p->off_l = p->off_m + align_up(items * sizeof(float), kAlign);
+    p->ws_bytes = p->off_l + align_up(items * sizeof(float), kAlign);
+  } else {
+    p->off_m = p->off_l = p->ws_bytes = 0;
+  }
+  return PA_OK;
+}
+
+int run(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+        const int32_t* seq_lens, int32_t hkv, float scale, void* out, const pa_dims_t* dims,
+        void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1,
+        hipEvent_t ev2) {
+  if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !out) return PA_ERR_NULL;
+  Plan p;
+  const int st = make_plan(dims, hkv, &p);
+  if (st != PA_OK) return st;
+  if (!isfinite(scale)) return PA_ERR_SHAPE;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(block_tables, 4) || !aligned(seq_lens, 4))
+    return PA_ERR_ALIGN;
+  if (p.ws_bytes > 0 && (workspace == nullptr || workspace_bytes < p.ws_bytes || !aligned(workspace, kAlign)))
+    return PA_ERR_WORKSPACE;
+
+  Args a;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  char* ws = static_cast<char*>(workspace);
+  a.part_o = p.ws_bytes ? reinterpret_cast<float*>(ws) : nullptr;
+  a.part_m = p.ws_bytes ? reinterpret_cast<float*>(ws + p.off_m) : nullptr;
+  a.part_l = p.ws_bytes ? reinterpret_cast<float*>(ws + p.off_l) : nullptr;
+  a.block_stride = (int64_t)hkv * dims->head_dim * dims->block_size;
+  a.num_seqs = dims->num_seqs;
+  a.num_heads = dims->num_heads;
+  a.num_kv_heads = hkv;
+  a.max_blocks = dims->max_blocks_per_seq;
+  a.partition_tokens = p.partition_tokens;
+  a.max_parts = p.max_parts;
+  a.score_scale = scale * dims->k_scale * 1.4426950408889634f;
+  a.v_scale = dims->v_scale;
+
+  if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return PA_ERR_HIP;
+  hipError_t e = p.kernel == PA_KERNEL_MFMA
+                     ? pa::launch_mfma(a, dims->q_dtype, dims->kv_dtype, dims->head_dim, p.group, stream)
+                     : pa::launch_valu(a, dims->q_dtype, dims->kv_dtype, dims->head_dim, p.group, stream);
+  if (e != hipSuccess) return PA_ERR_HIP;
+  if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return PA_ERR_HIP;
+  if (p.max_parts > 1) {
+    e = pa::launch_reduce(a, dims->q_dtype, dims->head_dim, p.group, stream);
+    if (e != hipSuccess) return PA_ERR_HIP;
+  }
+  if (ev2 && hipEventRecord(ev2, stream) != hipSuccess) return PA_ERR_HIP;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pa_decode_workspace_bytes(const pa_dims_t* dims, int32_t num_kv_heads, int* status) {
+  Plan p;
+  const int st = make_plan(dims, num_kv_heads, &p);
+  if (status) *status = st;
+  return st == PA_OK ? p.ws_bytes : 0;
+}
+
+int pa_decode_plan(const pa_dims_t* dims, int32_t num_kv_heads, pa_plan_t* plan) {
+  if (plan == nullptr) return PA_ERR_NULL;
+  Plan p;
+  const int st = make_plan(dims, num_kv_heads, &p);
+  if (st != PA_OK) return st;
+  memset(plan, 0, sizeof(*plan));
+  plan->kernel = p.kernel;
+  plan->partition_tokens = p.partition_tokens;
+  plan->max_partitions = p.max_parts;
+  plan->grid_workgroups = (int32_t)p.grid;
+  plan->reduce_workgroups = (int32_t)p.reduce_grid;
+  plan->workspace_bytes = p.ws_bytes;
+  return PA_OK;
+}
+
+int pa_decode_ws(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                 const int32_t* seq_lens, int32_t num_kv_heads, float scale, void* out,
+                 const pa_dims_t* dims, void* workspace, size_t workspace_bytes, void* stream) {
+  return run(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale, out, dims, workspace,
+             workspace_bytes, static_cast<hipStream_t>(stream), nullptr, nullptr, nullptr);
+}
+
+int pa_decode_ws_timed(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* seq_lens, int32_t num_kv_heads,
+                       float scale, void* out, const pa_dims_t* dims, void* workspace,
+                       size_t workspace_bytes, void* stream, void* ev_start, void* ev_mid,
+                       void* ev_end) {
+  return run(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale, out, dims, workspace,
+             workspace_bytes, static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(ev_start),
+             static_cast<hipEvent_t>(ev_mid), static_cast<hipEvent_t>(ev_end));
+}
+
+int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+              const int32_t* seq_lens, int32_t num_kv_heads, float scale, void* out,
+              const pa_dims_t* dims, void* stream) {
+  if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !out) return PA_ERR_NULL;
+  Plan p;
+  const int st = make_plan(dims, num_kv_heads, &p);
+  if (st != PA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if (p.ws_bytes > 0 && hipMallocAsync(&ws, p.ws_bytes, s) != hipSuccess) return PA_ERR_HIP;
+  const int rc = run(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale, out, dims, ws,
+                     p.ws_bytes, s, nullptr, nullptr, nullptr);
+  if (ws != nullptr && hipFreeAsync(ws, s) != hipSuccess && rc == PA_OK) return PA_ERR_HIP;
+  return rc;
+}
+
+const char* pa_status_str(int status) {
+  switch (status) {
+    case PA_OK: return "PA_OK: success";
+    case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE: invalid sizes (non-positive, num_heads % num_kv_heads, bounds, scale)";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: unsupported head_dim / block_size / group / dtype / kernel";
+    case PA_ERR_ALIGN: return "PA_ERR_ALIGN: q, caches and out need 16-byte alignment, tables and seq_lens 4";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing, too small or not 256-byte aligned";
+    case PA_ERR_HIP: return "PA_ERR_HIP: a HIP runtime call or kernel launch failed";
+    default: return "unknown pa_decode status";
+  }
+}
+
+int pa_version(void) { return (kVersionMajor << 16) | kVersionMinor; }
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Internal declarations shared by the host API and the kernels of the
+// PagedAttention decode library (gfx950). Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_decode.h"
+
+namespace pa {
+
+// Everything a partition or reduce kernel needs, passed by value.
+struct Args {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* tables;
+  const int32_t* seq_lens;
+  void* out;
+  float* part_o;   // [S][Hkv][max_parts][G][D]   unnormalised partition outputs
+  float* part_m;   // [S][Hkv][max_parts][G]      partition running max (log2 domain)
+  float* part_l;   // [S][Hkv][max_parts][G]      partition running sum
+  int64_t block_stride;   // elements per physical block: Hkv * D * block_size
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t max_blocks;     // block_tables row length
+  int32_t partition_tokens;
+  int32_t max_parts;
+  float score_scale;      // scale * k_scale * log2(e): scores live in the log2 domain
+  float v_scale;
+};
+
+// Host-side launchers; each returns the hipError_t of the launch.
+hipError_t launch_valu(const Args& a, int q_dtype, int kv_dtype, int head_dim, int group,
+                       hipStream_t stream);
+hipError_t launch_mfma(const Args& a, int q_dtype, int kv_dtype, int head_dim, int group,
+                       hipStream_t stream);
+hipError_t launch_reduce(const Args& a, int q_dtype, int head_dim, int group, hipStream_t stream);
+
+bool valu_supported(int q_dtype, int kv_dtype, int head_dim, int group);
+bool mfma_supported(int q_dtype, int kv_dtype, int head_dim, int group, int block_size);
+
+constexpr int kBlockSize = 16;     // tokens per physical block handled by the kernels
+constexpr int kTileTokens = 64;    // partition lengths are multiples of this
+
+}  // namespace pa

@@ -1,0 +1,356 @@
+// Matrix-core PagedAttention decode partition kernel (gfx950, wave64).
+//
+// Same work unit as the vector kernel: one wavefront per (sequence, KV head,
+// context partition), all G <= 16 query heads of the KV head together, so
+// every K/V tile is read once per KV head. The online-softmax state of the
+// PagedAttention kernel pseudocode (vLLM page: running max m, running sum l,
+// rescaled o, output o / l) stays in registers. Here the two contractions of
+// a grouped decode step run on v_mfma_f32_16x16x32_{bf16,f16}:
+//   S^T[token][head] = K^T[token][d] . Q^T[d][head]   (contract over head_dim)
+//   O^T[d][head]    += V[d][token]  . P^T[token][head] (contract over tokens)
+// with heads on the 16 MFMA columns (columns >= G carry zero queries).
+//
+// The cache tile is [head_dim][16 tokens] with tokens fastest, which suits PV
+// directly (a 128-bit load is 8 tokens of one row) but not QK, whose operand
+// wants several head_dim values of one token per lane. The kernel gets them
+// without LDS: each lane loads 8 rows x 4 tokens (one 64-bit load per row)
+// and transposes them in registers with v_perm_b32, feeding 4 MFMAs (one per
+// token of the quartet). The MFMA k index may map to head_dim in any order as
+// long as the Q operand uses the same order, so lane group c takes rows
+// 32*kstep + 4*i + c, which makes every load instruction cover whole
+// 128-byte lines.
+//
+// A tile is 64 tokens = 4 physical blocks. MFMA row (quartet) q = 4c + r of
+// the QK step holds block (c >> 1) + 2 * (r >> 1), tokens 8 * (c & 1) +
+// 4 * (r & 1) + j, j = 0..3 (one MFMA per j). With that placement the QK
+// accumulator already sits where the PV step needs P: lane (c, head) holds
+// the 8 consecutive tokens 8 * (c & 1) .. +7 of block (c >> 1) + 2 * hh for
+// PV instruction hh, which are exactly the tokens of its 128-bit V load.
+// So P moves from the score accumulator to the PV operand inside the lane;
+// the only cross-lane traffic is the max over the four lane groups per tile
+// and the final sum of l.
+//
+// Token slots at or past the partition end are selected out: their scores
+// become -inf, and their V values are zeroed before the MFMA (0 * NaN would
+// poison the sum). Logical blocks past the partition end are not looked up in
+// the table; the tile's first block stands in and is masked.
+//
+// fp8-e5m2 KV: an E5M2 byte is the top byte of the binary16 of the same
+// value, so v_perm_b32 widens K and V to fp16 exactly and the f16 MFMA runs
+// with q rounded to fp16 (exact for bf16 q in [2^-14, 65504]) and P in fp16.
+// bf16 KV: bf16 MFMA with q exact and P rounded to bf16.
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kD = 128;       // head_dim handled by this kernel
+constexpr int kTile = 64;     // tokens per tile
+constexpr int kKSteps = kD / 32;
+
+template <int KDT> struct Mfma;
+
+template <> struct Mfma<kBF16> {
+  using op_t = bf16x8;
+  using kload_t = u32x2;   // 4 tokens of one row
+  using vload_t = u32x4;   // 8 tokens of one row
+  static constexpr int kElem = 2;
+  static __device__ __forceinline__ f32x4 mma(op_t a, op_t b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  // Operand holding K[rows 2p, 2p+1 of the 8 loaded rows][token j of the quartet].
+  static __device__ __forceinline__ op_t k_operand(const kload_t (&r)[8], int j) {
+    const int w = j >> 1;
+    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+    u32x4 x;
+    x[0] = __builtin_amdgcn_perm(r[1][w], r[0][w], sel);
+    x[1] = __builtin_amdgcn_perm(r[3][w], r[2][w], sel);
+    x[2] = __builtin_amdgcn_perm(r[5][w], r[4][w], sel);
+    x[3] = __builtin_amdgcn_perm(r[7][w], r[6][w], sel);
+    return __builtin_bit_cast(op_t, x);
+  }
+  static __device__ __forceinline__ op_t v_operand(vload_t x) { return __builtin_bit_cast(op_t, x); }
+  // Zero the token slots at index >= nvalid (0..8) of an 8-token V segment.
+  static __device__ __forceinline__ vload_t mask_v(vload_t x, int nvalid) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t lo = (2 * w < nvalid) ? 0x0000FFFFu : 0u;
+      const uint32_t hi = (2 * w + 1 < nvalid) ? 0xFFFF0000u : 0u;
+      x[w] &= (lo | hi);
+    }
+    return x;
+  }
+  static __device__ __forceinline__ op_t q_operand(const float (&q)[8]) {
+    op_t o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = static_cast<__bf16>(q[i]);
+    return o;
+  }
+  static __device__ __forceinline__ op_t p_operand(const float (&p)[8]) {
+    op_t o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = static_cast<__bf16>(p[i]);
+    return o;
+  }
+};
+
+template <> struct Mfma<kE5M2> {
+  using op_t = f16x8;
+  using kload_t = uint32_t;  // 4 tokens of one row
+  using vload_t = u32x2;     // 8 tokens of one row
+  static constexpr int kElem = 1;
+  static __device__ __forceinline__ f32x4 mma(op_t a, op_t b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  // binary16 bits = e5m2 byte << 8; selector 0x0C yields a zero byte.
+  static __device__ __forceinline__ op_t k_operand(const kload_t (&r)[8], int j) {
+    const uint32_t sel = 0x0Cu | (uint32_t(j) << 8) | (0x0Cu << 16) | (uint32_t(4 + j) << 24);
+    u32x4 x;
+    x[0] = __builtin_amdgcn_perm(r[1], r[0], sel);
+    x[1] = __builtin_amdgcn_perm(r[3], r[2], sel);
+    x[2] = __builtin_amdgcn_perm(r[5], r[4], sel);
+    x[3] = __builtin_amdgcn_perm(r[7], r[6], sel);
+    return __builtin_bit_cast(op_t, x);
+  }
+  static __device__ __forceinline__ op_t v_operand(vload_t x) {
+    u32x4 y;
+    y[0] = __builtin_amdgcn_perm(x[0], x[0], 0x010C000Cu);
+    y[1] = __builtin_amdgcn_perm(x[0], x[0], 0x030C020Cu);
+    y[2] = __builtin_amdgcn_perm(x[1], x[1], 0x010C000Cu);
+    y[3] = __builtin_amdgcn_perm(x[1], x[1], 0x030C020Cu);
+    return __builtin_bit_cast(op_t, y);
+  }
+  static __device__ __forceinline__ vload_t mask_v(vload_t x, int nvalid) {
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) m |= (4 * w + b < nvalid) ? (0xFFu << (8 * b)) : 0u;
+      x[w] &= m;
+    }
+    return x;
+  }
+  static __device__ __forceinline__ op_t q_operand(const float (&q)[8]) {
+    op_t o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = static_cast<_Float16>(q[i]);
+    return o;
+  }
+  static __device__ __forceinline__ op_t p_operand(const float (&p)[8]) {
+    op_t o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = static_cast<_Float16>(p[i]);
+    return o;
+  }
+};
+
+template <int KDT>
+__global__ __launch_bounds__(64) void mfma_partition_kernel(const Args a, int group) {
+  using M = Mfma<KDT>;
+  using op_t = typename M::op_t;
+  using kload_t = typename M::kload_t;
+  using vload_t = typename M::vload_t;
+  constexpr int BS = kBlockSize;
+  constexpr int64_t kRowBytes = BS * M::kElem;             // one head_dim row of a block tile
+
+  const int part = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int s = blockIdx.z;
+  const int L = a.seq_lens[s];
+  const int P = a.partition_tokens;
+  const int nparts = L > 0 ? (L + P - 1) / P : 1;
+  if (part >= nparts) return;
+  const int tok0 = part * P;
+  const int tok1 = min(L, tok0 + P);
+
+  const int lane = threadIdx.x;
+  const int c = lane >> 4;   // lane group: k slots of the operands, rows 4c..4c+3 of results
+  const int n = lane & 15;   // MFMA row of A (quartet / head_dim row) and column of B (query head)
+
+  // Q^T operand: lane (c, n) holds q[head n][32*ks + 4*i + c], i = 0..7.
+  op_t qop[kKSteps];
+  {
+    const uint16_t* qh = static_cast<const uint16_t*>(a.q) +
+                         ((int64_t)s * a.num_heads + (int64_t)kvh * group + n) * kD;
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      float qf[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qf[i] = n < group ? bf16_bits_to_f32(qh[32 * ks + 4 * i + c]) : 0.f;
+      qop[ks] = M::q_operand(qf);
+    }
+  }
+
+  // This lane's block (0..3 within a tile) and token offset for the K loads.
+  const int kblk = (n >> 3) + 2 * ((n >> 1) & 1);
+  const int ktok = 8 * ((n >> 2) & 1) + 4 * (n & 1);
+  // Byte offsets inside a block tile of this KV head.
+  const int64_t head_off = (int64_t)kvh * kD * kRowBytes;
+  const int64_t blk_bytes = a.block_stride * M::kElem;
+  const char* kbase = static_cast<const char*>(a.k) + head_off;
+  const char* vbase = static_cast<const char*>(a.v) + head_off;
+  const int32_t* table = a.tables + (int64_t)s * a.max_blocks;
+  const int nblk_part = (tok1 + BS - 1) / BS;   // logical blocks that hold partition tokens
+
+  float m_run = -INFINITY;   // running max of head n (log2 domain), same in all lane groups
+  float l_run = 0.f;         // this lane group's share of the running sum
+  f32x4 oacc[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int t0 = tok0; t0 < tok1; t0 += kTile) {
+    const int b0 = t0 / BS;
+    int64_t boff[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int lb = b0 + k < nblk_part ? b0 + k : b0;
+      boff[k] = (int64_t)table[lb] * blk_bytes;
+    }
+    const int64_t kb_off = kblk == 0 ? boff[0] : kblk == 1 ? boff[1] : kblk == 2 ? boff[2] : boff[3];
+
+    // ---- K loads: 4 k-steps x 8 rows, 4 tokens each
+    kload_t kr[kKSteps][8];
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int d = 32 * ks + 4 * i + c;
+        kr[ks][i] = *reinterpret_cast<const kload_t*>(kbase + kb_off + d * kRowBytes + ktok * M::kElem);
+      }
+    }
+    // ---- V loads: 8 row tiles x 2 token halves, 8 tokens each
+    vload_t vr[8][2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int vb = (c >> 1) + 2 * hh;
+      const int64_t vb_off = vb == 0 ? boff[0] : vb == 1 ? boff[1] : vb == 2 ? boff[2] : boff[3];
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const int d = 16 * dt + n;
+        vr[dt][hh] = *reinterpret_cast<const vload_t*>(vbase + vb_off + d * kRowBytes + 8 * (c & 1) * M::kElem);
+      }
+    }
+
+    // ---- S^T = K^T Q^T: MFMA j covers token j of every quartet
+    f32x4 sacc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks) sacc[j] = M::mma(M::k_operand(kr[ks], j), qop[ks], sacc[j]);
+    }
+
+    // ---- online softmax for head n over this tile
+    const int nvalid = tok1 - t0;   // tokens of this tile inside the partition (may exceed 64)
+    float sc[4][4];                 // [r][j]
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tt = 16 * ((c >> 1) + 2 * (r >> 1)) + 8 * (c & 1) + 4 * (r & 1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x = sacc[j][r] * a.score_scale;
+        sc[r][j] = (tt + j < nvalid) ? x : -INFINITY;
+        tmax = fmaxf(tmax, sc[r][j]);
+      }
+    }
+    tmax = fmaxf(tmax, shfl_xor_f32(tmax, 16));
+    tmax = fmaxf(tmax, shfl_xor_f32(tmax, 32));
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = exp2f(m_run - m_new);
+    m_run = m_new;
+    float psum = 0.f;
+    float p[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        p[r][j] = exp2f(sc[r][j] - m_new);
+        psum += p[r][j];
+      }
+    }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) oacc[dt] *= alpha;
+
+    // ---- O^T += V P^T: PV instruction hh takes quartets r = 2hh, 2hh+1
+    op_t pop[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      float pv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pv[i] = p[2 * hh + (i >> 2)][i & 3];
+      pop[hh] = M::p_operand(pv);
+    }
+    if (nvalid < kTile) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int seg = 16 * ((c >> 1) + 2 * hh) + 8 * (c & 1);
+        const int nv = min(8, max(0, nvalid - seg));
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) vr[dt][hh] = M::mask_v(vr[dt][hh], nv);
+      }
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) oacc[dt] = M::mma(M::v_operand(vr[dt][hh]), pop[hh], oacc[dt]);
+    }
+  }
+
+  // ---- epilogue: lane (c, n) holds O^T[16*dt + 4*c + r][head n]
+  float l_tot = l_run;
+  l_tot += shfl_xor_f32(l_tot, 16);
+  l_tot += shfl_xor_f32(l_tot, 32);
+  if (n >= group) return;
+  if (nparts == 1) {
+    const float inv = l_tot > 0.f ? a.v_scale / l_tot : 0.f;
+    const int64_t orow = ((int64_t)s * a.num_heads + (int64_t)kvh * group + n) * kD;
+    uint16_t* out = static_cast<uint16_t*>(a.out) + orow;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      u32x2 w;
+      w[0] = uint32_t(f32_to_bf16_bits(oacc[dt][0] * inv)) | (uint32_t(f32_to_bf16_bits(oacc[dt][1] * inv)) << 16);
+      w[1] = uint32_t(f32_to_bf16_bits(oacc[dt][2] * inv)) | (uint32_t(f32_to_bf16_bits(oacc[dt][3] * inv)) << 16);
+      *reinterpret_cast<u32x2*>(out + 16 * dt + 4 * c) = w;
+    }
+  } else {
+    const int64_t item = ((int64_t)s * a.num_kv_heads + kvh) * a.max_parts + part;
+    float* po = a.part_o + (item * group + n) * kD;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * c) = oacc[dt] * a.v_scale;
+    if (c == 0) {
+      a.part_m[item * group + n] = m_run;
+      a.part_l[item * group + n] = l_tot;
+    }
+  }
+}
+
+}  // namespace
+
+bool mfma_supported(int q_dtype, int kv_dtype, int head_dim, int group, int block_size) {
+  return q_dtype == kBF16 && (kv_dtype == kBF16 || kv_dtype == kE5M2) && head_dim == kD &&
+         block_size == kBlockSize && group >= 1 && group <= 16;
+}
+
+hipError_t launch_mfma(const Args& a, int q_dtype, int kv_dtype, int head_dim, int group,
+                       hipStream_t stream) {
+  if (!mfma_supported(q_dtype, kv_dtype, head_dim, group, kBlockSize)) return hipErrorInvalidValue;
+  const dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
+  if (kv_dtype == kBF16) {
+    mfma_partition_kernel<kBF16><<<grid, 64, 0, stream>>>(a, group);
+  } else {
+    mfma_partition_kernel<kE5M2><<<grid, 64, 0, stream>>>(a, group);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pa

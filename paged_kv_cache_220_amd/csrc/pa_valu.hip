@@ -1,0 +1,232 @@
+// Vector-ALU PagedAttention decode partition kernel (gfx950, wave64).
+//
+// One workgroup of one wavefront handles one (sequence, KV head, context
+// partition) and all G query heads that share the KV head, so every K/V tile
+// is read once per KV head (grouped-query sharing; the KV-cache size on the
+// "Optimização da inferência" page counts KV heads, 64 query heads over 8).
+// It walks the partition's logical blocks through the block table and keeps
+// the online-softmax state (running max m, running sum l, rescaled o) of the
+// PagedAttention kernel pseudocode on the vLLM page in registers.
+//
+// Per 16-token block (tile [head_dim][16], tokens fastest):
+//   QK: lane = (token t = lane % 16, row group c = lane / 16); the lane reads
+//       rows d = 4i + c (one 128-byte line per wave instruction), multiplies
+//       by q from LDS, and the four row groups are summed with two xor
+//       shuffles. Every lane then holds the full score of its token.
+//   softmax: max and sum over the 16 tokens with xor shuffles; scores are in
+//       the log2 domain (scale * log2 e folded into one factor), so exp2.
+//   PV: lane = row d (head_dim / 64 rows per lane), 16-token rows read with
+//       128-bit loads, p broadcast from LDS.
+// Token slots past the sequence end are selected out of the max, the sum and
+// P.V (their bytes may be anything, NaN included).
+//
+// This kernel covers every supported shape and dtype; the matrix-core kernel
+// replaces it for the grouped bf16 / fp8 shapes.
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+template <int KDT> struct Row16;
+
+template <> struct Row16<kF32> {
+  static __device__ __forceinline__ void load(const float* row, float (&v)[16]) {
+    const float4* p = reinterpret_cast<const float4*>(row);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 x = p[i];
+      v[4 * i + 0] = x.x; v[4 * i + 1] = x.y; v[4 * i + 2] = x.z; v[4 * i + 3] = x.w;
+    }
+  }
+};
+
+template <> struct Row16<kBF16> {
+  static __device__ __forceinline__ void load(const uint16_t* row, float (&v)[16]) {
+    const uint4* p = reinterpret_cast<const uint4*>(row);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint4 x = p[i];
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[8 * i + 2 * j + 0] = __uint_as_float(w[j] << 16);
+        v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+      }
+    }
+  }
+};
+
+template <> struct Row16<kE5M2> {
+  static __device__ __forceinline__ void load(const uint8_t* row, float (&v)[16]) {
+    const uint4 x = *reinterpret_cast<const uint4*>(row);
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) v[4 * j + b] = e5m2_to_f32(w[j] >> (8 * b));
+    }
+  }
+};
+
+template <int QDT, int KDT, int D, int G>
+__global__ __launch_bounds__(64) void valu_partition_kernel(const Args a) {
+  using KT = typename Storage<KDT>::type;
+  using QT = typename Storage<QDT>::type;
+  constexpr int BS = kBlockSize;
+  constexpr int DPL = D / 64;
+
+  const int part = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int s = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int L = a.seq_lens[s];
+  const int P = a.partition_tokens;
+  const int nparts = L > 0 ? (L + P - 1) / P : 1;
+  if (part >= nparts) return;
+  const int tok0 = part * P;
+  const int tok1 = min(L, tok0 + P);
+
+  __shared__ float q_s[D][G];
+  __shared__ float p_s[G][BS];
+
+  const QT* qg = static_cast<const QT*>(a.q) + ((int64_t)s * a.num_heads + (int64_t)kvh * G) * D;
+  for (int i = lane; i < G * D; i += 64) q_s[i % D][i / D] = to_f32<QDT>(qg[i]);
+  __syncthreads();
+
+  const int t = lane & 15;
+  const int c = lane >> 4;
+  float m[G], lsum[G], o[G][DPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = -INFINITY;
+    lsum[h] = 0.f;
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) o[h][j] = 0.f;
+  }
+
+  const KT* kc = static_cast<const KT*>(a.k) + (int64_t)kvh * D * BS;
+  const KT* vc = static_cast<const KT*>(a.v) + (int64_t)kvh * D * BS;
+  const int32_t* table = a.tables + (int64_t)s * a.max_blocks;
+
+  for (int blk = tok0 / BS; blk * BS < tok1; ++blk) {
+    const int64_t phys = table[blk];
+    const KT* kb = kc + phys * a.block_stride;
+    const KT* vb = vc + phys * a.block_stride;
+    const int nvalid = min(BS, tok1 - blk * BS);
+
+    float acc[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) acc[h] = 0.f;
+#pragma unroll 8
+    for (int i = 0; i < D / 4; ++i) {
+      const int d = 4 * i + c;
+      const float kv = to_f32<KDT>(kb[d * BS + t]);
+#pragma unroll
+      for (int h = 0; h < G; ++h) acc[h] = fmaf(q_s[d][h], kv, acc[h]);
+    }
+
+    const bool valid = t < nvalid;
+    float alpha[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float x = acc[h];
+      x += shfl_xor_f32(x, 16);
+      x += shfl_xor_f32(x, 32);
+      const float sc = valid ? x * a.score_scale : -INFINITY;
+      float mx = sc;
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, shfl_xor_f32(mx, off));
+      const float m_new = fmaxf(m[h], mx);
+      alpha[h] = exp2f(m[h] - m_new);
+      const float p = valid ? exp2f(sc - m_new) : 0.f;
+      float ps = p;
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) ps += shfl_xor_f32(ps, off);
+      lsum[h] = lsum[h] * alpha[h] + ps;
+      m[h] = m_new;
+      if (c == 0) p_s[h][t] = p;
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) {
+      const int d = lane + 64 * j;
+      float vv[16];
+      Row16<KDT>::load(vb + d * BS, vv);
+#pragma unroll
+      for (int tt = 0; tt < BS; ++tt) vv[tt] = tt < nvalid ? vv[tt] : 0.f;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float pv = 0.f;
+#pragma unroll
+        for (int tt = 0; tt < BS; ++tt) pv = fmaf(p_s[h][tt], vv[tt], pv);
+        o[h][j] = o[h][j] * alpha[h] + pv;
+      }
+    }
+    __syncthreads();
+  }
+
+  if (nparts == 1) {
+    const int64_t obase = ((int64_t)s * a.num_heads + (int64_t)kvh * G) * D;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float inv = lsum[h] > 0.f ? a.v_scale / lsum[h] : 0.f;
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) store_out<QDT>(a.out, obase + (int64_t)h * D + lane + 64 * j, o[h][j] * inv);
+    }
+  } else {
+    const int64_t item = ((int64_t)s * a.num_kv_heads + kvh) * a.max_parts + part;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) a.part_o[(item * G + h) * D + lane + 64 * j] = o[h][j] * a.v_scale;
+      if (lane == 0) {
+        a.part_m[item * G + h] = m[h];
+        a.part_l[item * G + h] = lsum[h];
+      }
+    }
+  }
+}
+
+template <int QDT, int KDT, int D>
+hipError_t launch_g(const Args& a, int group, dim3 grid, hipStream_t st) {
+  switch (group) {
+    case 1: valu_partition_kernel<QDT, KDT, D, 1><<<grid, 64, 0, st>>>(a); break;
+    case 2: valu_partition_kernel<QDT, KDT, D, 2><<<grid, 64, 0, st>>>(a); break;
+    case 4: valu_partition_kernel<QDT, KDT, D, 4><<<grid, 64, 0, st>>>(a); break;
+    case 8: valu_partition_kernel<QDT, KDT, D, 8><<<grid, 64, 0, st>>>(a); break;
+    case 16: valu_partition_kernel<QDT, KDT, D, 16><<<grid, 64, 0, st>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int QDT, int KDT>
+hipError_t launch_d(const Args& a, int head_dim, int group, dim3 grid, hipStream_t st) {
+  if (head_dim == 64) return launch_g<QDT, KDT, 64>(a, group, grid, st);
+  if (head_dim == 128) return launch_g<QDT, KDT, 128>(a, group, grid, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool valu_supported(int q_dtype, int kv_dtype, int head_dim, int group) {
+  const bool types = (q_dtype == kF32 && kv_dtype == kF32) || (q_dtype == kBF16 && kv_dtype == kBF16) ||
+                     (q_dtype == kBF16 && kv_dtype == kE5M2);
+  const bool dims = head_dim == 64 || head_dim == 128;
+  const bool g = group == 1 || group == 2 || group == 4 || group == 8 || group == 16;
+  return types && dims && g;
+}
+
+hipError_t launch_valu(const Args& a, int q_dtype, int kv_dtype, int head_dim, int group,
+                       hipStream_t stream) {
+  const dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
+  if (q_dtype == kF32 && kv_dtype == kF32) return launch_d<kF32, kF32>(a, head_dim, group, grid, stream);
+  if (q_dtype == kBF16 && kv_dtype == kBF16) return launch_d<kBF16, kBF16>(a, head_dim, group, grid, stream);
+  if (q_dtype == kBF16 && kv_dtype == kE5M2) return launch_d<kBF16, kE5M2>(a, head_dim, group, grid, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

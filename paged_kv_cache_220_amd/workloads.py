@@ -25,6 +25,8 @@ from __future__ import annotations
 
 import dataclasses
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from typing import Dict, Optional
 
 import numpy as np
@@ -109,13 +111,28 @@ def to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def _normal_chunked(shape, seed_root, stream: int, dtype: str) -> np.ndarray:
-    """N(0,1) draws of `shape`, rounded to `dtype`, chunk by chunk from child seeds."""
+    """N(0,1) draws of `shape`, rounded to `dtype`, chunk by chunk from child seeds.
+
+    Chunk c always comes from default_rng(seed_root + [stream, c]), so the
+    result does not depend on how many threads fill it.
+    """
     n = int(np.prod(shape))
     out = np.empty(n, dtype=_NP_STORAGE[dtype])
-    for c, start in enumerate(range(0, n, _CHUNK)):
+
+    def fill(c):
+        start = c * _CHUNK
         stop = min(n, start + _CHUNK)
         rng = np.random.default_rng(list(seed_root) + [stream, c])
         out[start:stop] = to_storage(rng.standard_normal(stop - start, dtype=np.float32), dtype)
+
+    nchunks = (n + _CHUNK - 1) // _CHUNK
+    workers = max(1, min(8, len(os.sched_getaffinity(0)), nchunks))
+    if workers == 1:
+        for c in range(nchunks):
+            fill(c)
+    else:
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(fill, range(nchunks)))
     return out.reshape(shape)
 
 
