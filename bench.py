@@ -1,0 +1,277 @@
+#!/usr/bin/env python3
+"""Benchmark: PagedAttention decode on one MI355X.
+
+One step = one decode call (partition kernel + partition-merge kernel) over a
+seeded synthetic batch already resident in HBM. The default workload is the
+long-context bf16 GQA batch: 16 sequences x 32,768 tokens, 64 query / 8 KV
+heads, head_dim 128, block size 16, physical blocks scattered at random.
+
+Prints one JSON line. `value` is the achieved rate of algorithmic K/V bytes
+(token-exact, 2 * Hkv * D * elem bytes per token) in GB/s. `roofline` covers
+the partition kernel, timed with HIP events recorded by the library on the
+launch stream inside the timed region. `cpu_baseline` times the CPU oracle
+on a bounded sample of the same batch.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "PagedAttention decode: achieved HBM GB/s (% of peak) and seq·head/s"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c3", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--replicas", type=int, default=0,
+                    help="copies of the batch cycled through (0: enough for 2 GiB of cache, beating the 256 MB MALL)")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", default="", help="comma list of partition_tokens to time (printed to stderr)")
+    return ap.parse_args()
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime (the library records them)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        evs = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            evs.append(e.value)
+        return evs
+
+    def elapsed_ms(self, a, b):
+        self.hip.hipEventSynchronize(ctypes.c_void_p(b))
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "paged_kv_cache_220_amd", "csrc", "*"))):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()
+
+
+def load_traffic(kernel_name, workload, plan):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they still describe this kernel."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    e = t.get(f"{kernel_name}:{workload}:{plan['partition_tokens']}")
+    if not e or e.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    return e.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s):
+    from oracle import pa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    done, t_total, bytes_done, sh_done = [], 0.0, 0, 0
+    from paged_kv_cache_220_amd import accounting as A
+    order = list(range(w.num_seqs))
+    for s in order:
+        t0 = time.perf_counter()
+        O.paged_decode(w.q, w.k_cache, w.v_cache, w.block_tables, w.seq_lens, w.num_kv_heads, w.scale,
+                       w.q_dtype, w.kv_dtype, k_scale=float(w.k_scale), v_scale=float(w.v_scale), seqs=[s])
+        t_total += time.perf_counter() - t0
+        done.append(s)
+        bytes_done += A.algorithmic_kv_bytes(w.seq_lens[[s]], w.num_kv_heads, w.head_dim, w.kv_dtype)
+        sh_done += w.num_heads
+        if t_total >= budget_s:
+            break
+    return {"value": round(bytes_done / t_total / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(done)} of {w.num_seqs} sequences, all {w.num_heads} heads "
+                      f"({int(w.seq_lens[done].sum())} tokens); fp64 NumPy, {t_total:.2f} s",
+            "seq_head_per_s": round(sh_done / t_total, 3),
+            "cpu_model": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the decode path runs on a single MI355X here "
+              "(multi-GPU sharding is described, not built); rerun with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from paged_kv_cache_220_amd import accounting as A
+    from paged_kv_cache_220_amd import binding as B
+    from paged_kv_cache_220_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(3)
+    B.load_library()
+    dev = torch.device("cuda:0")
+    w = W.make_workload(args.config)
+
+    def upload(x, dtype):
+        if dtype == "f32":
+            return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+        if dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x)).view(torch.float8_e5m2).to(dev)
+
+    kv_bytes = A.algorithmic_kv_bytes(w.seq_lens, w.num_kv_heads, w.head_dim, w.kv_dtype)
+    pool_bytes = 2 * w.k_cache.nbytes
+    R = args.replicas or max(1, int(np.ceil(2 * 2 ** 30 / pool_bytes)))
+    q = upload(w.q, w.q_dtype)
+    tables = torch.from_numpy(w.block_tables).to(dev)
+    seq_lens = torch.from_numpy(w.seq_lens).to(dev)
+    caches = [(upload(w.k_cache, w.kv_dtype), upload(w.v_cache, w.kv_dtype)) for _ in range(R)]
+    out = torch.empty_like(q)
+    kw = dict(kernel=args.kernel, partition_tokens=args.partition_tokens, max_seq_len=w.max_seq_len,
+              k_scale=float(w.k_scale), v_scale=float(w.v_scale))
+    dims = B.make_dims(q, caches[0][0], tables, **kw)
+    plan = B.plan(dims, w.num_kv_heads)
+    ws = B.alloc_workspace(dims, w.num_kv_heads, dev)
+    hip = HipEvents()
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, events=None):
+        k, v = caches[i % R]
+        B.pa_decode(q, k, v, tables, seq_lens, w.num_kv_heads, float(w.scale), out, workspace=ws,
+                    events=events, **kw)
+
+    if args.sweep:
+        for ptok in [int(x) for x in args.sweep.split(",")]:
+            kw2 = dict(kw, partition_tokens=ptok)
+            d2 = B.make_dims(q, caches[0][0], tables, **kw2)
+            ws2 = B.alloc_workspace(d2, w.num_kv_heads, dev)
+            for i in range(3):
+                B.pa_decode(q, caches[i % R][0], caches[i % R][1], tables, seq_lens, w.num_kv_heads,
+                            float(w.scale), out, workspace=ws2, **kw2)
+            ev = hip.create(2)
+            torch.cuda.synchronize()
+            stream_ev0 = torch.cuda.Event(enable_timing=True)
+            stream_ev1 = torch.cuda.Event(enable_timing=True)
+            stream_ev0.record(stream)
+            for i in range(20):
+                B.pa_decode(q, caches[i % R][0], caches[i % R][1], tables, seq_lens, w.num_kv_heads,
+                            float(w.scale), out, workspace=ws2, **kw2)
+            stream_ev1.record(stream)
+            torch.cuda.synchronize()
+            ms = stream_ev0.elapsed_time(stream_ev1) / 20
+            print(f"sweep P={ptok}: {ms * 1e3:.1f} us/step {kv_bytes / ms / 1e6:.1f} GB/s", file=sys.stderr,
+                  flush=True)
+            hip.destroy(ev)
+            del ws2
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = hip.create(3 * K)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(K):
+        step(i, events=(evs[3 * i], evs[3 * i + 1], evs[3 * i + 2]))
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    part_ms = [hip.elapsed_ms(evs[3 * i], evs[3 * i + 1]) for i in range(K)]
+    red_ms = [hip.elapsed_ms(evs[3 * i + 1], evs[3 * i + 2]) for i in range(K)]
+    hip.destroy(evs)
+
+    ms_step = total_ms / K
+    gbs = kv_bytes / (ms_step * 1e-3) / 1e9
+    seq_heads = w.num_seqs * w.num_heads
+    part_avg = float(np.mean(part_ms))
+    achieved = kv_bytes / (part_avg * 1e-3) / 1e9
+    kname = "pa_mfma_partition" if plan["kernel"] == "mfma" else "pa_valu_partition"
+    traffic = load_traffic(kname, args.config, plan)
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.kv_dtype,
+        "data": "synthetic",
+        "config": {"workload": W.CONFIG_TITLES[args.config], "name": args.config,
+                   "num_seqs": w.num_seqs, "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "block_size": w.block_size, "q_dtype": w.q_dtype,
+                   "kv_dtype": w.kv_dtype, "total_tokens": int(w.seq_lens.sum()),
+                   "max_seq_len": w.max_seq_len, "kv_bytes_per_step": kv_bytes, "replicas": R,
+                   "kernel": plan["kernel"], "partition_tokens": plan["partition_tokens"],
+                   "partitions_max": plan["max_partitions"], "grid_workgroups": plan["grid_workgroups"],
+                   "seed": list(w.seed), "parallelism": "single GPU"},
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "seq_head_per_s": round(seq_heads / (ms_step * 1e-3), 1),
+        "wall_ms_per_step": round(wall * 1e3 / K, 5),
+        "partition_kernel_us": round(part_avg * 1e3, 2),
+        "reduce_kernel_us": round(float(np.mean(red_ms)) * 1e3, 2),
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -119,6 +119,13 @@ int run(const void* q, const void* k_cache, const void* v_cache, const int32_t* 
   a.max_blocks = dims->max_blocks_per_seq;
   a.partition_tokens = p.partition_tokens;
   a.max_parts = p.max_parts;
+  {
+    const long long cap_parts = (long long)p.max_parts * p.partition_tokens;
+    const long long cap_table = (long long)dims->max_blocks_per_seq * dims->block_size;
+    const long long cap = cap_parts < cap_table ? cap_parts : cap_table;
+    a.max_tokens = (int32_t)(cap < 0x7fffffffLL ? cap : 0x7fffffffLL);
+  }
+  a.num_blocks = dims->num_blocks;
   a.score_scale = scale * dims->k_scale * 1.4426950408889634f;
   a.v_scale = dims->v_scale;
 

@@ -27,6 +27,8 @@ struct Args {
   int32_t max_blocks;     // block_tables row length
   int32_t partition_tokens;
   int32_t max_parts;
+  int32_t max_tokens;     // min(max_parts * partition_tokens, max_blocks * block_size)
+  int32_t num_blocks;     // physical blocks in each cache
   float score_scale;      // scale * k_scale * log2(e): scores live in the log2 domain
   float v_scale;
 };
@@ -43,5 +45,17 @@ bool mfma_supported(int q_dtype, int kv_dtype, int head_dim, int group, int bloc
 
 constexpr int kBlockSize = 16;     // tokens per physical block handled by the kernels
 constexpr int kTileTokens = 64;    // partition lengths are multiples of this
+
+// Sequence length as the kernels use it. Lengths outside [0, max_tokens]
+// break a documented precondition; clamping keeps every access inside the
+// table, the caches and the workspace (the output is then unspecified).
+__device__ __forceinline__ int clamp_len(const Args& a, int s) {
+  return min(max(a.seq_lens[s], 0), a.max_tokens);
+}
+
+// Physical block id, clamped into the pool for the same reason.
+__device__ __forceinline__ int64_t clamp_block(const Args& a, int32_t id) {
+  return (int64_t)min(max(id, 0), a.num_blocks - 1);
+}
 
 }  // namespace pa

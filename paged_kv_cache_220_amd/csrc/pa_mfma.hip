@@ -37,8 +37,10 @@
 //
 // fp8-e5m2 KV: an E5M2 byte is the top byte of the binary16 of the same
 // value, so v_perm_b32 widens K and V to fp16 exactly and the f16 MFMA runs
-// with q rounded to fp16 (exact for bf16 q in [2^-14, 65504]) and P in fp16.
-// bf16 KV: bf16 MFMA with q exact and P rounded to bf16.
+// with q rounded to fp16 (exact for bf16 q in [2^-14, 65504]).
+// bf16 KV: bf16 MFMA with q exact. In both, P enters the PV product as two
+// 16-bit operands (the rounded weight and its rounding residual), so the
+// weights carry about twice the operand precision into the fp32 accumulator.
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -94,11 +96,15 @@ template <> struct Mfma<kBF16> {
     for (int i = 0; i < 8; ++i) o[i] = static_cast<__bf16>(q[i]);
     return o;
   }
-  static __device__ __forceinline__ op_t p_operand(const float (&p)[8]) {
-    op_t o;
+  // P as a sum of two operands: hi = round(p), lo = round(p - hi), so the PV
+  // product keeps about 16 significant bits of each weight.
+  static __device__ __forceinline__ void p_operands(const float (&p)[8], op_t& hi, op_t& lo) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = static_cast<__bf16>(p[i]);
-    return o;
+    for (int i = 0; i < 8; ++i) {
+      const __bf16 h = static_cast<__bf16>(p[i]);
+      hi[i] = h;
+      lo[i] = static_cast<__bf16>(p[i] - static_cast<float>(h));
+    }
   }
 };
 
@@ -144,11 +150,13 @@ template <> struct Mfma<kE5M2> {
     for (int i = 0; i < 8; ++i) o[i] = static_cast<_Float16>(q[i]);
     return o;
   }
-  static __device__ __forceinline__ op_t p_operand(const float (&p)[8]) {
-    op_t o;
+  static __device__ __forceinline__ void p_operands(const float (&p)[8], op_t& hi, op_t& lo) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = static_cast<_Float16>(p[i]);
-    return o;
+    for (int i = 0; i < 8; ++i) {
+      const _Float16 h = static_cast<_Float16>(p[i]);
+      hi[i] = h;
+      lo[i] = static_cast<_Float16>(p[i] - static_cast<float>(h));
+    }
   }
 };
 
@@ -164,7 +172,7 @@ __global__ __launch_bounds__(64) void mfma_partition_kernel(const Args a, int gr
   const int part = blockIdx.x;
   const int kvh = blockIdx.y;
   const int s = blockIdx.z;
-  const int L = a.seq_lens[s];
+  const int L = clamp_len(a, s);
   const int P = a.partition_tokens;
   const int nparts = L > 0 ? (L + P - 1) / P : 1;
   if (part >= nparts) return;
@@ -212,7 +220,7 @@ __global__ __launch_bounds__(64) void mfma_partition_kernel(const Args a, int gr
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int lb = b0 + k < nblk_part ? b0 + k : b0;
-      boff[k] = (int64_t)table[lb] * blk_bytes;
+      boff[k] = clamp_block(a, table[lb]) * blk_bytes;
     }
     const int64_t kb_off = kblk == 0 ? boff[0] : kblk == 1 ? boff[1] : kblk == 2 ? boff[2] : boff[3];
 
@@ -282,13 +290,13 @@ __global__ __launch_bounds__(64) void mfma_partition_kernel(const Args a, int gr
     for (int dt = 0; dt < 8; ++dt) oacc[dt] *= alpha;
 
     // ---- O^T += V P^T: PV instruction hh takes quartets r = 2hh, 2hh+1
-    op_t pop[2];
+    op_t phi[2], plo[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       float pv[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) pv[i] = p[2 * hh + (i >> 2)][i & 3];
-      pop[hh] = M::p_operand(pv);
+      M::p_operands(pv, phi[hh], plo[hh]);
     }
     if (nvalid < kTile) {
 #pragma unroll
@@ -302,7 +310,11 @@ __global__ __launch_bounds__(64) void mfma_partition_kernel(const Args a, int gr
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) oacc[dt] = M::mma(M::v_operand(vr[dt][hh]), pop[hh], oacc[dt]);
+      for (int hh = 0; hh < 2; ++hh) {
+        const op_t vop = M::v_operand(vr[dt][hh]);
+        oacc[dt] = M::mma(vop, phi[hh], oacc[dt]);
+        oacc[dt] = M::mma(vop, plo[hh], oacc[dt]);
+      }
     }
   }
 

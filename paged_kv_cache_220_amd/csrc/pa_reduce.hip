@@ -21,7 +21,7 @@ template <int QDT>
 __global__ __launch_bounds__(128) void reduce_kernel(const Args a, int head_dim, int group) {
   const int h = blockIdx.x;
   const int s = blockIdx.y;
-  const int L = a.seq_lens[s];
+  const int L = clamp_len(a, s);
   const int P = a.partition_tokens;
   const int nparts = (L + P - 1) / P;
   if (nparts <= 1) return;

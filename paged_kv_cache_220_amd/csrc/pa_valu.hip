@@ -81,7 +81,7 @@ __global__ __launch_bounds__(64) void valu_partition_kernel(const Args a) {
   const int kvh = blockIdx.y;
   const int s = blockIdx.z;
   const int lane = threadIdx.x;
-  const int L = a.seq_lens[s];
+  const int L = clamp_len(a, s);
   const int P = a.partition_tokens;
   const int nparts = L > 0 ? (L + P - 1) / P : 1;
   if (part >= nparts) return;
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(64) void valu_partition_kernel(const Args a) {
   const int32_t* table = a.tables + (int64_t)s * a.max_blocks;
 
   for (int blk = tok0 / BS; blk * BS < tok1; ++blk) {
-    const int64_t phys = table[blk];
+    const int64_t phys = clamp_block(a, table[blk]);
     const KT* kb = kc + phys * a.block_stride;
     const KT* vb = vc + phys * a.block_stride;
     const int nvalid = min(BS, tok1 - blk * BS);
