@@ -14,6 +14,7 @@ using pa::Args;
 constexpr int kVersionMajor = 0;
 constexpr int kVersionMinor = 1;
 constexpr size_t kAlign = 256;
+constexpr int kMaxParts = 65535;   // partitions per sequence: the grid's y dimension
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -40,7 +41,7 @@ int check_dims(const pa_dims_t* d, int32_t hkv) {
   if (!isfinite(d->k_scale) || !isfinite(d->v_scale)) return PA_ERR_SHAPE;
   if (d->kernel < PA_KERNEL_AUTO || d->kernel > PA_KERNEL_MFMA) return PA_ERR_UNSUPPORTED;
   if (d->block_size != pa::kBlockSize) return PA_ERR_UNSUPPORTED;
-  if (d->num_seqs > 65535 || hkv > 65535) return PA_ERR_UNSUPPORTED;  // grid y / z limits
+  if ((long long)d->num_seqs * hkv > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;  // grid x limit
   const int group = d->num_heads / hkv;
   if (!pa::valu_supported(d->q_dtype, d->kv_dtype, d->head_dim, group)) return PA_ERR_UNSUPPORTED;
   if (d->kernel == PA_KERNEL_MFMA &&
@@ -63,15 +64,27 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
   p->max_len = d->max_seq_len > 0 ? d->max_seq_len : d->max_blocks_per_seq * d->block_size;
   int P = d->partition_tokens;
   if (P == 0) {
-    // Long contexts are split so that the grid holds enough independent
-    // (sequence, KV head, partition) items to keep every CU streaming.
+    // Each work item (sequence, KV head, partition) is one wavefront that
+    // keeps one 64-token tile of K and V in flight. Covering HBM latency at
+    // full bandwidth takes about 32 MiB in flight, i.e. 1024 items of 32 KiB
+    // (bf16 / fp32 tiles) or 2048 of 16 KiB (fp8 tiles). Among the partition
+    // lengths that give that many items, the longest is taken: it amortises
+    // each item's start-up and shrinks the partial states the merge reads.
     const long long units = (long long)d->num_seqs * hkv;
-    P = 512;
-    while (P > 128 && units * ((p->max_len + P - 1) / P) < 2048) P /= 2;
+    const long long tile_bytes = 2LL * pa::kTileTokens * d->head_dim * (d->kv_dtype == PA_DTYPE_FP8_E5M2 ? 1 : 2);
+    const long long want = (32LL << 20) / tile_bytes;
+    long long cap = 4096;
+    while (cap / 2 >= p->max_len && cap > pa::kTileTokens) cap /= 2;   // no longer than the longest sequence needs
+    P = (int)cap;
+    while (P > 256 && units * ((p->max_len + P - 1) / P) < want) P /= 2;
+  }
+  if (d->partition_tokens == 0) {
+    while ((p->max_len + (long long)P - 1) / P > kMaxParts) P *= 2;   // grid y limit
   }
   p->partition_tokens = P;
-  p->max_parts = p->max_len > 0 ? (p->max_len + P - 1) / P : 1;
+  p->max_parts = p->max_len > 0 ? (int)((p->max_len + (long long)P - 1) / P) : 1;
   if (p->max_parts < 1) p->max_parts = 1;
+  if (p->max_parts > kMaxParts) return PA_ERR_UNSUPPORTED;
   p->grid = (long long)p->max_parts * hkv * d->num_seqs;
   p->reduce_grid = p->max_parts > 1 ? (long long)d->num_heads * d->num_seqs : 0;
   if (p->max_parts > 1) {

@@ -53,6 +53,28 @@ __device__ __forceinline__ int clamp_len(const Args& a, int s) {
   return min(max(a.seq_lens[s], 0), a.max_tokens);
 }
 
+// Work item of a partition-kernel workgroup. The grid is
+// (num_kv_heads * num_seqs, max_parts): consecutive workgroups differ in KV
+// head and sequence, and the partition index is the slowest. The hardware
+// deals workgroup i to XCD i % 8, so every partition index, and in particular
+// partition 0 that each sequence has, is spread over all eight XCDs whatever
+// the head count or length mix. Partitions are dispatched last index first:
+// the deep partitions that only long sequences have start early, and the
+// first partitions, which include every short sequence, fill the tail.
+struct Item {
+  int kvh, s, part;
+};
+__device__ __forceinline__ Item work_item(const Args& a) {
+  Item it;
+  it.s = blockIdx.x / a.num_kv_heads;
+  it.kvh = blockIdx.x - it.s * a.num_kv_heads;
+  it.part = a.max_parts - 1 - (int)blockIdx.y;
+  return it;
+}
+__host__ __forceinline__ dim3 partition_grid(const Args& a) {
+  return dim3((unsigned)a.num_kv_heads * (unsigned)a.num_seqs, (unsigned)a.max_parts, 1);
+}
+
 // Physical block id, clamped into the pool for the same reason.
 __device__ __forceinline__ int64_t clamp_block(const Args& a, int32_t id) {
   return (int64_t)min(max(id, 0), a.num_blocks - 1);

@@ -90,11 +90,12 @@ template <> struct Mfma<kBF16> {
     }
     return x;
   }
-  static __device__ __forceinline__ op_t q_operand(const float (&q)[8]) {
-    op_t o;
+  // q is bf16 already: the operand is its bits, packed two per register.
+  static __device__ __forceinline__ op_t q_operand(const uint32_t (&qb)[8]) {
+    u32x4 x;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = static_cast<__bf16>(q[i]);
-    return o;
+    for (int w = 0; w < 4; ++w) x[w] = qb[2 * w] | (qb[2 * w + 1] << 16);
+    return __builtin_bit_cast(op_t, x);
   }
   // P as a sum of two operands: hi = round(p), lo = round(p - hi), so the PV
   // product keeps about 16 significant bits of each weight.
@@ -144,10 +145,10 @@ template <> struct Mfma<kE5M2> {
     }
     return x;
   }
-  static __device__ __forceinline__ op_t q_operand(const float (&q)[8]) {
+  static __device__ __forceinline__ op_t q_operand(const uint32_t (&qb)[8]) {
     op_t o;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = static_cast<_Float16>(q[i]);
+    for (int i = 0; i < 8; ++i) o[i] = static_cast<_Float16>(bf16_bits_to_f32(qb[i]));
     return o;
   }
   static __device__ __forceinline__ void p_operands(const float (&p)[8], op_t& hi, op_t& lo) {
@@ -169,9 +170,10 @@ __global__ __launch_bounds__(64) void mfma_partition_kernel(const Args a, int gr
   constexpr int BS = kBlockSize;
   constexpr int64_t kRowBytes = BS * M::kElem;             // one head_dim row of a block tile
 
-  const int part = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int s = blockIdx.z;
+  const Item item = work_item(a);
+  const int part = item.part;
+  const int kvh = item.kvh;
+  const int s = item.s;
   const int L = clamp_len(a, s);
   const int P = a.partition_tokens;
   const int nparts = L > 0 ? (L + P - 1) / P : 1;
@@ -184,16 +186,24 @@ __global__ __launch_bounds__(64) void mfma_partition_kernel(const Args a, int gr
   const int n = lane & 15;   // MFMA row of A (quartet / head_dim row) and column of B (query head)
 
   // Q^T operand: lane (c, n) holds q[head n][32*ks + 4*i + c], i = 0..7.
+  // Lanes of columns n >= G read head 0 and zero it, so all 32 loads issue
+  // back to back without a branch between them.
   op_t qop[kKSteps];
   {
+    const bool head_ok = n < group;
     const uint16_t* qh = static_cast<const uint16_t*>(a.q) +
-                         ((int64_t)s * a.num_heads + (int64_t)kvh * group + n) * kD;
+                         ((int64_t)s * a.num_heads + (int64_t)kvh * group + (head_ok ? n : 0)) * kD;
+    uint32_t qb[kKSteps][8];
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) {
-      float qf[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) qf[i] = n < group ? bf16_bits_to_f32(qh[32 * ks + 4 * i + c]) : 0.f;
-      qop[ks] = M::q_operand(qf);
+      for (int i = 0; i < 8; ++i) qb[ks][i] = qh[32 * ks + 4 * i + c];
+    }
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qb[ks][i] = head_ok ? qb[ks][i] : 0u;
+      qop[ks] = M::q_operand(qb[ks]);
     }
   }
 
@@ -214,38 +224,47 @@ __global__ __launch_bounds__(64) void mfma_partition_kernel(const Args a, int gr
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int t0 = tok0; t0 < tok1; t0 += kTile) {
-    const int b0 = t0 / BS;
-    int64_t boff[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int lb = b0 + k < nblk_part ? b0 + k : b0;
-      boff[k] = clamp_block(a, table[lb]) * blk_bytes;
-    }
-    const int64_t kb_off = kblk == 0 ? boff[0] : kblk == 1 ? boff[1] : kblk == 2 ? boff[2] : boff[3];
+  // Physical ids this lane needs for a tile starting at logical block b0: the
+  // K-load block and the two V-load blocks. Blocks past the partition end are
+  // not looked up; the tile's first block stands in (its tokens are masked).
+  auto tile_ids = [&](int b0, int32_t& idk, int32_t& idv0, int32_t& idv1) {
+    const int bk = b0 + kblk, bv0 = b0 + (c >> 1), bv1 = b0 + (c >> 1) + 2;
+    idk = table[bk < nblk_part ? bk : b0];
+    idv0 = table[bv0 < nblk_part ? bv0 : b0];
+    idv1 = table[bv1 < nblk_part ? bv1 : b0];
+  };
+  int32_t idk, idv0, idv1;
+  tile_ids(tok0 / BS, idk, idv0, idv1);
 
-    // ---- K loads: 4 k-steps x 8 rows, 4 tokens each
+  for (int t0 = tok0; t0 < tok1; t0 += kTile) {
+    const int64_t kb_off = clamp_block(a, idk) * blk_bytes;
+    const int64_t vb_offs[2] = {clamp_block(a, idv0) * blk_bytes, clamp_block(a, idv1) * blk_bytes};
+
+    // ---- K loads: 4 k-steps x 8 rows, 4 tokens each. K/V bytes are used once
+    // per call, so they are loaded non-temporally (streamed past the caches).
     kload_t kr[kKSteps][8];
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int d = 32 * ks + 4 * i + c;
-        kr[ks][i] = *reinterpret_cast<const kload_t*>(kbase + kb_off + d * kRowBytes + ktok * M::kElem);
+        kr[ks][i] = __builtin_nontemporal_load(reinterpret_cast<const kload_t*>(kbase + kb_off + d * kRowBytes + ktok * M::kElem));
       }
     }
     // ---- V loads: 8 row tiles x 2 token halves, 8 tokens each
     vload_t vr[8][2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      const int vb = (c >> 1) + 2 * hh;
-      const int64_t vb_off = vb == 0 ? boff[0] : vb == 1 ? boff[1] : vb == 2 ? boff[2] : boff[3];
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const int d = 16 * dt + n;
-        vr[dt][hh] = *reinterpret_cast<const vload_t*>(vbase + vb_off + d * kRowBytes + 8 * (c & 1) * M::kElem);
+        vr[dt][hh] = __builtin_nontemporal_load(reinterpret_cast<const vload_t*>(vbase + vb_offs[hh] + d * kRowBytes + 8 * (c & 1) * M::kElem));
       }
     }
+    // Next tile's block ids behind this tile's loads; all 48 K/V loads of the
+    // tile are in flight before any compute is scheduled.
+    if (t0 + kTile < tok1) tile_ids((t0 + kTile) / BS, idk, idv0, idv1);
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- S^T = K^T Q^T: MFMA j covers token j of every quartet
     f32x4 sacc[4];
@@ -273,7 +292,7 @@ __global__ __launch_bounds__(64) void mfma_partition_kernel(const Args a, int gr
     tmax = fmaxf(tmax, shfl_xor_f32(tmax, 16));
     tmax = fmaxf(tmax, shfl_xor_f32(tmax, 32));
     const float m_new = fmaxf(m_run, tmax);
-    const float alpha = exp2f(m_run - m_new);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
     float psum = 0.f;
     float p[4][4];
@@ -281,7 +300,7 @@ __global__ __launch_bounds__(64) void mfma_partition_kernel(const Args a, int gr
     for (int r = 0; r < 4; ++r) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        p[r][j] = exp2f(sc[r][j] - m_new);
+        p[r][j] = __builtin_amdgcn_exp2f(sc[r][j] - m_new);
         psum += p[r][j];
       }
     }
@@ -335,13 +354,13 @@ __global__ __launch_bounds__(64) void mfma_partition_kernel(const Args a, int gr
       *reinterpret_cast<u32x2*>(out + 16 * dt + 4 * c) = w;
     }
   } else {
-    const int64_t item = ((int64_t)s * a.num_kv_heads + kvh) * a.max_parts + part;
-    float* po = a.part_o + (item * group + n) * kD;
+    const int64_t slot = ((int64_t)s * a.num_kv_heads + kvh) * a.max_parts + part;
+    float* po = a.part_o + (slot * group + n) * kD;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * c) = oacc[dt] * a.v_scale;
     if (c == 0) {
-      a.part_m[item * group + n] = m_run;
-      a.part_l[item * group + n] = l_tot;
+      a.part_m[slot * group + n] = m_run;
+      a.part_l[slot * group + n] = l_tot;
     }
   }
 }
@@ -356,7 +375,7 @@ bool mfma_supported(int q_dtype, int kv_dtype, int head_dim, int group, int bloc
 hipError_t launch_mfma(const Args& a, int q_dtype, int kv_dtype, int head_dim, int group,
                        hipStream_t stream) {
   if (!mfma_supported(q_dtype, kv_dtype, head_dim, group, kBlockSize)) return hipErrorInvalidValue;
-  const dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
+  const dim3 grid = partition_grid(a);
   if (kv_dtype == kBF16) {
     mfma_partition_kernel<kBF16><<<grid, 64, 0, stream>>>(a, group);
   } else {

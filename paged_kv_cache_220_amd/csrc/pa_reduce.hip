@@ -9,7 +9,11 @@
 // Sequences with a single partition were written directly by the partition
 // kernel and are skipped here.
 //
-// One workgroup per (sequence, query head); one thread per output element.
+// One workgroup of 256 threads per (sequence, query head): 8 partition
+// groups x 32 column groups of 4 output elements. Each thread walks every
+// 8th partition with 128-bit loads of o_p (a wave reads 512 contiguous bytes
+// per partition), then the 8 partial sums meet in LDS in a fixed order, so
+// the result does not depend on timing.
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -17,8 +21,12 @@
 namespace pa {
 namespace {
 
+constexpr int kThreads = 256;
+constexpr int kGroups = 8;          // partition groups
+constexpr int kCols = 32;           // column groups of 4 elements: head_dim <= 128
+
 template <int QDT>
-__global__ __launch_bounds__(128) void reduce_kernel(const Args a, int head_dim, int group) {
+__global__ __launch_bounds__(kThreads) void reduce_kernel(const Args a, int head_dim, int group) {
   const int h = blockIdx.x;
   const int s = blockIdx.y;
   const int L = clamp_len(a, s);
@@ -28,31 +36,70 @@ __global__ __launch_bounds__(128) void reduce_kernel(const Args a, int head_dim,
   const int kvh = h / group;
   const int g = h - kvh * group;
   const int64_t item0 = ((int64_t)s * a.num_kv_heads + kvh) * a.max_parts;
+  const int tid = threadIdx.x;
 
-  float M = -INFINITY;
-  for (int p = 0; p < nparts; ++p) M = fmaxf(M, a.part_m[(item0 + p) * group + g]);
+  __shared__ float red_m[kThreads / 64];
+  __shared__ float red_o[kGroups][kCols * 4];
+  __shared__ float red_l[kGroups];
 
-  for (int d = threadIdx.x; d < head_dim; d += blockDim.x) {
-    float num = 0.f, den = 0.f;
-    for (int p = 0; p < nparts; ++p) {
-      const int64_t it = (item0 + p) * group + g;
-      const float w = exp2f(a.part_m[it] - M);
-      den = fmaf(w, a.part_l[it], den);
-      num = fmaf(w, a.part_o[it * head_dim + d], num);
+  // M = max over partitions (strided over all threads, then wave and LDS reduction)
+  float mloc = -INFINITY;
+  for (int p = tid; p < nparts; p += kThreads) mloc = fmaxf(mloc, a.part_m[(item0 + p) * group + g]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mloc = fmaxf(mloc, shfl_xor_f32(mloc, off));
+  if ((tid & 63) == 0) red_m[tid >> 6] = mloc;
+  __syncthreads();
+  float M = red_m[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) M = fmaxf(M, red_m[w]);
+
+  const int pg = tid / kCols;
+  const int col = (tid % kCols) * 4;
+  const bool active = col < head_dim;
+  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+  float den = 0.f;
+#pragma unroll 2
+  for (int p = pg; p < nparts; p += kGroups) {
+    const int64_t it = (item0 + p) * group + g;
+    const float w = exp2f(a.part_m[it] - M);
+    den = fmaf(w, a.part_l[it], den);
+    if (active) {
+      const float4 o = *reinterpret_cast<const float4*>(a.part_o + it * head_dim + col);
+      num.x = fmaf(w, o.x, num.x);
+      num.y = fmaf(w, o.y, num.y);
+      num.z = fmaf(w, o.z, num.z);
+      num.w = fmaf(w, o.w, num.w);
     }
-    store_out<QDT>(a.out, ((int64_t)s * a.num_heads + h) * head_dim + d, num / den);
+  }
+  if (active) {
+    red_o[pg][col + 0] = num.x;
+    red_o[pg][col + 1] = num.y;
+    red_o[pg][col + 2] = num.z;
+    red_o[pg][col + 3] = num.w;
+  }
+  if (tid % kCols == 0) red_l[pg] = den;
+  __syncthreads();
+
+  if (tid < head_dim) {
+    float acc = 0.f, l = 0.f;
+#pragma unroll
+    for (int k = 0; k < kGroups; ++k) {
+      acc += red_o[k][tid];
+      l += red_l[k];
+    }
+    store_out<QDT>(a.out, ((int64_t)s * a.num_heads + h) * head_dim + tid, acc / l);
   }
 }
 
 }  // namespace
 
 hipError_t launch_reduce(const Args& a, int q_dtype, int head_dim, int group, hipStream_t stream) {
+  if (head_dim > kCols * 4 || head_dim % 4 != 0) return hipErrorInvalidValue;
   const dim3 grid(a.num_heads, a.num_seqs);
-  const int threads = head_dim >= 128 ? 128 : 64;
   if (q_dtype == kF32) {
-    reduce_kernel<kF32><<<grid, threads, 0, stream>>>(a, head_dim, group);
+    reduce_kernel<kF32><<<grid, kThreads, 0, stream>>>(a, head_dim, group);
   } else if (q_dtype == kBF16) {
-    reduce_kernel<kBF16><<<grid, threads, 0, stream>>>(a, head_dim, group);
+    reduce_kernel<kBF16><<<grid, kThreads, 0, stream>>>(a, head_dim, group);
   } else {
     return hipErrorInvalidValue;
   }

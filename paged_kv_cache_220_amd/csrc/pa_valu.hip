@@ -77,9 +77,10 @@ __global__ __launch_bounds__(64) void valu_partition_kernel(const Args a) {
   constexpr int BS = kBlockSize;
   constexpr int DPL = D / 64;
 
-  const int part = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int s = blockIdx.z;
+  const Item item = work_item(a);
+  const int part = item.part;
+  const int kvh = item.kvh;
+  const int s = item.s;
   const int lane = threadIdx.x;
   const int L = clamp_len(a, s);
   const int P = a.partition_tokens;
@@ -177,14 +178,14 @@ __global__ __launch_bounds__(64) void valu_partition_kernel(const Args a) {
       for (int j = 0; j < DPL; ++j) store_out<QDT>(a.out, obase + (int64_t)h * D + lane + 64 * j, o[h][j] * inv);
     }
   } else {
-    const int64_t item = ((int64_t)s * a.num_kv_heads + kvh) * a.max_parts + part;
+    const int64_t slot = ((int64_t)s * a.num_kv_heads + kvh) * a.max_parts + part;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
 #pragma unroll
-      for (int j = 0; j < DPL; ++j) a.part_o[(item * G + h) * D + lane + 64 * j] = o[h][j] * a.v_scale;
+      for (int j = 0; j < DPL; ++j) a.part_o[(slot * G + h) * D + lane + 64 * j] = o[h][j] * a.v_scale;
       if (lane == 0) {
-        a.part_m[item * G + h] = m[h];
-        a.part_l[item * G + h] = lsum[h];
+        a.part_m[slot * G + h] = m[h];
+        a.part_l[slot * G + h] = lsum[h];
       }
     }
   }
@@ -222,7 +223,7 @@ bool valu_supported(int q_dtype, int kv_dtype, int head_dim, int group) {
 
 hipError_t launch_valu(const Args& a, int q_dtype, int kv_dtype, int head_dim, int group,
                        hipStream_t stream) {
-  const dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
+  const dim3 grid = partition_grid(a);
   if (q_dtype == kF32 && kv_dtype == kF32) return launch_d<kF32, kF32>(a, head_dim, group, grid, stream);
   if (q_dtype == kBF16 && kv_dtype == kBF16) return launch_d<kBF16, kBF16>(a, head_dim, group, grid, stream);
   if (q_dtype == kBF16 && kv_dtype == kE5M2) return launch_d<kBF16, kE5M2>(a, head_dim, group, grid, stream);

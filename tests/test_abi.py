@@ -73,7 +73,7 @@ def status_of(d, hkv=8):
     (dict(q_dtype=B.PA_DTYPE_F32), 8, B.PA_ERR_UNSUPPORTED),   # f32 q with bf16 KV
     (dict(q_dtype=B.PA_DTYPE_FP8_E5M2), 8, B.PA_ERR_UNSUPPORTED),
     (dict(kernel=7), 8, B.PA_ERR_UNSUPPORTED),
-    (dict(num_seqs=70000), 8, B.PA_ERR_UNSUPPORTED),
+    (dict(num_seqs=300_000_000), 8, B.PA_ERR_UNSUPPORTED),       # grid x limit
 ])
 def test_validation_statuses(kw, hkv, expect):
     assert status_of(dims(**kw), hkv) == expect
@@ -85,11 +85,19 @@ def test_mfma_request_on_unsupported_shape():
 
 
 def test_plan_long_context():
+    # 16 x 8 (sequence, KV head) units of 32K tokens: 4096-token partitions give
+    # 1024 items of one 32 KiB tile in flight each, the 32 MiB the planner wants
     p = B.plan(dims(), 8)
-    assert p["partition_tokens"] == 512 and p["max_partitions"] == 64
-    assert p["grid_workgroups"] == 64 * 8 * 16 and p["reduce_workgroups"] == 64 * 16
-    items = 16 * 8 * 64 * 8
+    assert p["partition_tokens"] == 4096 and p["max_partitions"] == 8
+    assert p["grid_workgroups"] == 8 * 8 * 16 and p["reduce_workgroups"] == 64 * 16
+    items = 16 * 8 * 8 * 8
     assert p["workspace_bytes"] >= items * (128 + 2) * 4
+    # fp8 tiles are half as large, so twice the items: 2048-token partitions
+    pf = B.plan(dims(num_seqs=128, max_blocks_per_seq=256, kv_dtype=B.PA_DTYPE_FP8_E5M2), 8)
+    assert pf["partition_tokens"] == 2048 and pf["grid_workgroups"] == 2 * 8 * 128
+    # short chat batch: one partition per sequence, no merge
+    pc = B.plan(dims(num_seqs=128, max_blocks_per_seq=32, max_seq_len=507), 8)
+    assert pc["partition_tokens"] == 512 and pc["max_partitions"] == 1 and pc["workspace_bytes"] == 0
     p2 = B.plan(dims(partition_tokens=1024, max_seq_len=4096), 8)
     assert p2["max_partitions"] == 4 and p2["partition_tokens"] == 1024
 
