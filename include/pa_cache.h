@@ -1,0 +1,72 @@
+/*
+ * pa_cache.h - writes into the paged KV cache on MI355X (gfx950): the append
+ * that precedes every decode step and the copy-on-write block copy.
+ *
+ * Append ("Optimização da inferência" page, "Caches de KV": when token N is
+ * generated only its key and value are computed and added to the cache;
+ * vLLM e PagedAttention page: the block-table layout, and the fp8_e5m2 KV
+ * option):
+ *   for every new token i with sequence s = token_seq[i] and logical position
+ *   p = token_pos[i] >= 0, block b = block_tables[s][p / block_size] and slot
+ *   t = p % block_size:
+ *       k_cache[b][g][d][t] = encode(k_new[i][g][d] / k_scale)
+ *       v_cache[b][g][d][t] = encode(v_new[i][g][d] / v_scale)
+ *   for every KV head g and d < head_dim. encode() is the identity for an
+ *   fp32 cache fed fp32, and rounds to nearest even otherwise (bf16, or OCP
+ *   E5M2 with overflow to infinity). For an fp8 cache the division is one
+ *   correctly rounded fp32 division; for other caches the scales must be 1.
+ *   A negative token_pos marks a padding entry that writes nothing.
+ *
+ * Copy on write ("Optimização da inferência" page, "PagedAttention": pages
+ * of a shared prefix are stored once; a request that diverges gets its own):
+ *   for every pair i, physical block dst_blocks[i] of both caches (all KV
+ *   heads, all slots) becomes a copy of block src_blocks[i].
+ *
+ * Layouts are those of pa_decode.h: caches [num_blocks][num_kv_heads]
+ * [head_dim][block_size]; k_new / v_new [num_tokens][num_kv_heads][head_dim]
+ * in in_dtype (F32 or BF16), contiguous, 16-byte aligned; token_seq,
+ * token_pos, src_blocks, dst_blocks int32 device arrays.
+ *
+ * Ownership and errors as in pa_decode.h: caller-owned device memory, work
+ * enqueued on `stream` (hipStream_t as void*) without synchronising, host-side
+ * validation before any HIP call, a pa_status_t result.
+ *
+ * Device-side preconditions (not checked; violations are clamped or skipped
+ * so every access stays in bounds, and the result is then unspecified):
+ *   append: 0 <= token_seq[i] < num_seqs; token_pos[i] < max_blocks_per_seq *
+ *           block_size; the table entries used are valid block ids; no two
+ *           tokens write the same (block, slot).
+ *   copy:   ids in [0, num_blocks); destinations distinct, and no block both
+ *           a source and a destination.
+ */
+#ifndef PA_CACHE_H
+#define PA_CACHE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "pa_decode.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* dims: num_seqs, head_dim, num_blocks, block_size, max_blocks_per_seq,
+ * kv_dtype (cache element type), k_scale, v_scale are read; the rest ignored.
+ * Supported (in_dtype -> kv_dtype): F32->F32, F32->BF16, BF16->BF16,
+ * F32->FP8_E5M2, BF16->FP8_E5M2; head_dim 64 or 128; block_size 16. */
+int pa_cache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                    const int32_t* block_tables, const int32_t* token_seq,
+                    const int32_t* token_pos, int32_t num_tokens, int32_t num_kv_heads,
+                    int32_t in_dtype, const pa_dims_t* dims, void* stream);
+
+/* dims: head_dim, num_blocks, block_size, kv_dtype are read. num_pairs may be 0. */
+int pa_cache_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_blocks,
+                         const int32_t* dst_blocks, int32_t num_pairs, int32_t num_kv_heads,
+                         const pa_dims_t* dims, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_CACHE_H */

@@ -58,6 +58,7 @@ import numpy as np
 __all__ = [
     "decode_bits", "e5m2_value", "logical_kv", "paged_decode", "paged_decode_rows",
     "online_decode", "merge_partials", "dense_attention",
+    "e5m2_encode", "bf16_encode", "encode_bits", "paged_append", "copy_blocks",
 ]
 
 
@@ -256,3 +257,118 @@ def online_decode(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, sca
                      for b0 in range(0, nblk, step)]
             out[s, h] = merge_partials(parts) if parts else 0.0
     return out
+
+
+# ----------------------------------------------------------------------------
+# writing the cache: encoders, the paged append and the block copy
+# ----------------------------------------------------------------------------
+#
+# "Optimização da inferência", "Caches de KV": when token N is generated, only
+# its key and value are computed and appended to the cached ones (the KVCache
+# update of step 1 writes them at the next positions). In the paged layout of
+# the vLLM page the position t of sequence s lives in block
+# block_tables[s][t // bs], slot t % bs. The fp8 cache stores E5M2 bytes
+# (the vLLM page's fp8_e5m2 flag) of value / scale.
+#
+# "PagedAttention" on the same page: pages of a shared prefix are stored once
+# and copied only when a request diverges (copy on write). copy_blocks is that
+# copy: whole physical blocks, every KV head, K and V.
+
+def e5m2_encode(x) -> np.ndarray:
+    """Values (exactly representable in float64) -> OCP E5M2 codes.
+
+    Round to nearest, ties to even; magnitudes that round past the largest
+    finite value (57344) become infinity; NaN keeps its sign and becomes the
+    all-ones NaN code. Follows the format: 5 exponent bits with bias 15, 2
+    mantissa bits, subnormal step 2^-16.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    sign = (np.signbit(x).astype(np.uint16) << 7)
+    a = np.abs(x)
+    code = np.zeros(a.shape, dtype=np.uint16)
+    fin = np.isfinite(a)
+    m, e = np.frexp(np.where(fin, a, 0.0))          # a = m * 2^e, m in [0.5, 1)
+    E = e.astype(np.int64) - 1                      # a = (2m) * 2^E, 2m in [1, 2)
+    normal = fin & (a >= 2.0 ** -14)
+    # normal: q = RNE(a / 2^(E-2)) in [4, 8]; 8 carries into the exponent
+    q = np.round(np.where(normal, a, 0.0) / np.exp2(np.where(normal, E - 2, 0).astype(np.float64)))
+    carry = q >= 8
+    E2 = np.where(carry, E + 1, E)
+    q2 = np.where(carry, 4, q)
+    biased = E2 + 15
+    norm_code = (biased << 2) | (q2.astype(np.int64) - 4)
+    overflow = normal & (biased >= 31)
+    code = np.where(normal & ~overflow, norm_code, code)
+    # subnormal (and zero): q = RNE(a / 2^-16) in [0, 4]; 4 is the smallest normal code
+    sub = fin & (a < 2.0 ** -14)
+    code = np.where(sub, np.round(np.where(sub, a, 0.0) * 2.0 ** 16).astype(np.int64), code)
+    code = np.where(overflow | (np.isinf(a)), 0x7C, code)
+    code = np.where(np.isnan(a), 0x7F, code)
+    return (code.astype(np.uint16) | sign).astype(np.uint8)
+
+
+def bf16_encode(x) -> np.ndarray:
+    """float32 values -> bfloat16 bits, round to nearest even (8 significant bits).
+
+    Overflow past the largest finite bfloat16 rounds to infinity; NaN stays NaN.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    with np.errstate(invalid="ignore"):
+        a = np.abs(x.astype(np.float64))
+    sign = np.signbit(x)
+    fin = np.isfinite(a) & (a > 0)
+    m, e = np.frexp(np.where(fin, a, 1.0))
+    E = e.astype(np.int64) - 1
+    # bfloat16 keeps 8 significant bits down to 2^-126 (then subnormal, step 2^-133)
+    step_exp = np.maximum(E, -126) - 7
+    r = np.round(np.where(fin, a, 0.0) / np.exp2(step_exp.astype(np.float64))) * np.exp2(step_exp.astype(np.float64))
+    r = np.where(fin, r, a)
+    r = np.where(r > 3.3895313892515355e38, np.inf, r)        # past the largest finite bfloat16
+    r = np.where(sign, -r, r)
+    bits = (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    bits = np.where(np.isnan(x), np.uint16(0x7FC0) | (sign.astype(np.uint16) << 15), bits)
+    return bits.astype(np.uint16)
+
+
+def encode_bits(values_f32: np.ndarray, dtype: str, scale: float = 1.0) -> np.ndarray:
+    """float32 values -> cache storage bits. The fp8 code is taken of value / scale,
+    the division done in float32 (one correctly rounded division)."""
+    v = np.asarray(values_f32, dtype=np.float32)
+    if dtype == "f32":
+        return v.copy()
+    if dtype == "bf16":
+        return bf16_encode(v)
+    if dtype == "e5m2":
+        return e5m2_encode((v / np.float32(scale)).astype(np.float64))
+    raise ValueError(dtype)
+
+
+def paged_append(k_new, v_new, k_cache, v_cache, block_tables, token_seq, token_pos,
+                 in_dtype: str, kv_dtype: str, k_scale: float = 1.0, v_scale: float = 1.0):
+    """Write new tokens into copies of the caches; returns (k_cache', v_cache').
+
+    Token i (K/V rows [num_kv_heads, head_dim] in k_new[i], v_new[i]) belongs to
+    sequence token_seq[i] at logical position token_pos[i] >= 0; a negative
+    position marks a padding entry that writes nothing.
+    """
+    k_out, v_out = k_cache.copy(), v_cache.copy()
+    bs = k_cache.shape[3]
+    for i in range(len(token_seq)):
+        pos = int(token_pos[i])
+        if pos < 0:
+            continue
+        blk = int(block_tables[int(token_seq[i]), pos // bs])
+        kv = decode_bits(k_new[i], in_dtype).astype(np.float32)    # [Hkv, D], exact
+        vv = decode_bits(v_new[i], in_dtype).astype(np.float32)
+        k_out[blk, :, :, pos % bs] = encode_bits(kv, kv_dtype, k_scale)
+        v_out[blk, :, :, pos % bs] = encode_bits(vv, kv_dtype, v_scale)
+    return k_out, v_out
+
+
+def copy_blocks(k_cache, v_cache, src, dst):
+    """Copies of the caches with physical block dst[i] replaced by block src[i]."""
+    k_out, v_out = k_cache.copy(), v_cache.copy()
+    for a, b in zip(np.asarray(src), np.asarray(dst)):
+        k_out[int(b)] = k_cache[int(a)]
+        v_out[int(b)] = v_cache[int(a)]
+    return k_out, v_out

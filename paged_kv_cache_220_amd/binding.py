@@ -22,9 +22,9 @@ PA_DTYPE_F32, PA_DTYPE_BF16, PA_DTYPE_FP8_E5M2 = 0, 1, 2
 KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
 KERNEL_NAMES = {v: k for k, v in KERNELS.items()}
 
-# Symbols declared in include/pa_decode.h.
+# Symbols declared in include/pa_decode.h and include/pa_cache.h.
 EXPORTED = ("pa_decode", "pa_decode_ws", "pa_decode_ws_timed", "pa_decode_workspace_bytes",
-            "pa_decode_plan", "pa_status_str", "pa_version")
+            "pa_decode_plan", "pa_status_str", "pa_version", "pa_cache_append", "pa_cache_copy_blocks")
 
 
 class PaDims(ctypes.Structure):
@@ -79,6 +79,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.pa_status_str.restype = ctypes.c_char_p
     lib.pa_version.argtypes = []
     lib.pa_version.restype = ctypes.c_int
+    lib.pa_cache_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, dims_p, vp]
+    lib.pa_cache_append.restype = ctypes.c_int
+    lib.pa_cache_copy_blocks.argtypes = [vp, vp, vp, vp, i32, i32, dims_p, vp]
+    lib.pa_cache_copy_blocks.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -198,3 +202,52 @@ def alloc_workspace(dims: PaDims, num_kv_heads: int, device) -> torch.Tensor:
     n = workspace_bytes(dims, num_kv_heads)
     # torch's caching allocator hands out 512-byte aligned blocks
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def _cache_dims(k_cache: torch.Tensor, block_tables: Optional[torch.Tensor], kv_dtype: Optional[str],
+                k_scale: float, v_scale: float) -> PaDims:
+    NB, _, D, bs = k_cache.shape
+    S, MB = (block_tables.shape if block_tables is not None else (1, 1))
+    return PaDims(num_seqs=S, num_heads=k_cache.shape[1], head_dim=D, num_blocks=NB, block_size=bs,
+                  max_blocks_per_seq=MB, q_dtype=PA_DTYPE_BF16, kv_dtype=_kv_dtype_code(k_cache, kv_dtype),
+                  k_scale=k_scale, v_scale=v_scale, max_seq_len=0, partition_tokens=0, kernel=0)
+
+
+def pa_cache_append(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                    block_tables: torch.Tensor, token_seq: torch.Tensor, token_pos: torch.Tensor, *,
+                    kv_dtype: Optional[str] = None, k_scale: float = 1.0, v_scale: float = 1.0) -> None:
+    """Write new tokens' K/V ([num_tokens, num_kv_heads, head_dim]) into the paged caches in place."""
+    for name, t in (("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("block_tables", block_tables), ("token_seq", token_seq), ("token_pos", token_pos)):
+        if t.device != k_cache.device or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous on the caches' device")
+    if k_new.dtype not in _TORCH_DTYPES or v_new.dtype != k_new.dtype or k_new.shape != v_new.shape:
+        raise TypeError("k_new / v_new: same shape, float32 or bfloat16")
+    if token_seq.dtype != torch.int32 or token_pos.dtype != torch.int32 or block_tables.dtype != torch.int32:
+        raise TypeError("block_tables, token_seq and token_pos must be int32")
+    n, hkv, _ = k_new.shape
+    dims = _cache_dims(k_cache, block_tables, kv_dtype, k_scale, v_scale)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(k_cache.device).cuda_stream)
+    rc = load_library().pa_cache_append(
+        ctypes.c_void_p(k_new.data_ptr()), ctypes.c_void_p(v_new.data_ptr()), ctypes.c_void_p(k_cache.data_ptr()),
+        ctypes.c_void_p(v_cache.data_ptr()), ctypes.c_void_p(block_tables.data_ptr()),
+        ctypes.c_void_p(token_seq.data_ptr()), ctypes.c_void_p(token_pos.data_ptr()), n, hkv,
+        _TORCH_DTYPES[k_new.dtype], ctypes.byref(dims), stream)
+    _check(rc)
+
+
+def pa_cache_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, src_blocks: torch.Tensor,
+                         dst_blocks: torch.Tensor, *, kv_dtype: Optional[str] = None) -> None:
+    """Copy physical blocks src_blocks[i] -> dst_blocks[i] in both caches (in place)."""
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("src_blocks", src_blocks), ("dst_blocks", dst_blocks)):
+        if t.device != k_cache.device or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous on the caches' device")
+    if src_blocks.dtype != torch.int32 or dst_blocks.dtype != torch.int32 or src_blocks.shape != dst_blocks.shape:
+        raise TypeError("src_blocks / dst_blocks: int32 of the same length")
+    dims = _cache_dims(k_cache, None, kv_dtype, 1.0, 1.0)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(k_cache.device).cuda_stream)
+    rc = load_library().pa_cache_copy_blocks(
+        ctypes.c_void_p(k_cache.data_ptr()), ctypes.c_void_p(v_cache.data_ptr()),
+        ctypes.c_void_p(src_blocks.data_ptr()), ctypes.c_void_p(dst_blocks.data_ptr()), src_blocks.numel(),
+        k_cache.shape[1], ctypes.byref(dims), stream)
+    _check(rc)

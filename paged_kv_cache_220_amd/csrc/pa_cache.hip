@@ -1,0 +1,190 @@
+// Writes into the paged KV cache (gfx950): the per-step append of new
+// tokens' K/V through the block table, with encoding to the cache type, and
+// the copy-on-write block copy. Both are small memory-bound scatters/copies;
+// the append's stores follow the cache layout, whose tokens are the fastest
+// axis, so one token touches one element in each head_dim row.
+
+#include <math.h>
+
+#include "pa_cache.h"
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+// float -> OCP E5M2, round to nearest even, overflow to infinity, NaN kept.
+__device__ __forceinline__ uint8_t f32_to_e5m2(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return static_cast<uint8_t>(sign | 0x7Fu);      // NaN
+  if (a >= 0x47700000u) return static_cast<uint8_t>(sign | 0x7Cu);     // |x| >= 61440 rounds past 57344
+  if (a >= 0x38800000u) {                                               // |x| >= 2^-14: normal code
+    const uint32_t r = a + 0xFFFFFu + ((a >> 21) & 1u);                 // keep 2 mantissa bits, ties to even
+    return static_cast<uint8_t>(sign | ((r >> 21) - (112u << 2)));      // rebias 127 -> 15
+  }
+  // subnormal step 2^-16; the scaling is exact and rint rounds ties to even
+  const float q = rintf(__uint_as_float(a) * 65536.0f);
+  return static_cast<uint8_t>(sign | static_cast<uint32_t>(q));
+}
+
+template <int IN> __device__ __forceinline__ float load_in(const void* p, int64_t i);
+template <> __device__ __forceinline__ float load_in<kF32>(const void* p, int64_t i) {
+  return static_cast<const float*>(p)[i];
+}
+template <> __device__ __forceinline__ float load_in<kBF16>(const void* p, int64_t i) {
+  return bf16_bits_to_f32(static_cast<const uint16_t*>(p)[i]);
+}
+
+template <int KV> __device__ __forceinline__ void store_kv(void* cache, int64_t i, float x, float scale);
+template <> __device__ __forceinline__ void store_kv<kF32>(void* cache, int64_t i, float x, float) {
+  static_cast<float*>(cache)[i] = x;
+}
+template <> __device__ __forceinline__ void store_kv<kBF16>(void* cache, int64_t i, float x, float) {
+  static_cast<uint16_t*>(cache)[i] = f32_to_bf16_bits(x);
+}
+template <> __device__ __forceinline__ void store_kv<kE5M2>(void* cache, int64_t i, float x, float scale) {
+  static_cast<uint8_t*>(cache)[i] = f32_to_e5m2(x / scale);
+}
+
+struct AppendArgs {
+  const void* k_new;
+  const void* v_new;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* tables;
+  const int32_t* token_seq;
+  const int32_t* token_pos;
+  int32_t num_tokens, num_kv_heads, head_dim, num_seqs, max_blocks, num_blocks;
+  float k_scale, v_scale;
+};
+
+// One wavefront per (token, KV head); lane d writes rows d and d + 64.
+template <int IN, int KV>
+__global__ __launch_bounds__(64) void append_kernel(const AppendArgs a) {
+  const int i = blockIdx.x;
+  const int g = blockIdx.y;
+  const int s = a.token_seq[i];
+  const int pos = a.token_pos[i];
+  if (pos < 0 || s < 0 || s >= a.num_seqs || pos >= a.max_blocks * kBlockSize) return;
+  int32_t id = a.tables[(int64_t)s * a.max_blocks + pos / kBlockSize];
+  id = min(max(id, 0), a.num_blocks - 1);
+  const int slot = pos % kBlockSize;
+  const int64_t src = ((int64_t)i * a.num_kv_heads + g) * a.head_dim;
+  const int64_t dst = (((int64_t)id * a.num_kv_heads + g) * a.head_dim) * kBlockSize + slot;
+  for (int d = threadIdx.x; d < a.head_dim; d += 64) {
+    store_kv<KV>(a.k_cache, dst + (int64_t)d * kBlockSize, load_in<IN>(a.k_new, src + d), a.k_scale);
+    store_kv<KV>(a.v_cache, dst + (int64_t)d * kBlockSize, load_in<IN>(a.v_new, src + d), a.v_scale);
+  }
+}
+
+struct CopyArgs {
+  char* k_cache;
+  char* v_cache;
+  const int32_t* src;
+  const int32_t* dst;
+  int64_t block_bytes;   // one physical block, all KV heads
+  int32_t num_blocks;
+};
+
+constexpr int kCopyThreads = 256;
+constexpr int kCopyChunk = kCopyThreads * 16;   // bytes per workgroup
+
+// Grid (pair, chunk of the block, cache): 128-bit loads and stores.
+__global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(const CopyArgs a) {
+  const int i = blockIdx.x;
+  const int64_t off = (int64_t)blockIdx.y * kCopyChunk + (int64_t)threadIdx.x * 16;
+  if (off >= a.block_bytes) return;
+  const int64_t sb = min(max(a.src[i], 0), a.num_blocks - 1);
+  const int64_t db = min(max(a.dst[i], 0), a.num_blocks - 1);
+  char* base = blockIdx.z == 0 ? a.k_cache : a.v_cache;
+  const uint4 x = *reinterpret_cast<const uint4*>(base + sb * a.block_bytes + off);
+  *reinterpret_cast<uint4*>(base + db * a.block_bytes + off) = x;
+}
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
+
+int elem_bytes(int dtype) { return dtype == kF32 ? 4 : dtype == kBF16 ? 2 : 1; }
+
+int check_cache_dims(const pa_dims_t* d, int32_t hkv) {
+  if (d == nullptr) return PA_ERR_NULL;
+  if (d->head_dim <= 0 || d->num_blocks <= 0 || d->block_size <= 0 || hkv <= 0) return PA_ERR_SHAPE;
+  if (d->block_size != kBlockSize) return PA_ERR_UNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (d->kv_dtype != kF32 && d->kv_dtype != kBF16 && d->kv_dtype != kE5M2) return PA_ERR_UNSUPPORTED;
+  if (hkv > 65535) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+}  // namespace
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" int pa_cache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                               const int32_t* block_tables, const int32_t* token_seq,
+                               const int32_t* token_pos, int32_t num_tokens, int32_t num_kv_heads,
+                               int32_t in_dtype, const pa_dims_t* dims, void* stream) {
+  int st = check_cache_dims(dims, num_kv_heads);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0 || dims->num_seqs <= 0 || dims->max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
+  const int kv = dims->kv_dtype;
+  const bool combo = (in_dtype == kF32 && (kv == kF32 || kv == kBF16 || kv == kE5M2)) ||
+                     (in_dtype == kBF16 && (kv == kBF16 || kv == kE5M2));
+  if (!combo) return PA_ERR_UNSUPPORTED;
+  if (!isfinite(dims->k_scale) || !isfinite(dims->v_scale) || dims->k_scale == 0.f || dims->v_scale == 0.f)
+    return PA_ERR_SHAPE;
+  if (kv != kE5M2 && (dims->k_scale != 1.f || dims->v_scale != 1.f)) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !k_cache || !v_cache || !block_tables || !token_seq || !token_pos) return PA_ERR_NULL;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(block_tables, 4) || !aligned(token_seq, 4) || !aligned(token_pos, 4))
+    return PA_ERR_ALIGN;
+  AppendArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.tables = block_tables;
+  a.token_seq = token_seq;
+  a.token_pos = token_pos;
+  a.num_tokens = num_tokens;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = dims->head_dim;
+  a.num_seqs = dims->num_seqs;
+  a.max_blocks = dims->max_blocks_per_seq;
+  a.num_blocks = dims->num_blocks;
+  a.k_scale = dims->k_scale;
+  a.v_scale = dims->v_scale;
+  const dim3 grid(num_tokens, num_kv_heads);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (in_dtype == kF32 && kv == kF32) append_kernel<kF32, kF32><<<grid, 64, 0, s>>>(a);
+  else if (in_dtype == kF32 && kv == kBF16) append_kernel<kF32, kBF16><<<grid, 64, 0, s>>>(a);
+  else if (in_dtype == kF32 && kv == kE5M2) append_kernel<kF32, kE5M2><<<grid, 64, 0, s>>>(a);
+  else if (in_dtype == kBF16 && kv == kBF16) append_kernel<kBF16, kBF16><<<grid, 64, 0, s>>>(a);
+  else append_kernel<kBF16, kE5M2><<<grid, 64, 0, s>>>(a);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+extern "C" int pa_cache_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_blocks,
+                                    const int32_t* dst_blocks, int32_t num_pairs, int32_t num_kv_heads,
+                                    const pa_dims_t* dims, void* stream) {
+  int st = check_cache_dims(dims, num_kv_heads);
+  if (st != PA_OK) return st;
+  if (num_pairs < 0) return PA_ERR_SHAPE;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !src_blocks || !dst_blocks) return PA_ERR_NULL;
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(src_blocks, 4) || !aligned(dst_blocks, 4))
+    return PA_ERR_ALIGN;
+  CopyArgs a;
+  a.k_cache = static_cast<char*>(k_cache);
+  a.v_cache = static_cast<char*>(v_cache);
+  a.src = src_blocks;
+  a.dst = dst_blocks;
+  a.block_bytes = (int64_t)num_kv_heads * dims->head_dim * dims->block_size * elem_bytes(dims->kv_dtype);
+  a.num_blocks = dims->num_blocks;
+  const dim3 grid(num_pairs, (unsigned)((a.block_bytes + kCopyChunk - 1) / kCopyChunk), 2);
+  copy_blocks_kernel<<<grid, kCopyThreads, 0, static_cast<hipStream_t>(stream)>>>(a);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
