@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--op", default="decode", choices=["decode", "append", "copy"],
+                    help="decode (default): the attention hot path; append / copy: the cache writes")
     ap.add_argument("--config", default="c3", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--partition-tokens", type=int, default=0)
@@ -165,6 +167,8 @@ def main():
         sys.exit(3)
     B.load_library()
     dev = torch.device("cuda:0")
+    if args.op != "decode":
+        return bench_cache_op(args, dev)
     if args.copy_probe:
         n = args.copy_probe << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)
@@ -288,6 +292,86 @@ def main():
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+def _timed(fn, steps, warmup, stream):
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def bench_cache_op(args, dev):
+    """Cache writes: the bulk append of a whole batch, or a copy-on-write of many blocks."""
+    import torch
+    from oracle import pa_oracle as O
+    from paged_kv_cache_220_amd import binding as B
+    from paged_kv_cache_220_amd import workloads as W
+
+    stream = torch.cuda.current_stream(dev)
+    to_dev = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+    if args.op == "append":
+        # every token of the chat batch (128 seqs, 256..512 tokens, 8 KV heads x 128) appended into a bf16 cache
+        w = W.make_workload("c2")
+        rng = np.random.default_rng([220, 2, 9])
+        token_seq = np.repeat(np.arange(w.num_seqs, dtype=np.int32), w.seq_lens)
+        token_pos = np.concatenate([np.arange(L, dtype=np.int32) for L in w.seq_lens])
+        n = len(token_seq)
+        kn = W.to_storage(rng.standard_normal((n, w.num_kv_heads, w.head_dim), dtype=np.float32), "bf16")
+        vn = W.to_storage(rng.standard_normal((n, w.num_kv_heads, w.head_dim), dtype=np.float32), "bf16")
+        kd, vd = to_dev(w.k_cache), to_dev(w.v_cache)
+        knd, vnd = to_dev(kn), to_dev(vn)
+        td = torch.from_numpy(w.block_tables).to(dev)
+        tsd, tpd = torch.from_numpy(token_seq).to(dev), torch.from_numpy(token_pos).to(dev)
+        fn = lambda i: B.pa_cache_append(knd, vnd, kd, vd, td, tsd, tpd)
+        alg = 2 * n * w.num_kv_heads * w.head_dim * (2 + 2)          # read new K/V, write the cache slots
+        metric = "paged KV append: achieved HBM GB/s"
+        workload = f"bulk append of the chat batch: {n} tokens, 8 KV heads x 128, bf16 -> bf16 cache"
+        units = n
+        cpu = lambda: O.paged_append(kn[:2000], vn[:2000], w.k_cache, w.v_cache, w.block_tables,
+                                     token_seq[:2000], token_pos[:2000], "bf16", "bf16")
+        cpu_units, cpu_bytes = 2000, alg * 2000 // n
+    else:
+        w = W.make_workload("c3")
+        rng = np.random.default_rng([220, 3, 9])
+        perm = rng.permutation(w.num_blocks).astype(np.int32)
+        npairs = 4096
+        src, dst = perm[:npairs], perm[npairs:2 * npairs]
+        kd, vd = to_dev(w.k_cache), to_dev(w.v_cache)
+        sd, dd = torch.from_numpy(src).to(dev), torch.from_numpy(dst).to(dev)
+        fn = lambda i: B.pa_cache_copy_blocks(kd, vd, sd, dd)
+        block_bytes = w.num_kv_heads * w.head_dim * w.block_size * 2
+        alg = 2 * 2 * npairs * block_bytes                           # K and V, read and write
+        metric = "copy-on-write block copy: achieved HBM GB/s"
+        workload = f"copy of {npairs} random block pairs of the long-context pool (32 KiB per block per cache)"
+        units = npairs
+        cpu = lambda: O.copy_blocks(w.k_cache, w.v_cache, src[:512], dst[:512])
+        cpu_units, cpu_bytes = 512, alg * 512 // npairs
+    ms = _timed(fn, args.steps, args.warmup, stream)
+    gbs = alg / (ms * 1e-3) / 1e9
+    t0 = time.perf_counter()
+    reps = 0
+    while time.perf_counter() - t0 < min(args.cpu_budget, 5.0) or reps == 0:
+        cpu()
+        reps += 1
+    cpu_s = (time.perf_counter() - t0) / reps
+    result = {"metric": metric, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+              "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+              "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+              "config": {"workload": workload, "op": args.op, "bytes_per_step": alg, "units": units},
+              "roofline": {"bound": "hbm", "kernel": f"pa_cache_{args.op}", "achieved": round(gbs, 2),
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                           "traffic": None},
+              "cpu_baseline": {"value": round(cpu_bytes / cpu_s / 1e9, 4), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle", "sample": f"{cpu_units} of {units} units, {reps} repetitions"}}
     print(json.dumps(result), flush=True)
 
 

@@ -94,6 +94,14 @@ typedef struct pa_dims {
   int32_t partition_tokens;    /* context-partition length; 0 = chosen by the library,
                                   else a positive multiple of 64                      */
   int32_t kernel;              /* pa_kernel_t                                          */
+  int32_t q_len;               /* query positions per sequence; 0 or 1 = decode. With
+                                  q_len > 1, q and out are [num_seqs][q_len][num_heads]
+                                  [head_dim], seq_lens count the q_len new tokens, and
+                                  query i attends tokens t < seq_lens[s] - q_len + 1 + i
+                                  (the causal mask of the inference page's attention
+                                  with several query rows; a query with no token gets
+                                  a zero row). Matrix-core kernel only:
+                                  group * q_len <= 64.                                  */
 } pa_dims_t;
 
 /* Decode with a workspace the library takes from the stream-ordered allocator

@@ -59,6 +59,7 @@ __all__ = [
     "decode_bits", "e5m2_value", "logical_kv", "paged_decode", "paged_decode_rows",
     "online_decode", "merge_partials", "dense_attention",
     "e5m2_encode", "bf16_encode", "encode_bits", "paged_append", "copy_blocks",
+    "paged_attention_multi",
 ]
 
 
@@ -372,3 +373,47 @@ def copy_blocks(k_cache, v_cache, src, dst):
         k_out[int(b)] = k_cache[int(a)]
         v_out[int(b)] = v_cache[int(a)]
     return k_out, v_out
+
+
+# ----------------------------------------------------------------------------
+# several query positions per sequence (chunked prefill, speculative verify)
+# ----------------------------------------------------------------------------
+#
+# "Optimização da inferência", step 2: with more than one query row the
+# attention adds a causal mask, -1e9 on the scores of keys past each query's
+# own position: the q_len queries are the last q_len positions of the
+# sequence, and query i may attend keys j <= L - q_len + i. The large negative
+# addend only removes those keys from the softmax; here they are left out.
+# Speculative decoding verifies several candidate tokens in one pass, and
+# chunked prefill feeds a prompt in pieces (same page; vLLM page flags), which
+# is this computation over the paged cache.
+
+def paged_attention_multi(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale,
+                          q_dtype: str, kv_dtype: str, k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
+    """q [S, q_len, H, D] -> float64 [S, q_len, H, D].
+
+    seq_lens[s] counts every token in the cache, the q_len new ones included.
+    Query i of sequence s attends tokens t < seq_lens[s] - q_len + 1 + i (zero row if none).
+    """
+    S, QL, H, D = q.shape
+    if H % num_kv_heads:
+        raise ValueError("num_heads must be a multiple of num_kv_heads")
+    G = H // num_kv_heads
+    sc64 = float(np.float32(scale))
+    out = np.zeros((S, QL, H, D), dtype=np.float64)
+    for s in range(S):
+        L = int(seq_lens[s])
+        if L == 0:
+            continue
+        for g in range(num_kv_heads):
+            K = logical_kv(k_cache, block_tables, s, L, g, kv_dtype, k_scale)
+            V = logical_kv(v_cache, block_tables, s, L, g, kv_dtype, v_scale)
+            for i in range(QL):
+                n = L - QL + 1 + i
+                if n <= 0:
+                    continue
+                qg = decode_bits(q[s, i, g * G:(g + 1) * G], q_dtype)       # [G, D]
+                sc = sc64 * (qg @ K[:n].T)
+                w = np.exp(sc - sc.max(axis=1, keepdims=True))
+                out[s, i, g * G:(g + 1) * G] = (w @ V[:n]) / w.sum(axis=1, keepdims=True)
+    return out

@@ -33,7 +33,7 @@ class PaDims(ctypes.Structure):
                 ("max_blocks_per_seq", ctypes.c_int32), ("q_dtype", ctypes.c_int32),
                 ("kv_dtype", ctypes.c_int32), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
                 ("max_seq_len", ctypes.c_int32), ("partition_tokens", ctypes.c_int32),
-                ("kernel", ctypes.c_int32)]
+                ("kernel", ctypes.c_int32), ("q_len", ctypes.c_int32)]
 
 
 class PaPlan(ctypes.Structure):
@@ -114,16 +114,19 @@ def _kv_dtype_code(t: torch.Tensor, kv_dtype: Optional[str]) -> int:
 def make_dims(q: torch.Tensor, k_cache: torch.Tensor, block_tables: torch.Tensor, *,
               kv_dtype: Optional[str] = None, max_seq_len: int = 0, partition_tokens: int = 0,
               kernel: str = "auto", k_scale: float = 1.0, v_scale: float = 1.0) -> PaDims:
-    if q.dim() != 3 or k_cache.dim() != 4 or block_tables.dim() != 2:
-        raise ValueError("q [S,H,D], k_cache [NB,Hkv,D,bs], block_tables [S,max_blocks] expected")
+    if q.dim() not in (3, 4) or k_cache.dim() != 4 or block_tables.dim() != 2:
+        raise ValueError("q [S,H,D] or [S,q_len,H,D], k_cache [NB,Hkv,D,bs], block_tables [S,max_blocks] expected")
     if q.dtype not in _TORCH_DTYPES:
         raise TypeError(f"unsupported q dtype {q.dtype}")
-    S, H, D = q.shape
+    if q.dim() == 4:
+        S, QL, H, D = q.shape
+    else:
+        (S, H, D), QL = q.shape, 1
     NB, _, _, bs = k_cache.shape
     return PaDims(num_seqs=S, num_heads=H, head_dim=D, num_blocks=NB, block_size=bs,
                   max_blocks_per_seq=block_tables.shape[1], q_dtype=_TORCH_DTYPES[q.dtype],
                   kv_dtype=_kv_dtype_code(k_cache, kv_dtype), k_scale=k_scale, v_scale=v_scale,
-                  max_seq_len=max_seq_len, partition_tokens=partition_tokens, kernel=KERNELS[kernel])
+                  max_seq_len=max_seq_len, partition_tokens=partition_tokens, kernel=KERNELS[kernel], q_len=QL)
 
 
 def plan(dims: PaDims, num_kv_heads: int) -> dict:
@@ -165,6 +168,9 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, blo
               kernel: str = "auto", k_scale: float = 1.0, v_scale: float = 1.0,
               workspace: Optional[torch.Tensor] = None, events=None) -> torch.Tensor:
     """PagedAttention decode through the C ABI; returns `out`.
+
+    q may be [S, H, D] (one query per sequence) or [S, q_len, H, D] (the last
+    q_len positions of each sequence, causally masked).
 
     `workspace` (uint8 cuda tensor) selects ``pa_decode_ws``; without it the
     library takes its workspace from the stream-ordered allocator.

@@ -22,12 +22,15 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 struct Plan {
   int kernel = PA_KERNEL_VALU;
   int group = 1;
+  int q_len = 1;
   int max_len = 0;
   int partition_tokens = 0;
   int max_parts = 1;
   size_t off_m = 0, off_l = 0, ws_bytes = 0;
   long long grid = 0, reduce_grid = 0;
 };
+
+int q_len_of(const pa_dims_t* d) { return d->q_len > 1 ? d->q_len : 1; }
 
 int check_dims(const pa_dims_t* d, int32_t hkv) {
   if (d == nullptr) return PA_ERR_NULL;
@@ -39,14 +42,18 @@ int check_dims(const pa_dims_t* d, int32_t hkv) {
   if ((long long)d->max_seq_len > (long long)d->max_blocks_per_seq * d->block_size) return PA_ERR_SHAPE;
   if (d->partition_tokens % pa::kTileTokens != 0) return PA_ERR_SHAPE;
   if (!isfinite(d->k_scale) || !isfinite(d->v_scale)) return PA_ERR_SHAPE;
+  if (d->q_len < 0) return PA_ERR_SHAPE;
   if (d->kernel < PA_KERNEL_AUTO || d->kernel > PA_KERNEL_MFMA) return PA_ERR_UNSUPPORTED;
   if (d->block_size != pa::kBlockSize) return PA_ERR_UNSUPPORTED;
   if ((long long)d->num_seqs * hkv > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;  // grid x limit
   const int group = d->num_heads / hkv;
-  if (!pa::valu_supported(d->q_dtype, d->kv_dtype, d->head_dim, group)) return PA_ERR_UNSUPPORTED;
-  if (d->kernel == PA_KERNEL_MFMA &&
-      !pa::mfma_supported(d->q_dtype, d->kv_dtype, d->head_dim, group, d->block_size))
-    return PA_ERR_UNSUPPORTED;
+  const int ql = q_len_of(d);
+  if ((long long)d->num_heads * ql > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;   // merge grid x
+  const bool valu_ok = ql == 1 && pa::valu_supported(d->q_dtype, d->kv_dtype, d->head_dim, group);
+  const bool mfma_ok = pa::mfma_supported(d->q_dtype, d->kv_dtype, d->head_dim, group, d->block_size, ql);
+  if (d->kernel == PA_KERNEL_VALU && !valu_ok) return PA_ERR_UNSUPPORTED;
+  if (d->kernel == PA_KERNEL_MFMA && !mfma_ok) return PA_ERR_UNSUPPORTED;
+  if (!valu_ok && !mfma_ok) return PA_ERR_UNSUPPORTED;
   return PA_OK;
 }
 
@@ -54,8 +61,9 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
   const int st = check_dims(d, hkv);
   if (st != PA_OK) return st;
   p->group = d->num_heads / hkv;
+  p->q_len = q_len_of(d);
   if (d->kernel == PA_KERNEL_AUTO) {
-    p->kernel = pa::mfma_supported(d->q_dtype, d->kv_dtype, d->head_dim, p->group, d->block_size)
+    p->kernel = pa::mfma_supported(d->q_dtype, d->kv_dtype, d->head_dim, p->group, d->block_size, p->q_len)
                     ? PA_KERNEL_MFMA
                     : PA_KERNEL_VALU;
   } else {
@@ -86,9 +94,9 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
   if (p->max_parts < 1) p->max_parts = 1;
   if (p->max_parts > kMaxParts) return PA_ERR_UNSUPPORTED;
   p->grid = (long long)p->max_parts * hkv * d->num_seqs;
-  p->reduce_grid = p->max_parts > 1 ? (long long)d->num_heads * d->num_seqs : 0;
+  p->reduce_grid = p->max_parts > 1 ? (long long)d->num_heads * p->q_len * d->num_seqs : 0;
   if (p->max_parts > 1) {
-    const size_t items = (size_t)d->num_seqs * hkv * p->max_parts * p->group;
+    const size_t items = (size_t)d->num_seqs * hkv * p->max_parts * p->group * p->q_len;
     const size_t o_bytes = items * d->head_dim * sizeof(float);
     p->off_m = align_up(o_bytes, kAlign);
     p->off_l = p->off_m + align_up(items * sizeof(float), kAlign);
@@ -141,6 +149,7 @@ int run(const void* q, const void* k_cache, const void* v_cache, const int32_t* 
   a.num_blocks = dims->num_blocks;
   a.score_scale = scale * dims->k_scale * 1.4426950408889634f;
   a.v_scale = dims->v_scale;
+  a.q_len = p.q_len;
 
   if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return PA_ERR_HIP;
   hipError_t e = p.kernel == PA_KERNEL_MFMA

@@ -17,9 +17,9 @@ struct Args {
   const int32_t* tables;
   const int32_t* seq_lens;
   void* out;
-  float* part_o;   // [S][Hkv][max_parts][G][D]   unnormalised partition outputs
-  float* part_m;   // [S][Hkv][max_parts][G]      partition running max (log2 domain)
-  float* part_l;   // [S][Hkv][max_parts][G]      partition running sum
+  float* part_o;   // [S][Hkv][max_parts][G*q_len][D]   unnormalised partition outputs
+  float* part_m;   // [S][Hkv][max_parts][G*q_len]      partition running max (log2 domain)
+  float* part_l;   // [S][Hkv][max_parts][G*q_len]      partition running sum
   int64_t block_stride;   // elements per physical block: Hkv * D * block_size
   int32_t num_seqs;
   int32_t num_heads;
@@ -31,6 +31,7 @@ struct Args {
   int32_t num_blocks;     // physical blocks in each cache
   float score_scale;      // scale * k_scale * log2(e): scores live in the log2 domain
   float v_scale;
+  int32_t q_len;          // query positions per sequence (1 = decode)
 };
 
 // Host-side launchers; each returns the hipError_t of the launch.
@@ -41,10 +42,11 @@ hipError_t launch_mfma(const Args& a, int q_dtype, int kv_dtype, int head_dim, i
 hipError_t launch_reduce(const Args& a, int q_dtype, int head_dim, int group, hipStream_t stream);
 
 bool valu_supported(int q_dtype, int kv_dtype, int head_dim, int group);
-bool mfma_supported(int q_dtype, int kv_dtype, int head_dim, int group, int block_size);
+bool mfma_supported(int q_dtype, int kv_dtype, int head_dim, int group, int block_size, int q_len);
 
 constexpr int kBlockSize = 16;     // tokens per physical block handled by the kernels
 constexpr int kTileTokens = 64;    // partition lengths are multiples of this
+constexpr int kMaxColumnGroups = 4; // matrix-core kernel: group * q_len <= 64
 
 // Sequence length as the kernels use it. Lengths outside [0, max_tokens]
 // break a documented precondition; clamping keeps every access inside the

@@ -161,8 +161,16 @@ template <> struct Mfma<kE5M2> {
   }
 };
 
-template <int KDT>
-__global__ __launch_bounds__(64) void mfma_partition_kernel(const Args a, int group) {
+// Query columns. Query position qi (0 <= qi < q_len) of query head kvh*G + h
+// is "virtual head" v = qi*G + h, placed on MFMA column v % 16 of column group
+// v / 16; NCG groups cover G * q_len <= 16 * NCG. All groups share each K and
+// V operand, so a tile is read once whatever the number of queries. With one
+// query (decode) and G <= 16 there is a single group.
+// One column group fits two waves per SIMD (<= 256 registers per lane), so
+// one wave's compute overlaps the other's loads; more groups take one wave.
+template <int KDT, int NCG>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCG == 1 ? 2 : 1, 8)))
+void mfma_partition_kernel(const Args a, int group) {
   using M = Mfma<KDT>;
   using op_t = typename M::op_t;
   using kload_t = typename M::kload_t;
@@ -175,6 +183,8 @@ __global__ __launch_bounds__(64) void mfma_partition_kernel(const Args a, int gr
   const int kvh = item.kvh;
   const int s = item.s;
   const int L = clamp_len(a, s);
+  const int QL = a.q_len;
+  const int GV = group * QL;                               // virtual heads of this KV head
   const int P = a.partition_tokens;
   const int nparts = L > 0 ? (L + P - 1) / P : 1;
   if (part >= nparts) return;
@@ -183,16 +193,22 @@ __global__ __launch_bounds__(64) void mfma_partition_kernel(const Args a, int gr
 
   const int lane = threadIdx.x;
   const int c = lane >> 4;   // lane group: k slots of the operands, rows 4c..4c+3 of results
-  const int n = lane & 15;   // MFMA row of A (quartet / head_dim row) and column of B (query head)
+  const int n = lane & 15;   // MFMA row of A (quartet / head_dim row) and column of B (virtual head)
 
-  // Q^T operand: lane (c, n) holds q[head n][32*ks + 4*i + c], i = 0..7.
-  // Lanes of columns n >= G read head 0 and zero it, so all 32 loads issue
-  // back to back without a branch between them.
-  op_t qop[kKSteps];
-  {
-    const bool head_ok = n < group;
+  // Q^T operands: lane (c, n) of group cg holds q[query qi][head h][32*ks + 4*i + c],
+  // i = 0..7. Columns past the last virtual head read a valid row and zero it, so
+  // all loads issue back to back without a branch between them.
+  op_t qop[NCG][kKSteps];
+  int lim[NCG];                // tokens the column's query may attend: t < lim
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+    const int v = 16 * cg + n;
+    const bool col_ok = v < GV;
+    const int qi = col_ok ? v / group : 0;
+    const int h = col_ok ? v - qi * group : 0;
+    lim[cg] = col_ok ? L - QL + 1 + qi : 0;
     const uint16_t* qh = static_cast<const uint16_t*>(a.q) +
-                         ((int64_t)s * a.num_heads + (int64_t)kvh * group + (head_ok ? n : 0)) * kD;
+                         (((int64_t)s * QL + qi) * a.num_heads + (int64_t)kvh * group + h) * kD;
     uint32_t qb[kKSteps][8];
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) {
@@ -202,8 +218,8 @@ __global__ __launch_bounds__(64) void mfma_partition_kernel(const Args a, int gr
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) qb[ks][i] = head_ok ? qb[ks][i] : 0u;
-      qop[ks] = M::q_operand(qb[ks]);
+      for (int i = 0; i < 8; ++i) qb[ks][i] = col_ok ? qb[ks][i] : 0u;
+      qop[cg][ks] = M::q_operand(qb[ks]);
     }
   }
 
@@ -218,11 +234,16 @@ __global__ __launch_bounds__(64) void mfma_partition_kernel(const Args a, int gr
   const int32_t* table = a.tables + (int64_t)s * a.max_blocks;
   const int nblk_part = (tok1 + BS - 1) / BS;   // logical blocks that hold partition tokens
 
-  float m_run = -INFINITY;   // running max of head n (log2 domain), same in all lane groups
-  float l_run = 0.f;         // this lane group's share of the running sum
-  f32x4 oacc[8];
+  float m_run[NCG];          // running max per column (log2 domain), same in all lane groups
+  float l_run[NCG];          // this lane group's share of the running sum
+  f32x4 oacc[NCG][8];
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int cg = 0; cg < NCG; ++cg) {
+    m_run[cg] = -INFINITY;
+    l_run[cg] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) oacc[cg][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   // Physical ids this lane needs for a tile starting at logical block b0: the
   // K-load block and the two V-load blocks. Blocks past the partition end are
@@ -266,57 +287,70 @@ __global__ __launch_bounds__(64) void mfma_partition_kernel(const Args a, int gr
     if (t0 + kTile < tok1) tile_ids((t0 + kTile) / BS, idk, idv0, idv1);
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- S^T = K^T Q^T: MFMA j covers token j of every quartet
-    f32x4 sacc[4];
+    // ---- S^T = K^T Q^T: MFMA j covers token j of every quartet; the K operand
+    // is shared by all column groups
+    f32x4 sacc[NCG][4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks) sacc[j] = M::mma(M::k_operand(kr[ks], j), qop[ks], sacc[j]);
+      for (int ks = 0; ks < kKSteps; ++ks) {
+        const op_t kop = M::k_operand(kr[ks], j);
+#pragma unroll
+        for (int cg = 0; cg < NCG; ++cg)
+          sacc[cg][j] = M::mma(kop, qop[cg][ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[cg][j]);
+      }
     }
 
-    // ---- online softmax for head n over this tile
+    // ---- online softmax per column over this tile
+    op_t phi[NCG][2], plo[NCG][2];
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) {
+      const int nval = min(tok1, lim[cg]) - t0;   // this column's tokens in the tile (may be <= 0)
+      float sc[4][4];                             // [r][j]; tokens outside the window: -inf
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tt = 16 * ((c >> 1) + 2 * (r >> 1)) + 8 * (c & 1) + 4 * (r & 1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sc[r][j] = (tt + j < nval) ? sacc[cg][j][r] * a.score_scale : -INFINITY;
+          tmax = fmaxf(tmax, sc[r][j]);
+        }
+      }
+      tmax = fmaxf(tmax, shfl_xor_f32(tmax, 16));
+      tmax = fmaxf(tmax, shfl_xor_f32(tmax, 32));
+      const float m_new = fmaxf(m_run[cg], tmax);
+      // A column with no token yet keeps m = -inf. Subtracting 0 instead of -inf
+      // then makes every weight and the rescale 2^-inf = 0, so its state stays
+      // zero and -inf - -inf is never formed.
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run[cg] - m_use);
+      m_run[cg] = m_new;
+      float psum = 0.f;
+      float p[4][4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          p[r][j] = __builtin_amdgcn_exp2f(sc[r][j] - m_use);
+          psum += p[r][j];
+        }
+      }
+      l_run[cg] = l_run[cg] * alpha + psum;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) oacc[cg][dt] *= alpha;
+      // PV instruction hh takes quartets r = 2hh, 2hh+1
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        float pv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pv[i] = p[2 * hh + (i >> 2)][i & 3];
+        M::p_operands(pv, phi[cg][hh], plo[cg][hh]);
+      }
+    }
+
+    // ---- O^T += V P^T
     const int nvalid = tok1 - t0;   // tokens of this tile inside the partition (may exceed 64)
-    float sc[4][4];                 // [r][j]
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int tt = 16 * ((c >> 1) + 2 * (r >> 1)) + 8 * (c & 1) + 4 * (r & 1);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float x = sacc[j][r] * a.score_scale;
-        sc[r][j] = (tt + j < nvalid) ? x : -INFINITY;
-        tmax = fmaxf(tmax, sc[r][j]);
-      }
-    }
-    tmax = fmaxf(tmax, shfl_xor_f32(tmax, 16));
-    tmax = fmaxf(tmax, shfl_xor_f32(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    float psum = 0.f;
-    float p[4][4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        p[r][j] = __builtin_amdgcn_exp2f(sc[r][j] - m_new);
-        psum += p[r][j];
-      }
-    }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) oacc[dt] *= alpha;
-
-    // ---- O^T += V P^T: PV instruction hh takes quartets r = 2hh, 2hh+1
-    op_t phi[2], plo[2];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      float pv[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pv[i] = p[2 * hh + (i >> 2)][i & 3];
-      M::p_operands(pv, phi[hh], plo[hh]);
-    }
     if (nvalid < kTile) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
@@ -331,55 +365,74 @@ __global__ __launch_bounds__(64) void mfma_partition_kernel(const Args a, int gr
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const op_t vop = M::v_operand(vr[dt][hh]);
-        oacc[dt] = M::mma(vop, phi[hh], oacc[dt]);
-        oacc[dt] = M::mma(vop, plo[hh], oacc[dt]);
+#pragma unroll
+        for (int cg = 0; cg < NCG; ++cg) {
+          oacc[cg][dt] = M::mma(vop, phi[cg][hh], oacc[cg][dt]);
+          oacc[cg][dt] = M::mma(vop, plo[cg][hh], oacc[cg][dt]);
+        }
       }
     }
   }
 
-  // ---- epilogue: lane (c, n) holds O^T[16*dt + 4*c + r][head n]
-  float l_tot = l_run;
-  l_tot += shfl_xor_f32(l_tot, 16);
-  l_tot += shfl_xor_f32(l_tot, 32);
-  if (n >= group) return;
-  if (nparts == 1) {
-    const float inv = l_tot > 0.f ? a.v_scale / l_tot : 0.f;
-    const int64_t orow = ((int64_t)s * a.num_heads + (int64_t)kvh * group + n) * kD;
-    uint16_t* out = static_cast<uint16_t*>(a.out) + orow;
+  // ---- epilogue: lane (c, n) of group cg holds O^T[16*dt + 4*c + r][virtual head 16*cg + n]
+  float l_tot[NCG];
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      u32x2 w;
-      w[0] = uint32_t(f32_to_bf16_bits(oacc[dt][0] * inv)) | (uint32_t(f32_to_bf16_bits(oacc[dt][1] * inv)) << 16);
-      w[1] = uint32_t(f32_to_bf16_bits(oacc[dt][2] * inv)) | (uint32_t(f32_to_bf16_bits(oacc[dt][3] * inv)) << 16);
-      *reinterpret_cast<u32x2*>(out + 16 * dt + 4 * c) = w;
-    }
-  } else {
-    const int64_t slot = ((int64_t)s * a.num_kv_heads + kvh) * a.max_parts + part;
-    float* po = a.part_o + (slot * group + n) * kD;
+  for (int cg = 0; cg < NCG; ++cg) {
+    l_tot[cg] = l_run[cg];
+    l_tot[cg] += shfl_xor_f32(l_tot[cg], 16);
+    l_tot[cg] += shfl_xor_f32(l_tot[cg], 32);
+  }
+  const int64_t slot = ((int64_t)s * a.num_kv_heads + kvh) * a.max_parts + part;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * c) = oacc[dt] * a.v_scale;
-    if (c == 0) {
-      a.part_m[slot * group + n] = m_run;
-      a.part_l[slot * group + n] = l_tot;
+  for (int cg = 0; cg < NCG; ++cg) {
+    const int v = 16 * cg + n;
+    if (v >= GV) continue;
+    if (nparts == 1) {
+      const int qi = v / group;
+      const int h = v - qi * group;
+      const float inv = l_tot[cg] > 0.f ? a.v_scale / l_tot[cg] : 0.f;
+      uint16_t* out = static_cast<uint16_t*>(a.out) +
+                      (((int64_t)s * QL + qi) * a.num_heads + (int64_t)kvh * group + h) * kD;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        u32x2 w;
+        w[0] = uint32_t(f32_to_bf16_bits(oacc[cg][dt][0] * inv)) | (uint32_t(f32_to_bf16_bits(oacc[cg][dt][1] * inv)) << 16);
+        w[1] = uint32_t(f32_to_bf16_bits(oacc[cg][dt][2] * inv)) | (uint32_t(f32_to_bf16_bits(oacc[cg][dt][3] * inv)) << 16);
+        *reinterpret_cast<u32x2*>(out + 16 * dt + 4 * c) = w;
+      }
+    } else {
+      float* po = a.part_o + (slot * GV + v) * kD;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * c) = oacc[cg][dt] * a.v_scale;
+      if (c == 0) {
+        a.part_m[slot * GV + v] = m_run[cg];
+        a.part_l[slot * GV + v] = l_tot[cg];
+      }
     }
   }
 }
 
 }  // namespace
 
-bool mfma_supported(int q_dtype, int kv_dtype, int head_dim, int group, int block_size) {
+bool mfma_supported(int q_dtype, int kv_dtype, int head_dim, int group, int block_size, int q_len) {
   return q_dtype == kBF16 && (kv_dtype == kBF16 || kv_dtype == kE5M2) && head_dim == kD &&
-         block_size == kBlockSize && group >= 1 && group <= 16;
+         block_size == kBlockSize && group >= 1 && q_len >= 1 && group * q_len <= 16 * kMaxColumnGroups;
 }
 
 hipError_t launch_mfma(const Args& a, int q_dtype, int kv_dtype, int head_dim, int group,
                        hipStream_t stream) {
-  if (!mfma_supported(q_dtype, kv_dtype, head_dim, group, kBlockSize)) return hipErrorInvalidValue;
+  if (!mfma_supported(q_dtype, kv_dtype, head_dim, group, kBlockSize, a.q_len)) return hipErrorInvalidValue;
   const dim3 grid = partition_grid(a);
+  const int gv = group * a.q_len;
+  const int ncg = gv <= 16 ? 1 : gv <= 32 ? 2 : 4;
   if (kv_dtype == kBF16) {
-    mfma_partition_kernel<kBF16><<<grid, 64, 0, stream>>>(a, group);
+    if (ncg == 1) mfma_partition_kernel<kBF16, 1><<<grid, 64, 0, stream>>>(a, group);
+    else if (ncg == 2) mfma_partition_kernel<kBF16, 2><<<grid, 64, 0, stream>>>(a, group);
+    else mfma_partition_kernel<kBF16, 4><<<grid, 64, 0, stream>>>(a, group);
   } else {
-    mfma_partition_kernel<kE5M2><<<grid, 64, 0, stream>>>(a, group);
+    if (ncg == 1) mfma_partition_kernel<kE5M2, 1><<<grid, 64, 0, stream>>>(a, group);
+    else if (ncg == 2) mfma_partition_kernel<kE5M2, 2><<<grid, 64, 0, stream>>>(a, group);
+    else mfma_partition_kernel<kE5M2, 4><<<grid, 64, 0, stream>>>(a, group);
   }
   return hipGetLastError();
 }

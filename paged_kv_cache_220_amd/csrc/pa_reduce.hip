@@ -9,6 +9,10 @@
 // Sequences with a single partition were written directly by the partition
 // kernel and are skipped here.
 //
+// With several query positions per sequence, (query position, head) pairs are
+// merged alike; a query whose window holds no token in any partition gets a
+// zero row.
+//
 // One workgroup of 256 threads per (sequence, query head): 8 partition
 // groups x 32 column groups of 4 output elements. Each thread walks every
 // 8th partition with 128-bit loads of o_p (a wave reads 512 contiguous bytes
@@ -27,15 +31,18 @@ constexpr int kCols = 32;           // column groups of 4 elements: head_dim <= 
 
 template <int QDT>
 __global__ __launch_bounds__(kThreads) void reduce_kernel(const Args a, int head_dim, int group) {
-  const int h = blockIdx.x;
+  const int qi = blockIdx.x / a.num_heads;          // query position (0 for decode)
+  const int h = blockIdx.x - qi * a.num_heads;
   const int s = blockIdx.y;
   const int L = clamp_len(a, s);
   const int P = a.partition_tokens;
   const int nparts = (L + P - 1) / P;
   if (nparts <= 1) return;
   const int kvh = h / group;
-  const int g = h - kvh * group;
+  const int GV = group * a.q_len;                     // virtual heads (query position, head) per KV head
+  const int g = qi * group + (h - kvh * group);
   const int64_t item0 = ((int64_t)s * a.num_kv_heads + kvh) * a.max_parts;
+  const int64_t orow = (((int64_t)s * a.q_len + qi) * a.num_heads + h) * head_dim;
   const int tid = threadIdx.x;
 
   __shared__ float red_m[kThreads / 64];
@@ -44,7 +51,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(const Args a, int head
 
   // M = max over partitions (strided over all threads, then wave and LDS reduction)
   float mloc = -INFINITY;
-  for (int p = tid; p < nparts; p += kThreads) mloc = fmaxf(mloc, a.part_m[(item0 + p) * group + g]);
+  for (int p = tid; p < nparts; p += kThreads) mloc = fmaxf(mloc, a.part_m[(item0 + p) * GV + g]);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) mloc = fmaxf(mloc, shfl_xor_f32(mloc, off));
   if ((tid & 63) == 0) red_m[tid >> 6] = mloc;
@@ -52,6 +59,11 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(const Args a, int head
   float M = red_m[0];
 #pragma unroll
   for (int w = 1; w < kThreads / 64; ++w) M = fmaxf(M, red_m[w]);
+  if (M == -INFINITY) {
+    // no partition saw a token this query may attend (query window longer than the sequence)
+    if (tid < head_dim) store_out<QDT>(a.out, orow + tid, 0.f);
+    return;
+  }
 
   const int pg = tid / kCols;
   const int col = (tid % kCols) * 4;
@@ -60,7 +72,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(const Args a, int head
   float den = 0.f;
 #pragma unroll 2
   for (int p = pg; p < nparts; p += kGroups) {
-    const int64_t it = (item0 + p) * group + g;
+    const int64_t it = (item0 + p) * GV + g;
     const float w = exp2f(a.part_m[it] - M);
     den = fmaf(w, a.part_l[it], den);
     if (active) {
@@ -87,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(const Args a, int head
       acc += red_o[k][tid];
       l += red_l[k];
     }
-    store_out<QDT>(a.out, ((int64_t)s * a.num_heads + h) * head_dim + tid, acc / l);
+    store_out<QDT>(a.out, orow + tid, acc / l);
   }
 }
 
@@ -95,7 +107,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(const Args a, int head
 
 hipError_t launch_reduce(const Args& a, int q_dtype, int head_dim, int group, hipStream_t stream) {
   if (head_dim > kCols * 4 || head_dim % 4 != 0) return hipErrorInvalidValue;
-  const dim3 grid(a.num_heads, a.num_seqs);
+  const dim3 grid(a.num_heads * a.q_len, a.num_seqs);
   if (q_dtype == kF32) {
     reduce_kernel<kF32><<<grid, kThreads, 0, stream>>>(a, head_dim, group);
   } else if (q_dtype == kBF16) {

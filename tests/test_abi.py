@@ -49,7 +49,7 @@ def test_missing_library_fails_loudly(tmp_path):
 def dims(**kw):
     d = dict(num_seqs=16, num_heads=64, head_dim=128, num_blocks=32768, block_size=16, max_blocks_per_seq=2048,
              q_dtype=B.PA_DTYPE_BF16, kv_dtype=B.PA_DTYPE_BF16, k_scale=1.0, v_scale=1.0, max_seq_len=0,
-             partition_tokens=0, kernel=0)
+             partition_tokens=0, kernel=0, q_len=0)
     d.update(kw)
     return B.PaDims(**d)
 
@@ -71,11 +71,17 @@ def status_of(d, hkv=8):
     (dict(k_scale=float("inf")), 8, B.PA_ERR_SHAPE),
     (dict(block_size=32), 8, B.PA_ERR_UNSUPPORTED),
     (dict(head_dim=96), 8, B.PA_ERR_UNSUPPORTED),
-    (dict(num_heads=24), 8, B.PA_ERR_UNSUPPORTED),            # group 3
+    (dict(num_heads=24), 8, B.PA_OK),                          # group 3: matrix-core kernel
+    (dict(num_heads=24, head_dim=64), 8, B.PA_ERR_UNSUPPORTED),  # group 3, vector kernel only
     (dict(q_dtype=B.PA_DTYPE_F32), 8, B.PA_ERR_UNSUPPORTED),   # f32 q with bf16 KV
     (dict(q_dtype=B.PA_DTYPE_FP8_E5M2), 8, B.PA_ERR_UNSUPPORTED),
     (dict(kernel=7), 8, B.PA_ERR_UNSUPPORTED),
     (dict(num_seqs=300_000_000), 8, B.PA_ERR_UNSUPPORTED),       # grid x limit
+    (dict(q_len=-1), 8, B.PA_ERR_SHAPE),
+    (dict(q_len=8), 8, B.PA_OK),                                 # 8 heads x 8 positions: 4 column groups
+    (dict(q_len=9), 8, B.PA_ERR_UNSUPPORTED),                    # 72 virtual heads
+    (dict(q_len=2, kernel=1), 8, B.PA_ERR_UNSUPPORTED),          # vector kernel: one query only
+    (dict(q_len=2, head_dim=64), 8, B.PA_ERR_UNSUPPORTED),
 ])
 def test_validation_statuses(kw, hkv, expect):
     assert status_of(dims(**kw), hkv) == expect
@@ -143,7 +149,7 @@ def test_missing_or_small_workspace_rejected():
 def cdims(**kw):
     d = dict(num_seqs=4, num_heads=8, head_dim=128, num_blocks=100, block_size=16, max_blocks_per_seq=8,
              q_dtype=B.PA_DTYPE_BF16, kv_dtype=B.PA_DTYPE_BF16, k_scale=1.0, v_scale=1.0, max_seq_len=0,
-             partition_tokens=0, kernel=0)
+             partition_tokens=0, kernel=0, q_len=0)
     d.update(kw)
     return B.PaDims(**d)
 

@@ -356,3 +356,48 @@ def test_kv_size_formula_matches_page_example():
     # one layer of that model: 2 * 8 * 128 * 2 bytes per token, the figure the decode kernel reads
     assert A.kv_bytes_per_token_layer(8, 128, "bf16") * m["num_layers"] == g["bytes_per_token"]
     assert g["gqa_query_heads"] // g["gqa_kv_heads"] == g["gqa_kv_saving"]
+
+
+# ------------------------------------------------- several query positions --
+
+def _masked_sdpa_pages_form(qrows, K, V, scale):
+    """The inference page's attention with seq_len_q > 1: additive -1e9 upper-triangular mask."""
+    Lq, Lk = qrows.shape[0], K.shape[0]
+    scores = (qrows @ K.T) * scale
+    mask = np.triu(np.ones((Lq, Lk)), k=Lk - Lq + 1)
+    scores = scores + mask * (-1e9)
+    e = np.exp(scores - scores.max(axis=-1, keepdims=True))
+    return (e / e.sum(axis=-1, keepdims=True)) @ V
+
+
+@pytest.mark.parametrize("ql", [1, 2, 5])
+def test_multi_query_matches_masked_dense_form(ql):
+    w = W.make_workload("c2", num_seqs=3)
+    rng = np.random.default_rng(ql)
+    q = W.to_storage(rng.standard_normal((3, ql, 64, 128), dtype=np.float32), "bf16")
+    got = O.paged_attention_multi(q, w.k_cache, w.v_cache, w.block_tables, w.seq_lens, 8, w.scale, "bf16", "bf16")
+    for s in range(3):
+        L = int(w.seq_lens[s])
+        for g in range(8):
+            K = O.logical_kv(w.k_cache, w.block_tables, s, L, g, "bf16")
+            V = O.logical_kv(w.v_cache, w.block_tables, s, L, g, "bf16")
+            for h in range(g * 8, g * 8 + 8):
+                ref = _masked_sdpa_pages_form(O.decode_bits(q[s, :, h], "bf16"), K, V, float(np.float32(w.scale)))
+                assert np.allclose(got[s, :, h], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_multi_query_rows_are_prefix_decodes():
+    w = W.make_workload("c5", num_seqs=2, seq_len=300)
+    rng = np.random.default_rng(4)
+    ql = 4
+    q = W.to_storage(rng.standard_normal((2, ql, 64, 128), dtype=np.float32), "bf16")
+    got = O.paged_attention_multi(q, w.k_cache, w.v_cache, w.block_tables, w.seq_lens, 8, w.scale, "bf16", "e5m2")
+    for i in range(ql):
+        lens = (w.seq_lens - (ql - 1 - i)).astype(np.int32)
+        ref = O.paged_decode(np.ascontiguousarray(q[:, i]), w.k_cache, w.v_cache, w.block_tables, lens, 8, w.scale,
+                             "bf16", "e5m2")
+        assert np.array_equal(got[:, i], ref)
+    # a sequence shorter than the query window: early queries see nothing
+    short = O.paged_attention_multi(q, w.k_cache, w.v_cache, w.block_tables, np.array([2, 300], np.int32), 8,
+                                    w.scale, "bf16", "e5m2")
+    assert np.all(short[0, :2] == 0) and np.any(short[0, 2:] != 0)

@@ -19,7 +19,15 @@ pytestmark = pytest.mark.gpu
 
 
 def kernels_for(w):
-    ks = ["valu"]
+    ks = []
+    try:
+        B.plan(B.PaDims(num_seqs=w.num_seqs, num_heads=w.num_heads, head_dim=w.head_dim, num_blocks=w.num_blocks,
+                        block_size=w.block_size, max_blocks_per_seq=w.max_blocks_per_seq,
+                        q_dtype=B._KV_NAMES[w.q_dtype], kv_dtype=B._KV_NAMES[w.kv_dtype], k_scale=1.0, v_scale=1.0,
+                        max_seq_len=0, partition_tokens=0, kernel=B.KERNELS["valu"]), w.num_kv_heads)
+        ks.append("valu")
+    except B.PagedAttentionError:
+        pass
     dims = B.PaDims(num_seqs=w.num_seqs, num_heads=w.num_heads, head_dim=w.head_dim, num_blocks=w.num_blocks,
                     block_size=w.block_size, max_blocks_per_seq=w.max_blocks_per_seq,
                     q_dtype=B._KV_NAMES[w.q_dtype], kv_dtype=B._KV_NAMES[w.kv_dtype], k_scale=1.0, v_scale=1.0,
@@ -54,6 +62,8 @@ EDGE = [
     ("bf16 G2 D64", dict(S=3, H=8, Hkv=4, D=64, seq_lens=[5, 70, 300])),
     ("bf16 G4 D128", dict(S=3, H=8, Hkv=2, D=128, seq_lens=[31, 97, 513])),
     ("bf16 G16 D128", dict(S=3, H=32, Hkv=2, D=128, seq_lens=[2, 100, 700])),
+    ("bf16 G3 D128", dict(S=3, H=6, Hkv=2, D=128, seq_lens=[7, 64, 450])),
+    ("e5m2 G5 D128", dict(S=2, H=10, Hkv=2, D=128, seq_lens=[30, 333], kv_dtype="e5m2")),
     ("f32 G1 D64", dict(S=5, H=2, Hkv=2, D=64, seq_lens=[0, 1, 16, 17, 400], q_dtype="f32", kv_dtype="f32")),
     ("f32 G8 D128", dict(S=3, H=16, Hkv=2, D=128, seq_lens=[3, 64, 190], q_dtype="f32", kv_dtype="f32")),
     ("e5m2 G8 D128", dict(S=5, H=16, Hkv=2, D=128, seq_lens=[1, 16, 17, 64, 333], kv_dtype="e5m2")),
