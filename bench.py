@@ -43,6 +43,7 @@ def parse():
     ap.add_argument("--config", default="c3", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--schedule", default="auto", choices=["auto", "grid", "queue"])
     ap.add_argument("--replicas", type=int, default=0,
                     help="copies of the batch cycled through (0: enough for 2 GiB of cache, beating the 256 MB MALL)")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for cpu_baseline")
@@ -196,17 +197,18 @@ def main():
     caches = [(upload(w.k_cache, w.kv_dtype), upload(w.v_cache, w.kv_dtype)) for _ in range(R)]
     out = torch.empty_like(q)
     kw = dict(kernel=args.kernel, partition_tokens=args.partition_tokens, max_seq_len=w.max_seq_len,
-              k_scale=float(w.k_scale), v_scale=float(w.v_scale))
+              k_scale=float(w.k_scale), v_scale=float(w.v_scale), schedule=args.schedule)
     dims = B.make_dims(q, caches[0][0], tables, **kw)
     plan = B.plan(dims, w.num_kv_heads)
     ws = B.alloc_workspace(dims, w.num_kv_heads, dev)
     hip = HipEvents()
     stream = torch.cuda.current_stream(dev)
+    # arguments marshalled once per replica: a step costs the host one library call
+    calls = [B.DecodeCall(q, k, v, tables, seq_lens, w.num_kv_heads, float(w.scale), out, workspace=ws, **kw)
+             for (k, v) in caches]
 
     def step(i, events=None):
-        k, v = caches[i % R]
-        B.pa_decode(q, k, v, tables, seq_lens, w.num_kv_heads, float(w.scale), out, workspace=ws,
-                    events=events, **kw)
+        calls[i % R](events)
 
     if args.sweep:
         for ptok in [int(x) for x in args.sweep.split(",")]:
@@ -278,7 +280,7 @@ def main():
                    "head_dim": w.head_dim, "block_size": w.block_size, "q_dtype": w.q_dtype,
                    "kv_dtype": w.kv_dtype, "total_tokens": int(w.seq_lens.sum()),
                    "max_seq_len": w.max_seq_len, "kv_bytes_per_step": kv_bytes, "replicas": R,
-                   "kernel": plan["kernel"], "partition_tokens": plan["partition_tokens"],
+                   "kernel": plan["kernel"], "schedule": plan["schedule"], "partition_tokens": plan["partition_tokens"],
                    "partitions_max": plan["max_partitions"], "grid_workgroups": plan["grid_workgroups"],
                    "seed": list(w.seed), "parallelism": "single GPU"},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),

@@ -54,7 +54,7 @@ extern "C" {
 /* dims: num_seqs, head_dim, num_blocks, block_size, max_blocks_per_seq,
  * kv_dtype (cache element type), k_scale, v_scale are read; the rest ignored.
  * Supported (in_dtype -> kv_dtype): F32->F32, F32->BF16, BF16->BF16,
- * F32->FP8_E5M2, BF16->FP8_E5M2; head_dim 64 or 128; block_size 16. */
+ * F32 or BF16 -> FP8_E5M2 or FP8_E4M3; head_dim 64 or 128; block_size 16. */
 int pa_cache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                     const int32_t* block_tables, const int32_t* token_seq,
                     const int32_t* token_pos, int32_t num_tokens, int32_t num_kv_heads,

@@ -65,19 +65,30 @@ typedef enum pa_status {
 typedef enum pa_dtype {
   PA_DTYPE_F32 = 0,
   PA_DTYPE_BF16 = 1,      /* bfloat16; outputs rounded to nearest even              */
-  PA_DTYPE_FP8_E5M2 = 2   /* OCP E5M2 (bias 15, IEEE-style inf/NaN); KV cache only  */
+  PA_DTYPE_FP8_E5M2 = 2,  /* OCP E5M2 (bias 15, IEEE-style inf/NaN); KV cache only  */
+  PA_DTYPE_FP8_E4M3 = 3   /* OCP E4M3 (bias 7, no inf, S.1111.111 NaN); KV cache only */
 } pa_dtype_t;
+
+typedef enum pa_schedule {
+  PA_SCHEDULE_AUTO = 0,   /* queue when the dense grid far exceeds the resident waves */
+  PA_SCHEDULE_GRID = 1,   /* one workgroup per (KV head, sequence, partition)          */
+  PA_SCHEDULE_QUEUE = 2   /* a plan kernel lists the non-empty items, longest first,
+                             and workgroup i takes item i (matrix-core kernel,
+                             partitions of at most 8192 tokens)                     */
+} pa_schedule_t;
 
 typedef enum pa_kernel {
   PA_KERNEL_AUTO = 0,     /* matrix-core kernel where supported, else vector kernel  */
   PA_KERNEL_VALU = 1,     /* vector-ALU kernel (every supported shape)               */
-  PA_KERNEL_MFMA = 2      /* matrix-core kernel: head_dim 128, block 16, group <= 16,
-                             q bf16 with KV bf16 or fp8-e5m2                         */
+  PA_KERNEL_MFMA = 2      /* matrix-core kernel: head_dim 128, block 16,
+                             group * q_len <= 64, q bf16 with KV bf16 or fp8          */
 } pa_kernel_t;
 
 /* Sizes and types of one call. Supported: block_size 16; head_dim 64 or 128;
  * group = num_heads / num_kv_heads in {1, 2, 4, 8, 16}; (q_dtype, kv_dtype) in
- * {(F32, F32), (BF16, BF16), (BF16, FP8_E5M2)}. */
+ * {(F32, F32), (BF16, BF16), (BF16, FP8_E5M2), (BF16, FP8_E4M3)}.
+ * Non-finite K/V values in attended slots give non-finite outputs (the
+ * matrix-core kernel may return NaN where exact arithmetic gives +-inf). */
 typedef struct pa_dims {
   int32_t num_seqs;
   int32_t num_heads;           /* query heads                                         */
@@ -102,6 +113,7 @@ typedef struct pa_dims {
                                   with several query rows; a query with no token gets
                                   a zero row). Matrix-core kernel only:
                                   group * q_len <= 64.                                  */
+  int32_t schedule;            /* pa_schedule_t                                        */
 } pa_dims_t;
 
 /* Decode with a workspace the library takes from the stream-ordered allocator
@@ -141,7 +153,7 @@ typedef struct pa_plan {
   int32_t max_partitions;      /* partitions of the longest allowed sequence           */
   int32_t grid_workgroups;     /* workgroups of the partition kernel                   */
   int32_t reduce_workgroups;   /* workgroups of the reduce kernel (0 = not launched)   */
-  int32_t pad;
+  int32_t schedule;            /* pa_schedule_t actually used (never AUTO)             */
   size_t workspace_bytes;
 } pa_plan_t;
 

@@ -35,7 +35,9 @@ Sources on the pages:
   * The fp8-e5m2 KV option appears only as the flag name ``fp8_e5m2`` on the
     vLLM page; its decoding follows the OCP 8-bit floating point format
     (1 sign, 5 exponent bits with bias 15, 2 mantissa bits, IEEE-style
-    subnormals, infinities and NaNs).
+    subnormals, infinities and NaNs). The inference page's exercise compares
+    KV caches in other precisions; the OCP E4M3 format (bias 7, 3 mantissa
+    bits, no infinities, one NaN pattern per sign) is the other fp8 option.
 
 Readings where the pages are silent (each is also listed with the design notes):
   * tail slots of the last block (t >= L) do not exist and take no part in
@@ -59,7 +61,7 @@ __all__ = [
     "decode_bits", "e5m2_value", "logical_kv", "paged_decode", "paged_decode_rows",
     "online_decode", "merge_partials", "dense_attention",
     "e5m2_encode", "bf16_encode", "encode_bits", "paged_append", "copy_blocks",
-    "paged_attention_multi",
+    "paged_attention_multi", "e4m3_value", "e4m3_encode",
 ]
 
 
@@ -82,6 +84,22 @@ def e5m2_value(code: int) -> float:
 _E5M2_TABLE = np.array([e5m2_value(c) for c in range(256)], dtype=np.float64)
 
 
+def e4m3_value(code: int) -> float:
+    """Exact value of one OCP E4M3 (E4M3FN) byte: 4 exponent bits with bias 7,
+    3 mantissa bits, no infinities; S.1111.111 is NaN."""
+    sign = -1.0 if (code >> 7) & 1 else 1.0
+    exp = (code >> 3) & 0xF
+    man = code & 0x7
+    if exp == 0xF and man == 0x7:
+        return math.nan
+    if exp == 0:
+        return sign * (man / 8.0) * 2.0 ** (1 - 7)
+    return sign * (1.0 + man / 8.0) * 2.0 ** (exp - 7)
+
+
+_E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
 def decode_bits(bits: np.ndarray, dtype: str) -> np.ndarray:
     """Storage bits -> float64 values, exactly."""
     if dtype == "f32":
@@ -92,6 +110,8 @@ def decode_bits(bits: np.ndarray, dtype: str) -> np.ndarray:
             return b.view(np.float32).astype(np.float64)
     if dtype == "e5m2":
         return _E5M2_TABLE[np.asarray(bits, dtype=np.uint8)]
+    if dtype == "e4m3":
+        return _E4M3_TABLE[np.asarray(bits, dtype=np.uint8)]
     raise ValueError(dtype)
 
 
@@ -308,6 +328,35 @@ def e5m2_encode(x) -> np.ndarray:
     return (code.astype(np.uint16) | sign).astype(np.uint8)
 
 
+def e4m3_encode(x) -> np.ndarray:
+    """Values (exact in float64) -> OCP E4M3 codes, round to nearest, ties to even.
+
+    The format has no infinity: a magnitude that rounds past 448 (the tie at
+    464 rounds to 448, which is even), an infinity or a NaN becomes the NaN
+    code with the input's sign. Subnormal step 2^-9.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    sign = (np.signbit(x).astype(np.uint16) << 7)
+    a = np.abs(x)
+    code = np.zeros(a.shape, dtype=np.int64)
+    fin = np.isfinite(a)
+    m, e = np.frexp(np.where(fin, a, 0.0))
+    E = e.astype(np.int64) - 1
+    normal = fin & (a >= 2.0 ** -6)
+    q = np.round(np.where(normal, a, 0.0) / np.exp2(np.where(normal, E - 3, 0).astype(np.float64)))   # [8, 16]
+    carry = q >= 16
+    E2 = np.where(carry, E + 1, E)
+    q2 = np.where(carry, 8, q).astype(np.int64)
+    biased = E2 + 7
+    norm_code = (biased << 3) | (q2 - 8)
+    nan_code = normal & (norm_code >= 0x7F)            # rounds to 480 or beyond: no such value
+    code = np.where(normal & ~nan_code, norm_code, code)
+    sub = fin & (a < 2.0 ** -6)
+    code = np.where(sub, np.round(np.where(sub, a, 0.0) * 2.0 ** 9).astype(np.int64), code)
+    code = np.where(nan_code | ~fin, 0x7F, code)
+    return (code.astype(np.uint16) | sign).astype(np.uint8)
+
+
 def bf16_encode(x) -> np.ndarray:
     """float32 values -> bfloat16 bits, round to nearest even (8 significant bits).
 
@@ -341,6 +390,8 @@ def encode_bits(values_f32: np.ndarray, dtype: str, scale: float = 1.0) -> np.nd
         return bf16_encode(v)
     if dtype == "e5m2":
         return e5m2_encode((v / np.float32(scale)).astype(np.float64))
+    if dtype == "e4m3":
+        return e4m3_encode((v / np.float32(scale)).astype(np.float64))
     raise ValueError(dtype)
 
 

@@ -11,7 +11,7 @@ from __future__ import annotations
 
 import numpy as np
 
-ELEM_BYTES = {"f32": 4, "bf16": 2, "e5m2": 1}
+ELEM_BYTES = {"f32": 4, "bf16": 2, "e5m2": 1, "e4m3": 1}
 
 
 def kv_cache_bytes(num_layers: int, num_kv_heads: int, head_dim: int, seq_len: int, elem_bytes: int) -> int:

@@ -18,9 +18,11 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libpadecode.so")
 
 PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_ALIGN, PA_ERR_WORKSPACE, PA_ERR_HIP = range(7)
-PA_DTYPE_F32, PA_DTYPE_BF16, PA_DTYPE_FP8_E5M2 = 0, 1, 2
+PA_DTYPE_F32, PA_DTYPE_BF16, PA_DTYPE_FP8_E5M2, PA_DTYPE_FP8_E4M3 = 0, 1, 2, 3
 KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
 KERNEL_NAMES = {v: k for k, v in KERNELS.items()}
+SCHEDULES = {"auto": 0, "grid": 1, "queue": 2}
+SCHEDULE_NAMES = {v: k for k, v in SCHEDULES.items()}
 
 # Symbols declared in include/pa_decode.h and include/pa_cache.h.
 EXPORTED = ("pa_decode", "pa_decode_ws", "pa_decode_ws_timed", "pa_decode_workspace_bytes",
@@ -33,13 +35,13 @@ class PaDims(ctypes.Structure):
                 ("max_blocks_per_seq", ctypes.c_int32), ("q_dtype", ctypes.c_int32),
                 ("kv_dtype", ctypes.c_int32), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
                 ("max_seq_len", ctypes.c_int32), ("partition_tokens", ctypes.c_int32),
-                ("kernel", ctypes.c_int32), ("q_len", ctypes.c_int32)]
+                ("kernel", ctypes.c_int32), ("q_len", ctypes.c_int32), ("schedule", ctypes.c_int32)]
 
 
 class PaPlan(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("partition_tokens", ctypes.c_int32),
                 ("max_partitions", ctypes.c_int32), ("grid_workgroups", ctypes.c_int32),
-                ("reduce_workgroups", ctypes.c_int32), ("pad", ctypes.c_int32),
+                ("reduce_workgroups", ctypes.c_int32), ("schedule", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_size_t)]
 
 
@@ -98,7 +100,7 @@ def _check(rc: int):
 
 
 _TORCH_DTYPES = {torch.float32: PA_DTYPE_F32, torch.bfloat16: PA_DTYPE_BF16}
-_KV_NAMES = {"f32": PA_DTYPE_F32, "bf16": PA_DTYPE_BF16, "e5m2": PA_DTYPE_FP8_E5M2}
+_KV_NAMES = {"f32": PA_DTYPE_F32, "bf16": PA_DTYPE_BF16, "e5m2": PA_DTYPE_FP8_E5M2, "e4m3": PA_DTYPE_FP8_E4M3}
 
 
 def _kv_dtype_code(t: torch.Tensor, kv_dtype: Optional[str]) -> int:
@@ -106,6 +108,8 @@ def _kv_dtype_code(t: torch.Tensor, kv_dtype: Optional[str]) -> int:
         return _KV_NAMES[kv_dtype]
     if t.dtype == torch.float8_e5m2:
         return PA_DTYPE_FP8_E5M2
+    if t.dtype == torch.float8_e4m3fn:
+        return PA_DTYPE_FP8_E4M3
     if t.dtype in _TORCH_DTYPES:
         return _TORCH_DTYPES[t.dtype]
     raise TypeError(f"unsupported KV cache dtype {t.dtype}; pass kv_dtype for raw byte views")
@@ -113,7 +117,8 @@ def _kv_dtype_code(t: torch.Tensor, kv_dtype: Optional[str]) -> int:
 
 def make_dims(q: torch.Tensor, k_cache: torch.Tensor, block_tables: torch.Tensor, *,
               kv_dtype: Optional[str] = None, max_seq_len: int = 0, partition_tokens: int = 0,
-              kernel: str = "auto", k_scale: float = 1.0, v_scale: float = 1.0) -> PaDims:
+              kernel: str = "auto", k_scale: float = 1.0, v_scale: float = 1.0,
+              schedule: str = "auto") -> PaDims:
     if q.dim() not in (3, 4) or k_cache.dim() != 4 or block_tables.dim() != 2:
         raise ValueError("q [S,H,D] or [S,q_len,H,D], k_cache [NB,Hkv,D,bs], block_tables [S,max_blocks] expected")
     if q.dtype not in _TORCH_DTYPES:
@@ -126,7 +131,8 @@ def make_dims(q: torch.Tensor, k_cache: torch.Tensor, block_tables: torch.Tensor
     return PaDims(num_seqs=S, num_heads=H, head_dim=D, num_blocks=NB, block_size=bs,
                   max_blocks_per_seq=block_tables.shape[1], q_dtype=_TORCH_DTYPES[q.dtype],
                   kv_dtype=_kv_dtype_code(k_cache, kv_dtype), k_scale=k_scale, v_scale=v_scale,
-                  max_seq_len=max_seq_len, partition_tokens=partition_tokens, kernel=KERNELS[kernel], q_len=QL)
+                  max_seq_len=max_seq_len, partition_tokens=partition_tokens, kernel=KERNELS[kernel], q_len=QL,
+                  schedule=SCHEDULES[schedule])
 
 
 def plan(dims: PaDims, num_kv_heads: int) -> dict:
@@ -134,7 +140,8 @@ def plan(dims: PaDims, num_kv_heads: int) -> dict:
     _check(load_library().pa_decode_plan(ctypes.byref(dims), num_kv_heads, ctypes.byref(p)))
     return dict(kernel=KERNEL_NAMES[p.kernel], partition_tokens=p.partition_tokens,
                 max_partitions=p.max_partitions, grid_workgroups=p.grid_workgroups,
-                reduce_workgroups=p.reduce_workgroups, workspace_bytes=p.workspace_bytes)
+                reduce_workgroups=p.reduce_workgroups, workspace_bytes=p.workspace_bytes,
+                schedule=SCHEDULE_NAMES[p.schedule])
 
 
 def workspace_bytes(dims: PaDims, num_kv_heads: int) -> int:
@@ -165,7 +172,7 @@ def _validate_tensors(q, k_cache, v_cache, block_tables, seq_lens, out):
 def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
               seq_lens: torch.Tensor, num_kv_heads: int, scale: float, out: Optional[torch.Tensor] = None, *,
               kv_dtype: Optional[str] = None, max_seq_len: int = 0, partition_tokens: int = 0,
-              kernel: str = "auto", k_scale: float = 1.0, v_scale: float = 1.0,
+              kernel: str = "auto", k_scale: float = 1.0, v_scale: float = 1.0, schedule: str = "auto",
               workspace: Optional[torch.Tensor] = None, events=None) -> torch.Tensor:
     """PagedAttention decode through the C ABI; returns `out`.
 
@@ -180,7 +187,8 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, blo
         out = torch.empty_like(q)
     _validate_tensors(q, k_cache, v_cache, block_tables, seq_lens, out)
     dims = make_dims(q, k_cache, block_tables, kv_dtype=kv_dtype, max_seq_len=max_seq_len,
-                     partition_tokens=partition_tokens, kernel=kernel, k_scale=k_scale, v_scale=v_scale)
+                     partition_tokens=partition_tokens, kernel=kernel, k_scale=k_scale, v_scale=v_scale,
+                     schedule=schedule)
     lib = load_library()
     stream = ctypes.c_void_p(torch.cuda.current_stream(q.device).cuda_stream)
     args = (ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_cache.data_ptr()),
@@ -204,6 +212,38 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, blo
     return out
 
 
+class DecodeCall:
+    """One pa_decode_ws / pa_decode_ws_timed call with its arguments checked and
+    marshalled once, for loops that repeat the same call (the tensors are kept
+    alive by this object; the stream is the current one at construction)."""
+
+    def __init__(self, q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale, out, *,
+                 workspace=None, kv_dtype=None, max_seq_len=0, partition_tokens=0, kernel="auto",
+                 k_scale=1.0, v_scale=1.0, schedule="auto"):
+        _validate_tensors(q, k_cache, v_cache, block_tables, seq_lens, out)
+        self.dims = make_dims(q, k_cache, block_tables, kv_dtype=kv_dtype, max_seq_len=max_seq_len,
+                              partition_tokens=partition_tokens, kernel=kernel, k_scale=k_scale, v_scale=v_scale,
+                              schedule=schedule)
+        if workspace is None:
+            workspace = alloc_workspace(self.dims, num_kv_heads, q.device)
+        self._keep = (q, k_cache, v_cache, block_tables, seq_lens, out, workspace)
+        self._lib = load_library()
+        self._args = (ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_cache.data_ptr()),
+                      ctypes.c_void_p(v_cache.data_ptr()), ctypes.c_void_p(block_tables.data_ptr()),
+                      ctypes.c_void_p(seq_lens.data_ptr()), ctypes.c_int32(num_kv_heads), ctypes.c_float(scale),
+                      ctypes.c_void_p(out.data_ptr()), ctypes.byref(self.dims),
+                      ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(workspace.numel()),
+                      ctypes.c_void_p(torch.cuda.current_stream(q.device).cuda_stream))
+
+    def __call__(self, events=None):
+        if events is None:
+            rc = self._lib.pa_decode_ws(*self._args)
+        else:
+            rc = self._lib.pa_decode_ws_timed(*self._args, *[ctypes.c_void_p(e) if e else None for e in events])
+        if rc != PA_OK:
+            _check(rc)
+
+
 def alloc_workspace(dims: PaDims, num_kv_heads: int, device) -> torch.Tensor:
     n = workspace_bytes(dims, num_kv_heads)
     # torch's caching allocator hands out 512-byte aligned blocks
@@ -216,7 +256,8 @@ def _cache_dims(k_cache: torch.Tensor, block_tables: Optional[torch.Tensor], kv_
     S, MB = (block_tables.shape if block_tables is not None else (1, 1))
     return PaDims(num_seqs=S, num_heads=k_cache.shape[1], head_dim=D, num_blocks=NB, block_size=bs,
                   max_blocks_per_seq=MB, q_dtype=PA_DTYPE_BF16, kv_dtype=_kv_dtype_code(k_cache, kv_dtype),
-                  k_scale=k_scale, v_scale=v_scale, max_seq_len=0, partition_tokens=0, kernel=0)
+                  k_scale=k_scale, v_scale=v_scale, max_seq_len=0, partition_tokens=0, kernel=0, q_len=0,
+                  schedule=0)
 
 
 def pa_cache_append(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

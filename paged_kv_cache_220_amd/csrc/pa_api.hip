@@ -26,7 +26,8 @@ struct Plan {
   int max_len = 0;
   int partition_tokens = 0;
   int max_parts = 1;
-  size_t off_m = 0, off_l = 0, ws_bytes = 0;
+  int schedule = PA_SCHEDULE_GRID;
+  size_t off_m = 0, off_l = 0, off_items = 0, off_qlen = 0, ws_bytes = 0;
   long long grid = 0, reduce_grid = 0;
 };
 
@@ -44,6 +45,7 @@ int check_dims(const pa_dims_t* d, int32_t hkv) {
   if (!isfinite(d->k_scale) || !isfinite(d->v_scale)) return PA_ERR_SHAPE;
   if (d->q_len < 0) return PA_ERR_SHAPE;
   if (d->kernel < PA_KERNEL_AUTO || d->kernel > PA_KERNEL_MFMA) return PA_ERR_UNSUPPORTED;
+  if (d->schedule < PA_SCHEDULE_AUTO || d->schedule > PA_SCHEDULE_QUEUE) return PA_ERR_UNSUPPORTED;
   if (d->block_size != pa::kBlockSize) return PA_ERR_UNSUPPORTED;
   if ((long long)d->num_seqs * hkv > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;  // grid x limit
   const int group = d->num_heads / hkv;
@@ -79,7 +81,8 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
     // lengths that give that many items, the longest is taken: it amortises
     // each item's start-up and shrinks the partial states the merge reads.
     const long long units = (long long)d->num_seqs * hkv;
-    const long long tile_bytes = 2LL * pa::kTileTokens * d->head_dim * (d->kv_dtype == PA_DTYPE_FP8_E5M2 ? 1 : 2);
+    const bool fp8 = d->kv_dtype == PA_DTYPE_FP8_E5M2 || d->kv_dtype == PA_DTYPE_FP8_E4M3;
+    const long long tile_bytes = 2LL * pa::kTileTokens * d->head_dim * (fp8 ? 1 : 2);
     const long long want = (32LL << 20) / tile_bytes;
     long long cap = 4096;
     while (cap / 2 >= p->max_len && cap > pa::kTileTokens) cap /= 2;   // no longer than the longest sequence needs
@@ -95,15 +98,32 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
   if (p->max_parts > kMaxParts) return PA_ERR_UNSUPPORTED;
   p->grid = (long long)p->max_parts * hkv * d->num_seqs;
   p->reduce_grid = p->max_parts > 1 ? (long long)d->num_heads * p->q_len * d->num_seqs : 0;
+  // List schedule: for the matrix-core kernel when asked, or when the dense
+  // grid is far larger than the resident workgroups (a skewed or sparse
+  // length mix leaves most of it empty and its long partitions in the tail).
+  const bool queue_ok = p->kernel == PA_KERNEL_MFMA && P / pa::kTileTokens < pa::kMaxQueueBuckets;
+  if (d->schedule == PA_SCHEDULE_QUEUE) {
+    if (!queue_ok) return PA_ERR_UNSUPPORTED;
+    p->schedule = PA_SCHEDULE_QUEUE;
+  } else if (d->schedule == PA_SCHEDULE_AUTO && queue_ok && p->grid > 4LL * pa::kResidentWorkgroups) {
+    p->schedule = PA_SCHEDULE_QUEUE;
+  } else {
+    p->schedule = PA_SCHEDULE_GRID;
+  }
+  size_t off = 0;
   if (p->max_parts > 1) {
     const size_t items = (size_t)d->num_seqs * hkv * p->max_parts * p->group * p->q_len;
     const size_t o_bytes = items * d->head_dim * sizeof(float);
     p->off_m = align_up(o_bytes, kAlign);
     p->off_l = p->off_m + align_up(items * sizeof(float), kAlign);
-    p->ws_bytes = p->off_l + align_up(items * sizeof(float), kAlign);
-  } else {
-    p->off_m = p->off_l = p->ws_bytes = 0;
+    off = p->off_l + align_up(items * sizeof(float), kAlign);
   }
+  if (p->schedule == PA_SCHEDULE_QUEUE) {
+    p->off_items = off;
+    p->off_qlen = off + align_up((size_t)p->grid * sizeof(int2), kAlign);
+    off = p->off_qlen + kAlign;          // list length
+  }
+  p->ws_bytes = off;
   return PA_OK;
 }
 
@@ -130,9 +150,9 @@ int run(const void* q, const void* k_cache, const void* v_cache, const int32_t* 
   a.seq_lens = seq_lens;
   a.out = out;
   char* ws = static_cast<char*>(workspace);
-  a.part_o = p.ws_bytes ? reinterpret_cast<float*>(ws) : nullptr;
-  a.part_m = p.ws_bytes ? reinterpret_cast<float*>(ws + p.off_m) : nullptr;
-  a.part_l = p.ws_bytes ? reinterpret_cast<float*>(ws + p.off_l) : nullptr;
+  a.part_o = p.max_parts > 1 ? reinterpret_cast<float*>(ws) : nullptr;
+  a.part_m = p.max_parts > 1 ? reinterpret_cast<float*>(ws + p.off_m) : nullptr;
+  a.part_l = p.max_parts > 1 ? reinterpret_cast<float*>(ws + p.off_l) : nullptr;
   a.block_stride = (int64_t)hkv * dims->head_dim * dims->block_size;
   a.num_seqs = dims->num_seqs;
   a.num_heads = dims->num_heads;
@@ -150,8 +170,17 @@ int run(const void* q, const void* k_cache, const void* v_cache, const int32_t* 
   a.score_scale = scale * dims->k_scale * 1.4426950408889634f;
   a.v_scale = dims->v_scale;
   a.q_len = p.q_len;
+  a.queue_items = nullptr;
+  a.queue_len = nullptr;
+  a.queue_workgroups = 0;
+  if (p.schedule == PA_SCHEDULE_QUEUE) {
+    a.queue_items = reinterpret_cast<const int2*>(ws + p.off_items);
+    a.queue_len = reinterpret_cast<const int*>(ws + p.off_qlen);
+    a.queue_workgroups = (int32_t)p.grid;            // the list never holds more items than the dense grid
+  }
 
   if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return PA_ERR_HIP;
+  if (p.schedule == PA_SCHEDULE_QUEUE && pa::launch_plan(a, stream) != hipSuccess) return PA_ERR_HIP;
   hipError_t e = p.kernel == PA_KERNEL_MFMA
                      ? pa::launch_mfma(a, dims->q_dtype, dims->kv_dtype, dims->head_dim, p.group, stream)
                      : pa::launch_valu(a, dims->q_dtype, dims->kv_dtype, dims->head_dim, p.group, stream);
@@ -187,6 +216,7 @@ int pa_decode_plan(const pa_dims_t* dims, int32_t num_kv_heads, pa_plan_t* plan)
   plan->max_partitions = p.max_parts;
   plan->grid_workgroups = (int32_t)p.grid;
   plan->reduce_workgroups = (int32_t)p.reduce_grid;
+  plan->schedule = p.schedule;
   plan->workspace_bytes = p.ws_bytes;
   return PA_OK;
 }

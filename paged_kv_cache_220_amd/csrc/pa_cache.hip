@@ -29,6 +29,21 @@ __device__ __forceinline__ uint8_t f32_to_e5m2(float x) {
   return static_cast<uint8_t>(sign | static_cast<uint32_t>(q));
 }
 
+// float -> OCP E4M3, round to nearest even; no infinities: magnitudes above
+// 464 (which round past 448), infinities and NaN give the NaN code.
+__device__ __forceinline__ uint8_t f32_to_e4m3(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x43E80000u) return static_cast<uint8_t>(sign | 0x7Fu);      // > 464, inf, NaN
+  if (a >= 0x3C800000u) {                                               // |x| >= 2^-6: normal code
+    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);                 // keep 3 mantissa bits, ties to even
+    return static_cast<uint8_t>(sign | ((r >> 20) - (120u << 3)));      // rebias 127 -> 7
+  }
+  const float q = rintf(__uint_as_float(a) * 512.0f);                   // subnormal step 2^-9
+  return static_cast<uint8_t>(sign | static_cast<uint32_t>(q));
+}
+
 template <int IN> __device__ __forceinline__ float load_in(const void* p, int64_t i);
 template <> __device__ __forceinline__ float load_in<kF32>(const void* p, int64_t i) {
   return static_cast<const float*>(p)[i];
@@ -46,6 +61,9 @@ template <> __device__ __forceinline__ void store_kv<kBF16>(void* cache, int64_t
 }
 template <> __device__ __forceinline__ void store_kv<kE5M2>(void* cache, int64_t i, float x, float scale) {
   static_cast<uint8_t*>(cache)[i] = f32_to_e5m2(x / scale);
+}
+template <> __device__ __forceinline__ void store_kv<kE4M3>(void* cache, int64_t i, float x, float scale) {
+  static_cast<uint8_t*>(cache)[i] = f32_to_e4m3(x / scale);
 }
 
 struct AppendArgs {
@@ -112,7 +130,8 @@ int check_cache_dims(const pa_dims_t* d, int32_t hkv) {
   if (d->head_dim <= 0 || d->num_blocks <= 0 || d->block_size <= 0 || hkv <= 0) return PA_ERR_SHAPE;
   if (d->block_size != kBlockSize) return PA_ERR_UNSUPPORTED;
   if (d->head_dim != 64 && d->head_dim != 128) return PA_ERR_UNSUPPORTED;
-  if (d->kv_dtype != kF32 && d->kv_dtype != kBF16 && d->kv_dtype != kE5M2) return PA_ERR_UNSUPPORTED;
+  if (d->kv_dtype != kF32 && d->kv_dtype != kBF16 && d->kv_dtype != kE5M2 && d->kv_dtype != kE4M3)
+    return PA_ERR_UNSUPPORTED;
   if (hkv > 65535) return PA_ERR_UNSUPPORTED;
   return PA_OK;
 }
@@ -130,12 +149,12 @@ extern "C" int pa_cache_append(const void* k_new, const void* v_new, void* k_cac
   if (st != PA_OK) return st;
   if (num_tokens < 0 || dims->num_seqs <= 0 || dims->max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
   const int kv = dims->kv_dtype;
-  const bool combo = (in_dtype == kF32 && (kv == kF32 || kv == kBF16 || kv == kE5M2)) ||
-                     (in_dtype == kBF16 && (kv == kBF16 || kv == kE5M2));
+  const bool fp8 = kv == kE5M2 || kv == kE4M3;
+  const bool combo = (in_dtype == kF32 && (kv == kF32 || kv == kBF16 || fp8)) || (in_dtype == kBF16 && (kv == kBF16 || fp8));
   if (!combo) return PA_ERR_UNSUPPORTED;
   if (!isfinite(dims->k_scale) || !isfinite(dims->v_scale) || dims->k_scale == 0.f || dims->v_scale == 0.f)
     return PA_ERR_SHAPE;
-  if (kv != kE5M2 && (dims->k_scale != 1.f || dims->v_scale != 1.f)) return PA_ERR_UNSUPPORTED;
+  if (!fp8 && (dims->k_scale != 1.f || dims->v_scale != 1.f)) return PA_ERR_UNSUPPORTED;
   if (num_tokens == 0) return PA_OK;
   if (!k_new || !v_new || !k_cache || !v_cache || !block_tables || !token_seq || !token_pos) return PA_ERR_NULL;
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
@@ -163,7 +182,9 @@ extern "C" int pa_cache_append(const void* k_new, const void* v_new, void* k_cac
   else if (in_dtype == kF32 && kv == kBF16) append_kernel<kF32, kBF16><<<grid, 64, 0, s>>>(a);
   else if (in_dtype == kF32 && kv == kE5M2) append_kernel<kF32, kE5M2><<<grid, 64, 0, s>>>(a);
   else if (in_dtype == kBF16 && kv == kBF16) append_kernel<kBF16, kBF16><<<grid, 64, 0, s>>>(a);
-  else append_kernel<kBF16, kE5M2><<<grid, 64, 0, s>>>(a);
+  else if (in_dtype == kF32 && kv == kE4M3) append_kernel<kF32, kE4M3><<<grid, 64, 0, s>>>(a);
+  else if (in_dtype == kBF16 && kv == kE5M2) append_kernel<kBF16, kE5M2><<<grid, 64, 0, s>>>(a);
+  else append_kernel<kBF16, kE4M3><<<grid, 64, 0, s>>>(a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

@@ -7,12 +7,13 @@
 namespace pa {
 
 // Storage-type tags (match pa_dtype_t).
-enum : int { kF32 = 0, kBF16 = 1, kE5M2 = 2 };
+enum : int { kF32 = 0, kBF16 = 1, kE5M2 = 2, kE4M3 = 3 };
 
 template <int T> struct Storage;
 template <> struct Storage<kF32> { using type = float; };
 template <> struct Storage<kBF16> { using type = uint16_t; };
 template <> struct Storage<kE5M2> { using type = uint8_t; };
+template <> struct Storage<kE4M3> { using type = uint8_t; };
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
@@ -27,6 +28,8 @@ template <int T> __device__ __forceinline__ float to_f32(typename Storage<T>::ty
 template <> __device__ __forceinline__ float to_f32<kF32>(float x) { return x; }
 template <> __device__ __forceinline__ float to_f32<kBF16>(uint16_t x) { return bf16_bits_to_f32(x); }
 template <> __device__ __forceinline__ float to_f32<kE5M2>(uint8_t x) { return e5m2_to_f32(x); }
+// OCP E4M3 (bias 7, no infinities, S.1111.111 = NaN): gfx950's fp8 convert reads this format.
+template <> __device__ __forceinline__ float to_f32<kE4M3>(uint8_t x) { return __builtin_amdgcn_cvt_f32_fp8(x, 0); }
 
 // float -> bfloat16 bits, round to nearest even (NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {

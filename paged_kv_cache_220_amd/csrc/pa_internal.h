@@ -32,6 +32,12 @@ struct Args {
   float score_scale;      // scale * k_scale * log2(e): scores live in the log2 domain
   float v_scale;
   int32_t q_len;          // query positions per sequence (1 = decode)
+  // List schedule (null queue_items: dense grid). The plan kernel fills
+  // queue_items[0 .. *queue_len) with (sequence * Hkv + kv head, partition),
+  // longest first; workgroup i of queue_workgroups processes item i.
+  const int2* queue_items;
+  const int* queue_len;
+  int32_t queue_workgroups;
 };
 
 // Host-side launchers; each returns the hipError_t of the launch.
@@ -40,6 +46,7 @@ hipError_t launch_valu(const Args& a, int q_dtype, int kv_dtype, int head_dim, i
 hipError_t launch_mfma(const Args& a, int q_dtype, int kv_dtype, int head_dim, int group,
                        hipStream_t stream);
 hipError_t launch_reduce(const Args& a, int q_dtype, int head_dim, int group, hipStream_t stream);
+hipError_t launch_plan(const Args& a, hipStream_t stream);
 
 bool valu_supported(int q_dtype, int kv_dtype, int head_dim, int group);
 bool mfma_supported(int q_dtype, int kv_dtype, int head_dim, int group, int block_size, int q_len);
@@ -47,6 +54,8 @@ bool mfma_supported(int q_dtype, int kv_dtype, int head_dim, int group, int bloc
 constexpr int kBlockSize = 16;     // tokens per physical block handled by the kernels
 constexpr int kTileTokens = 64;    // partition lengths are multiples of this
 constexpr int kMaxColumnGroups = 4; // matrix-core kernel: group * q_len <= 64
+constexpr int kMaxQueueBuckets = 129;  // queue schedule: partitions of at most 128 tiles
+constexpr int kResidentWorkgroups = 2048;  // gfx950: 256 CUs x 8 one-wave workgroups (planning)
 
 // Sequence length as the kernels use it. Lengths outside [0, max_tokens]
 // break a documented precondition; clamping keeps every access inside the

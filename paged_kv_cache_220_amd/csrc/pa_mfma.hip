@@ -35,7 +35,7 @@
 // poison the sum). Logical blocks past the partition end are not looked up in
 // the table; the tile's first block stands in and is masked.
 //
-// fp8-e5m2 KV: an E5M2 byte is the top byte of the binary16 of the same
+// fp8 KV (E5M2 here, E4M3 below): an E5M2 byte is the top byte of the binary16 of the same
 // value, so v_perm_b32 widens K and V to fp16 exactly and the f16 MFMA runs
 // with q rounded to fp16 (exact for bf16 q in [2^-14, 65504]).
 // bf16 KV: bf16 MFMA with q exact. In both, P enters the PV product as two
@@ -166,11 +166,49 @@ template <> struct Mfma<kE5M2> {
 // v / 16; NCG groups cover G * q_len <= 16 * NCG. All groups share each K and
 // V operand, so a tile is read once whatever the number of queries. With one
 // query (decode) and G <= 16 there is a single group.
-// One column group fits two waves per SIMD (<= 256 registers per lane), so
-// one wave's compute overlaps the other's loads; more groups take one wave.
+// One work item: partition `part` of sequence s for KV head kvh, all its columns.
+// fp8-e4m3 KV: gfx950 converts two OCP E4M3 codes to two binary16 values in
+// one instruction; every E4M3 value (subnormals included, |x| <= 448) is a
+// normal binary16, so the widening is exact. Otherwise as for E5M2.
+template <> struct Mfma<kE4M3> {
+  using op_t = f16x8;
+  using kload_t = uint32_t;  // 4 tokens of one row
+  using vload_t = u32x2;     // 8 tokens of one row
+  static constexpr int kElem = 1;
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  template <bool kHiWord>   // codes in bytes 2, 3 (else 0, 1) -> two binary16 values
+  static __device__ __forceinline__ uint32_t cvt2(uint32_t x) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, kHiWord));
+  }
+  static __device__ __forceinline__ f32x4 mma(op_t a, op_t b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ op_t k_operand(const kload_t (&r)[8], int j) {
+    const uint32_t sel = uint32_t(j) | (uint32_t(4 + j) << 8) | 0x0C0C0000u;   // token j of rows 2p, 2p+1
+    u32x4 x;
+    x[0] = cvt2<false>(__builtin_amdgcn_perm(r[1], r[0], sel));
+    x[1] = cvt2<false>(__builtin_amdgcn_perm(r[3], r[2], sel));
+    x[2] = cvt2<false>(__builtin_amdgcn_perm(r[5], r[4], sel));
+    x[3] = cvt2<false>(__builtin_amdgcn_perm(r[7], r[6], sel));
+    return __builtin_bit_cast(op_t, x);
+  }
+  static __device__ __forceinline__ op_t v_operand(vload_t x) {
+    u32x4 y;
+    y[0] = cvt2<false>(x[0]);
+    y[1] = cvt2<true>(x[0]);
+    y[2] = cvt2<false>(x[1]);
+    y[3] = cvt2<true>(x[1]);
+    return __builtin_bit_cast(op_t, y);
+  }
+  static __device__ __forceinline__ vload_t mask_v(vload_t x, int nvalid) { return Mfma<kE5M2>::mask_v(x, nvalid); }
+  static __device__ __forceinline__ op_t q_operand(const uint32_t (&qb)[8]) { return Mfma<kE5M2>::q_operand(qb); }
+  static __device__ __forceinline__ void p_operands(const float (&p)[8], op_t& hi, op_t& lo) {
+    Mfma<kE5M2>::p_operands(p, hi, lo);
+  }
+};
+
 template <int KDT, int NCG>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCG == 1 ? 2 : 1, 8)))
-void mfma_partition_kernel(const Args a, int group) {
+__device__ __forceinline__ void partition_item(const Args& a, int group, int s, int kvh, int part) {
   using M = Mfma<KDT>;
   using op_t = typename M::op_t;
   using kload_t = typename M::kload_t;
@@ -178,10 +216,6 @@ void mfma_partition_kernel(const Args a, int group) {
   constexpr int BS = kBlockSize;
   constexpr int64_t kRowBytes = BS * M::kElem;             // one head_dim row of a block tile
 
-  const Item item = work_item(a);
-  const int part = item.part;
-  const int kvh = item.kvh;
-  const int s = item.s;
   const int L = clamp_len(a, s);
   const int QL = a.q_len;
   const int GV = group * QL;                               // virtual heads of this KV head
@@ -412,28 +446,64 @@ void mfma_partition_kernel(const Args a, int group) {
   }
 }
 
+// One column group fits two waves per SIMD (<= 256 registers per lane), so
+// one wave's compute overlaps the other's loads; more groups take one wave.
+#define PA_MFMA_KERNEL_ATTRS \
+  __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCG == 1 ? 2 : 1, 8)))
+
+// Grid schedule: one workgroup per (KV head, sequence, partition) of the dense grid.
+template <int KDT, int NCG>
+PA_MFMA_KERNEL_ATTRS void mfma_partition_kernel(const Args a, int group) {
+  const Item it = work_item(a);
+  partition_item<KDT, NCG>(a, group, it.s, it.kvh, it.part);
+}
+
+// List schedule: workgroup i takes item i of the list the plan kernel built,
+// longest first, and workgroups past its end exit at once. Workgroups are
+// dispatched in index order, so long items start first and short ones fill
+// the end; consecutive (similar) items go to consecutive XCDs.
+template <int KDT, int NCG>
+PA_MFMA_KERNEL_ATTRS void mfma_partition_list_kernel(const Args a, int group) {
+  const int idx = blockIdx.x;
+  if (idx >= *a.queue_len) return;
+  const int2 w = a.queue_items[idx];
+  const int s = w.x / a.num_kv_heads;
+  partition_item<KDT, NCG>(a, group, s, w.x - s * a.num_kv_heads, w.y);
+}
+
 }  // namespace
 
 bool mfma_supported(int q_dtype, int kv_dtype, int head_dim, int group, int block_size, int q_len) {
-  return q_dtype == kBF16 && (kv_dtype == kBF16 || kv_dtype == kE5M2) && head_dim == kD &&
+  return q_dtype == kBF16 && (kv_dtype == kBF16 || kv_dtype == kE5M2 || kv_dtype == kE4M3) && head_dim == kD &&
          block_size == kBlockSize && group >= 1 && q_len >= 1 && group * q_len <= 16 * kMaxColumnGroups;
 }
 
 hipError_t launch_mfma(const Args& a, int q_dtype, int kv_dtype, int head_dim, int group,
                        hipStream_t stream) {
   if (!mfma_supported(q_dtype, kv_dtype, head_dim, group, kBlockSize, a.q_len)) return hipErrorInvalidValue;
-  const dim3 grid = partition_grid(a);
   const int gv = group * a.q_len;
   const int ncg = gv <= 16 ? 1 : gv <= 32 ? 2 : 4;
+  const bool queue = a.queue_items != nullptr;
+  const dim3 grid = queue ? dim3((unsigned)a.queue_workgroups) : partition_grid(a);   // list: one per possible item
+#define PA_LAUNCH(KDT, NCG)                                                            \
+  do {                                                                                 \
+    if (queue) mfma_partition_list_kernel<KDT, NCG><<<grid, 64, 0, stream>>>(a, group);  \
+    else mfma_partition_kernel<KDT, NCG><<<grid, 64, 0, stream>>>(a, group);             \
+  } while (0)
   if (kv_dtype == kBF16) {
-    if (ncg == 1) mfma_partition_kernel<kBF16, 1><<<grid, 64, 0, stream>>>(a, group);
-    else if (ncg == 2) mfma_partition_kernel<kBF16, 2><<<grid, 64, 0, stream>>>(a, group);
-    else mfma_partition_kernel<kBF16, 4><<<grid, 64, 0, stream>>>(a, group);
+    if (ncg == 1) PA_LAUNCH(kBF16, 1);
+    else if (ncg == 2) PA_LAUNCH(kBF16, 2);
+    else PA_LAUNCH(kBF16, 4);
+  } else if (kv_dtype == kE5M2) {
+    if (ncg == 1) PA_LAUNCH(kE5M2, 1);
+    else if (ncg == 2) PA_LAUNCH(kE5M2, 2);
+    else PA_LAUNCH(kE5M2, 4);
   } else {
-    if (ncg == 1) mfma_partition_kernel<kE5M2, 1><<<grid, 64, 0, stream>>>(a, group);
-    else if (ncg == 2) mfma_partition_kernel<kE5M2, 2><<<grid, 64, 0, stream>>>(a, group);
-    else mfma_partition_kernel<kE5M2, 4><<<grid, 64, 0, stream>>>(a, group);
+    if (ncg == 1) PA_LAUNCH(kE4M3, 1);
+    else if (ncg == 2) PA_LAUNCH(kE4M3, 2);
+    else PA_LAUNCH(kE4M3, 4);
   }
+#undef PA_LAUNCH
   return hipGetLastError();
 }
 

@@ -1,0 +1,69 @@
+// Work list for the list schedule of the partition kernel (gfx950).
+//
+// With a skewed length mix the dense (KV head, sequence, partition) grid is
+// mostly empty workgroups, and the few long partitions dispatched late leave a
+// tail in which most CUs idle. This kernel (one workgroup) lists the items that
+// exist, ordered by their number of 64-token tiles, longest first (a counting
+// sort: full partitions, then each sequence's last partial partition by
+// length, then empty sequences, which still get a zero output row). The
+// partition kernel's workgroup i then takes item i, so long items start first
+// and the short ones fill the end. It also writes the list length the
+// partition kernel reads, so nothing else needs clearing first.
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kPlanThreads = 1024;
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(const Args a) {
+  __shared__ int cnt[kMaxQueueBuckets];
+  __shared__ int cur[kMaxQueueBuckets];
+  const int tid = threadIdx.x;
+  const int P = a.partition_tokens;
+  const int full = P / kTileTokens;             // bucket of a full partition
+  const int hkv = a.num_kv_heads;
+  int2* items = const_cast<int2*>(a.queue_items);
+  for (int b = tid; b <= full; b += kPlanThreads) cnt[b] = 0;
+  __syncthreads();
+  for (int s = tid; s < a.num_seqs; s += kPlanThreads) {
+    const int L = clamp_len(a, s);
+    const int nfull = L / P;
+    const int rem = L - nfull * P;
+    if (nfull > 0) atomicAdd(&cnt[full], nfull * hkv);
+    if (rem > 0 || L == 0) atomicAdd(&cnt[(rem + kTileTokens - 1) / kTileTokens], hkv);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int off = 0;
+    for (int b = full; b >= 0; --b) {
+      cur[b] = off;
+      off += cnt[b];
+    }
+    *const_cast<int*>(a.queue_len) = off;
+  }
+  __syncthreads();
+  for (int s = tid; s < a.num_seqs; s += kPlanThreads) {
+    const int L = clamp_len(a, s);
+    const int nfull = L / P;
+    const int rem = L - nfull * P;
+    const int bucket = (rem + kTileTokens - 1) / kTileTokens;
+    for (int g = 0; g < hkv; ++g) {
+      const int unit = s * hkv + g;
+      for (int p = 0; p < nfull; ++p) items[atomicAdd(&cur[full], 1)] = make_int2(unit, p);
+      if (rem > 0 || L == 0) items[atomicAdd(&cur[bucket], 1)] = make_int2(unit, nfull);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_plan(const Args& a, hipStream_t stream) {
+  if (a.partition_tokens / kTileTokens >= kMaxQueueBuckets) return hipErrorInvalidValue;
+  plan_kernel<<<1, kPlanThreads, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace pa

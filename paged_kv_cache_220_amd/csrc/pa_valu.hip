@@ -70,6 +70,19 @@ template <> struct Row16<kE5M2> {
   }
 };
 
+template <> struct Row16<kE4M3> {
+  static __device__ __forceinline__ void load(const uint8_t* row, float (&v)[16]) {
+    const uint4 x = *reinterpret_cast<const uint4*>(row);
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[j], false);   // bytes 0, 1
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[j], true);    // bytes 2, 3
+      v[4 * j + 0] = lo[0]; v[4 * j + 1] = lo[1]; v[4 * j + 2] = hi[0]; v[4 * j + 3] = hi[1];
+    }
+  }
+};
+
 template <int QDT, int KDT, int D, int G>
 __global__ __launch_bounds__(64) void valu_partition_kernel(const Args a) {
   using KT = typename Storage<KDT>::type;
@@ -215,7 +228,7 @@ hipError_t launch_d(const Args& a, int head_dim, int group, dim3 grid, hipStream
 
 bool valu_supported(int q_dtype, int kv_dtype, int head_dim, int group) {
   const bool types = (q_dtype == kF32 && kv_dtype == kF32) || (q_dtype == kBF16 && kv_dtype == kBF16) ||
-                     (q_dtype == kBF16 && kv_dtype == kE5M2);
+                     (q_dtype == kBF16 && kv_dtype == kE5M2) || (q_dtype == kBF16 && kv_dtype == kE4M3);
   const bool dims = head_dim == 64 || head_dim == 128;
   const bool g = group == 1 || group == 2 || group == 4 || group == 8 || group == 16;
   return types && dims && g;
@@ -227,6 +240,7 @@ hipError_t launch_valu(const Args& a, int q_dtype, int kv_dtype, int head_dim, i
   if (q_dtype == kF32 && kv_dtype == kF32) return launch_d<kF32, kF32>(a, head_dim, group, grid, stream);
   if (q_dtype == kBF16 && kv_dtype == kBF16) return launch_d<kBF16, kBF16>(a, head_dim, group, grid, stream);
   if (q_dtype == kBF16 && kv_dtype == kE5M2) return launch_d<kBF16, kE5M2>(a, head_dim, group, grid, stream);
+  if (q_dtype == kBF16 && kv_dtype == kE4M3) return launch_d<kBF16, kE4M3>(a, head_dim, group, grid, stream);
   return hipErrorInvalidValue;
 }
 

@@ -38,12 +38,14 @@ BLOCK_SIZE_DEFAULT = 16
 F32 = "f32"
 BF16 = "bf16"
 E5M2 = "e5m2"
+E4M3 = "e4m3"
 
-_NP_STORAGE = {F32: np.float32, BF16: np.uint16, E5M2: np.uint8}
-ELEM_BYTES = {F32: 4, BF16: 2, E5M2: 1}
+_NP_STORAGE = {F32: np.float32, BF16: np.uint16, E5M2: np.uint8, E4M3: np.uint8}
+ELEM_BYTES = {F32: 4, BF16: 2, E5M2: 1, E4M3: 1}
 
 # Quiet-NaN bit patterns used to poison memory the kernel must never read.
-NAN_BITS = {F32: np.uint32(0x7FC00000).view(np.float32), BF16: np.uint16(0x7FC0), E5M2: np.uint8(0x7F)}
+NAN_BITS = {F32: np.uint32(0x7FC00000).view(np.float32), BF16: np.uint16(0x7FC0), E5M2: np.uint8(0x7F),
+            E4M3: np.uint8(0x7F)}
 
 _CHUNK = 1 << 22  # elements per K/V generation chunk
 
@@ -107,6 +109,8 @@ def to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
         return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     if dtype == E5M2:
         return t.to(torch.float8_e5m2).view(torch.uint8).numpy()
+    if dtype == E4M3:
+        return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     raise ValueError(dtype)
 
 
@@ -216,11 +220,13 @@ def _seq_lens_for(name: str, rng, num_seqs: Optional[int], seq_len: Optional[int
 
 
 def make_workload(name: str, *, num_seqs: Optional[int] = None, seq_len: Optional[int] = None,
-                  poison: bool = False, seed_extra: int = 0) -> Workload:
+                  poison: bool = False, seed_extra: int = 0, kv_dtype: Optional[str] = None) -> Workload:
     """Build decode batch `name` (c1..c5).
 
     `num_seqs` / `seq_len` shrink a configuration while keeping its head
     shapes, dtypes and placement rule (used for small parity cases).
+    `kv_dtype` overrides the cache type of the bf16-q batches (c2..c5), e.g.
+    "e4m3" for the fp8 batch in the other OCP format.
     `poison=True` fills every byte the kernel must not read (unreferenced pool
     blocks, tail slots past seq_len in the last block, and table padding,
     which then points at a dedicated NaN block) with NaN.
@@ -237,6 +243,10 @@ def make_workload(name: str, *, num_seqs: Optional[int] = None, seq_len: Optiona
         H, Hkv, D, qd, kvd = 64, 8, 128, BF16, E5M2
     else:
         H, Hkv, D, qd, kvd = 64, 8, 128, BF16, BF16
+    if kv_dtype is not None:
+        if qd != BF16 or kv_dtype not in (BF16, E5M2, E4M3):
+            raise ValueError(f"{name} cannot take a {kv_dtype} cache")
+        kvd = kv_dtype
 
     seq_lens = _seq_lens_for(name, rng, num_seqs, seq_len)
     S = len(seq_lens)

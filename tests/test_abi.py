@@ -82,6 +82,10 @@ def status_of(d, hkv=8):
     (dict(q_len=9), 8, B.PA_ERR_UNSUPPORTED),                    # 72 virtual heads
     (dict(q_len=2, kernel=1), 8, B.PA_ERR_UNSUPPORTED),          # vector kernel: one query only
     (dict(q_len=2, head_dim=64), 8, B.PA_ERR_UNSUPPORTED),
+    (dict(schedule=7), 8, B.PA_ERR_UNSUPPORTED),
+    (dict(schedule=2, kernel=1), 8, B.PA_ERR_UNSUPPORTED),       # queue: matrix-core kernel only
+    (dict(schedule=2, partition_tokens=16384), 8, B.PA_ERR_UNSUPPORTED),   # > 128 tiles per item
+    (dict(schedule=2), 8, B.PA_OK),
 ])
 def test_validation_statuses(kw, hkv, expect):
     assert status_of(dims(**kw), hkv) == expect
@@ -108,6 +112,18 @@ def test_plan_long_context():
     assert pc["partition_tokens"] == 512 and pc["max_partitions"] == 1 and pc["workspace_bytes"] == 0
     p2 = B.plan(dims(partition_tokens=1024, max_seq_len=4096), 8)
     assert p2["max_partitions"] == 4 and p2["partition_tokens"] == 1024
+
+
+def test_plan_schedule_choice():
+    # 16 x 8 units x 8 partitions = 1024 workgroups: dense grid
+    assert B.plan(dims(), 8)["schedule"] == "grid"
+    # 256 x 8 units x 8 partitions = 16384 >> 2048 resident workgroups: work queue
+    p = B.plan(dims(num_seqs=256, max_seq_len=32657), 8)
+    assert p["schedule"] == "queue" and p["partition_tokens"] == 4096
+    g = B.plan(dims(num_seqs=256, max_seq_len=32657, schedule=1), 8)
+    assert g["schedule"] == "grid"
+    assert p["workspace_bytes"] >= g["workspace_bytes"] + 16384 * 8      # item list
+    assert B.plan(dims(kernel=1, num_seqs=256), 8)["schedule"] == "grid"
 
 
 def test_plan_single_partition_needs_no_workspace():

@@ -19,6 +19,8 @@ def _to_dev(bits, dtype):
         return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.float32)).cuda()
     if dtype == "bf16":
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+    if dtype == "e4m3":
+        return torch.from_numpy(np.ascontiguousarray(bits)).view(torch.float8_e4m3fn).cuda()
     return torch.from_numpy(np.ascontiguousarray(bits)).view(torch.float8_e5m2).cuda()
 
 
@@ -27,7 +29,7 @@ def _from_dev(t, dtype):
         return t.cpu().numpy()
     if dtype == "bf16":
         return t.view(torch.int16).cpu().numpy().view(np.uint16)
-    return t.view(torch.uint8).cpu().numpy()
+    return t.view(torch.uint8).cpu().numpy()        # fp8 codes
 
 
 def _special_rows(shape, in_dtype, kv_dtype, rng):
@@ -37,6 +39,10 @@ def _special_rows(shape, in_dtype, kv_dtype, rng):
         vals = np.array(sorted({O.e5m2_value(c) for c in range(0x7C)}))
         ties = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
         extra = np.concatenate([ties, -ties, [61440.0, 61439.0, 1e6, -1e9, 0.0, -0.0, np.inf, np.nan, 2.0 ** -17]])
+    elif kv_dtype == "e4m3":
+        vals = np.array(sorted({O.e4m3_value(c) for c in range(0x7F)}))
+        ties = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+        extra = np.concatenate([ties, -ties, [464.0, 464.5, 480.0, 1e6, -1e9, 0.0, -0.0, np.inf, np.nan, 2.0 ** -10]])
     else:
         extra = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, 3.39e38, -3.4e38, 1e-40, -0.0, np.inf, np.nan], np.float32)
     extra = extra.astype(np.float32)
@@ -58,7 +64,8 @@ def _same(a, b, dtype):
 
 
 COMBOS = [("f32", "f32", 1.0), ("f32", "bf16", 1.0), ("bf16", "bf16", 1.0), ("bf16", "e5m2", 1.0),
-          ("f32", "e5m2", 1.0), ("f32", "e5m2", 0.37), ("bf16", "e5m2", 2.0)]
+          ("f32", "e5m2", 1.0), ("f32", "e5m2", 0.37), ("bf16", "e5m2", 2.0),
+          ("bf16", "e4m3", 1.0), ("f32", "e4m3", 1.0), ("f32", "e4m3", 0.37), ("bf16", "e4m3", 2.0)]
 
 
 @pytest.mark.parametrize("in_dtype,kv_dtype,scale", COMBOS)
@@ -111,7 +118,7 @@ def test_copy_blocks_byte_exact(name, kw):
     assert np.array_equal(_from_dev(vd, w.kv_dtype).view(np.uint8), v_ref.view(np.uint8))
 
 
-@pytest.mark.parametrize("kv_dtype", ["bf16", "e5m2"])
+@pytest.mark.parametrize("kv_dtype", ["bf16", "e5m2", "e4m3"])
 def test_append_then_decode(kv_dtype):
     """One decode step: write the new token's K/V, then attend over seq_len + 1 tokens."""
     rng = np.random.default_rng(5)

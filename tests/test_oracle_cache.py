@@ -124,3 +124,34 @@ def test_copy_blocks_definition():
         assert np.array_equal(k2[b], w.k_cache[a]) and np.array_equal(v2[b], w.v_cache[a])
     keep = np.setdiff1d(np.arange(w.num_blocks), dst)
     assert np.array_equal(k2[keep], w.k_cache[keep]) and np.array_equal(v2[keep], w.v_cache[keep])
+
+
+# ------------------------------------------------------------------ E4M3 ----
+
+def _torch_e4m3(x32):
+    return torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_e4m3_decode_table_two_ways():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = O.decode_bits(codes, "e4m3")
+    tor = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(tor))
+    fin = ~np.isnan(ours)
+    assert np.array_equal(ours[fin], tor[fin])
+    assert O.e4m3_value(0x7E) == 448.0 and O.e4m3_value(0x01) == 2.0 ** -9 and O.e4m3_value(0x38) == 1.0
+    assert np.isnan(O.e4m3_value(0x7F)) and np.isnan(O.e4m3_value(0xFF))
+
+
+def test_e4m3_encoder_matches_torch_random_and_ties():
+    rng = np.random.default_rng(6)
+    x = (rng.standard_normal(300000) * 10.0 ** rng.uniform(-5, 3.5, 300000)).astype(np.float32)
+    vals = np.array(sorted({O.e4m3_value(c) for c in range(0x7F)}))
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    edges = np.concatenate([mids, np.nextafter(mids, np.float32(np.inf)), np.nextafter(mids, np.float32(0)),
+                            vals.astype(np.float32), [464.0, 464.01, 479.0, 480.0, 1e6, 0.0, -0.0, np.inf, -np.inf,
+                                                      np.nan, 2.0 ** -10, 3 * 2.0 ** -10]])
+    x = np.concatenate([x, edges.astype(np.float32), -edges.astype(np.float32)])
+    assert np.array_equal(O.e4m3_encode(x.astype(np.float64)), _torch_e4m3(x))
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)
+    assert np.array_equal(O.e4m3_encode(O.decode_bits(codes, "e4m3")), codes)

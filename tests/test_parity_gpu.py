@@ -12,6 +12,7 @@ import pytest
 import torch
 
 from gpu_helpers import check, log, oracle_full, oracle_rows, run_gpu, upload
+from oracle import pa_oracle as O
 from paged_kv_cache_220_amd import binding as B
 from paged_kv_cache_220_amd import workloads as W
 
@@ -41,10 +42,11 @@ def kernels_for(w):
 
 
 SMALL = [("c1", {}), ("c2", dict(num_seqs=12)), ("c3", dict(num_seqs=2, seq_len=3000)),
-         ("c4", dict(num_seqs=20, seq_len=5000)), ("c5", dict(num_seqs=4, seq_len=2100))]
+         ("c4", dict(num_seqs=20, seq_len=5000)), ("c5", dict(num_seqs=4, seq_len=2100)),
+         ("c5", dict(num_seqs=4, seq_len=2100, kv_dtype="e4m3"))]
 
 
-@pytest.mark.parametrize("name,kw", SMALL, ids=[s[0] for s in SMALL])
+@pytest.mark.parametrize("name,kw", SMALL, ids=[s[0] + s[1].get("kv_dtype", "") for s in SMALL])
 @pytest.mark.parametrize("ptok", [0, 64, 256])
 def test_small_batches(name, kw, ptok):
     w = W.make_workload(name, **kw)
@@ -68,6 +70,8 @@ EDGE = [
     ("f32 G8 D128", dict(S=3, H=16, Hkv=2, D=128, seq_lens=[3, 64, 190], q_dtype="f32", kv_dtype="f32")),
     ("e5m2 G8 D128", dict(S=5, H=16, Hkv=2, D=128, seq_lens=[1, 16, 17, 64, 333], kv_dtype="e5m2")),
     ("e5m2 G4 D64", dict(S=3, H=8, Hkv=2, D=64, seq_lens=[9, 80, 260], kv_dtype="e5m2")),
+    ("e4m3 G8 D128", dict(S=5, H=16, Hkv=2, D=128, seq_lens=[1, 16, 17, 64, 333], kv_dtype="e4m3")),
+    ("e4m3 G4 D64", dict(S=3, H=8, Hkv=2, D=64, seq_lens=[9, 80, 260], kv_dtype="e4m3")),
 ]
 
 
@@ -95,7 +99,8 @@ def test_library_workspace_path_matches_caller_workspace():
 
 
 @pytest.mark.parametrize("name,kw", [("c1", {}), ("c2", dict(num_seqs=8)), ("c4", dict(num_seqs=12, seq_len=3000)),
-                                     ("c5", dict(num_seqs=3, seq_len=1500))])
+                                     ("c5", dict(num_seqs=3, seq_len=1500)),
+                                     ("c5", dict(num_seqs=3, seq_len=1500, kv_dtype="e4m3"))])
 def test_bitwise_repeat_relabel_poison(name, kw):
     w = W.make_workload(name, **kw)
     wp = W.permute_pool(w, 5)
@@ -155,3 +160,57 @@ def test_full_size_sampled(name, sample):
         del got
     del dev
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------ queue schedule --
+
+QUEUE = [("c4", dict(num_seqs=40, seq_len=6000), 0), ("c4", dict(num_seqs=40, seq_len=6000), 512),
+         ("c2", dict(num_seqs=16), 128), ("c5", dict(num_seqs=5, seq_len=2500), 1024),
+         ("c3", dict(num_seqs=2, seq_len=4100), 2048)]
+
+
+@pytest.mark.parametrize("name,kw,ptok", QUEUE, ids=[f"{q[0]}-P{q[2]}" for q in QUEUE])
+def test_queue_schedule_matches_grid(name, kw, ptok):
+    """The work-list schedule computes every item exactly as the grid does."""
+    w = W.make_workload(name, **kw)
+    dev = upload(w)
+    ref = oracle_full(w)
+    log(f"case queue {name}{kw} P={ptok}")
+    g = run_gpu(w, dev, kernel="mfma", partition_tokens=ptok, schedule="grid")
+    q = run_gpu(w, dev, kernel="mfma", partition_tokens=ptok, schedule="queue")
+    assert np.array_equal(g, q)
+    check(q, ref, w, f"queue {name} P={ptok}")
+
+
+def test_queue_schedule_edge_lengths():
+    w = W.random_edge_workload(31, S=9, H=16, Hkv=2, D=128, seq_lens=[0, 1, 15, 16, 17, 63, 64, 65, 900])
+    ref = oracle_full(w)
+    dev = upload(w)
+    for ptok in (64, 128):
+        got = run_gpu(w, dev, kernel="mfma", partition_tokens=ptok, schedule="queue")
+        check(got, ref, w, f"queue edge P={ptok}")
+        assert np.all(got[0] == 0)
+
+
+
+@pytest.mark.parametrize("kv_dtype", ["e5m2", "e4m3"])
+def test_every_fp8_code_decodes_exactly(kv_dtype):
+    """One-token sequences return their V row; two sequences cover all 256 codes.
+
+    The output is bf16, and every finite fp8 value is exact in bf16, so each
+    output element must equal the oracle's decoding of its code; non-finite
+    codes must give non-finite outputs."""
+    w = W.random_edge_workload(5, S=2, H=8, Hkv=1, D=128, seq_lens=[1, 1], kv_dtype=kv_dtype)
+    codes = np.arange(256, dtype=np.uint8)
+    for s in range(2):
+        w.v_cache[w.block_tables[s, 0], 0, :, 0] = codes[128 * s:128 * (s + 1)]
+        w.k_cache[w.block_tables[s, 0], 0, :, 0] = 0x3C if kv_dtype == "e5m2" else 0x38     # finite keys
+    dev = upload(w)
+    want = O.decode_bits(codes, kv_dtype).reshape(2, 128)
+    for kern in kernels_for(w):
+        got = run_gpu(w, dev, kernel=kern)
+        for s in range(2):
+            for h in range(8):
+                fin = np.isfinite(want[s])
+                assert np.array_equal(got[s, h][fin], want[s][fin]), (kern, s)
+                assert not np.isfinite(got[s, h][~fin]).any(), (kern, s)
