@@ -12,9 +12,11 @@
  *       k_cache[b][g][d][t] = encode(k_new[i][g][d] / k_scale)
  *       v_cache[b][g][d][t] = encode(v_new[i][g][d] / v_scale)
  *   for every KV head g and d < head_dim. encode() is the identity for an
- *   fp32 cache fed fp32, and rounds to nearest even otherwise (bf16, or OCP
- *   E5M2 with overflow to infinity). For an fp8 cache the division is one
- *   correctly rounded fp32 division; for other caches the scales must be 1.
+ *   fp32 cache fed fp32, and rounds to nearest even otherwise: bf16; OCP
+ *   E5M2, where values beyond the largest finite code go to infinity; OCP
+ *   E4M3 (no infinities), where values that round beyond 448 become NaN.
+ *   For an fp8 cache the division is one correctly rounded fp32 division;
+ *   for other caches the scales must be 1.
  *   A negative token_pos marks a padding entry that writes nothing.
  *
  * Copy on write ("Optimização da inferência" page, "PagedAttention": pages

@@ -114,6 +114,10 @@ typedef struct pa_dims {
                                   a zero row). Matrix-core kernel only:
                                   group * q_len <= 64.                                  */
   int32_t schedule;            /* pa_schedule_t                                        */
+  int32_t waves_per_item;      /* matrix-core kernel: waves that share one (sequence,
+                                  KV head, partition) item and merge their states in
+                                  LDS: 1, 2 or 4 (4 only with group * q_len <= 16);
+                                  0 = chosen by the library                          */
 } pa_dims_t;
 
 /* Decode with a workspace the library takes from the stream-ordered allocator
@@ -154,6 +158,8 @@ typedef struct pa_plan {
   int32_t grid_workgroups;     /* workgroups of the partition kernel                   */
   int32_t reduce_workgroups;   /* workgroups of the reduce kernel (0 = not launched)   */
   int32_t schedule;            /* pa_schedule_t actually used (never AUTO)             */
+  int32_t waves_per_item;      /* waves per work item actually used                    */
+  int32_t pad;
   size_t workspace_bytes;
 } pa_plan_t;
 

@@ -35,13 +35,15 @@ class PaDims(ctypes.Structure):
                 ("max_blocks_per_seq", ctypes.c_int32), ("q_dtype", ctypes.c_int32),
                 ("kv_dtype", ctypes.c_int32), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
                 ("max_seq_len", ctypes.c_int32), ("partition_tokens", ctypes.c_int32),
-                ("kernel", ctypes.c_int32), ("q_len", ctypes.c_int32), ("schedule", ctypes.c_int32)]
+                ("kernel", ctypes.c_int32), ("q_len", ctypes.c_int32), ("schedule", ctypes.c_int32),
+                ("waves_per_item", ctypes.c_int32)]
 
 
 class PaPlan(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("partition_tokens", ctypes.c_int32),
                 ("max_partitions", ctypes.c_int32), ("grid_workgroups", ctypes.c_int32),
                 ("reduce_workgroups", ctypes.c_int32), ("schedule", ctypes.c_int32),
+                ("waves_per_item", ctypes.c_int32), ("pad", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_size_t)]
 
 
@@ -118,7 +120,7 @@ def _kv_dtype_code(t: torch.Tensor, kv_dtype: Optional[str]) -> int:
 def make_dims(q: torch.Tensor, k_cache: torch.Tensor, block_tables: torch.Tensor, *,
               kv_dtype: Optional[str] = None, max_seq_len: int = 0, partition_tokens: int = 0,
               kernel: str = "auto", k_scale: float = 1.0, v_scale: float = 1.0,
-              schedule: str = "auto") -> PaDims:
+              schedule: str = "auto", waves_per_item: int = 0) -> PaDims:
     if q.dim() not in (3, 4) or k_cache.dim() != 4 or block_tables.dim() != 2:
         raise ValueError("q [S,H,D] or [S,q_len,H,D], k_cache [NB,Hkv,D,bs], block_tables [S,max_blocks] expected")
     if q.dtype not in _TORCH_DTYPES:
@@ -132,7 +134,7 @@ def make_dims(q: torch.Tensor, k_cache: torch.Tensor, block_tables: torch.Tensor
                   max_blocks_per_seq=block_tables.shape[1], q_dtype=_TORCH_DTYPES[q.dtype],
                   kv_dtype=_kv_dtype_code(k_cache, kv_dtype), k_scale=k_scale, v_scale=v_scale,
                   max_seq_len=max_seq_len, partition_tokens=partition_tokens, kernel=KERNELS[kernel], q_len=QL,
-                  schedule=SCHEDULES[schedule])
+                  schedule=SCHEDULES[schedule], waves_per_item=waves_per_item)
 
 
 def plan(dims: PaDims, num_kv_heads: int) -> dict:
@@ -141,7 +143,7 @@ def plan(dims: PaDims, num_kv_heads: int) -> dict:
     return dict(kernel=KERNEL_NAMES[p.kernel], partition_tokens=p.partition_tokens,
                 max_partitions=p.max_partitions, grid_workgroups=p.grid_workgroups,
                 reduce_workgroups=p.reduce_workgroups, workspace_bytes=p.workspace_bytes,
-                schedule=SCHEDULE_NAMES[p.schedule])
+                schedule=SCHEDULE_NAMES[p.schedule], waves_per_item=p.waves_per_item)
 
 
 def workspace_bytes(dims: PaDims, num_kv_heads: int) -> int:
@@ -173,7 +175,7 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, blo
               seq_lens: torch.Tensor, num_kv_heads: int, scale: float, out: Optional[torch.Tensor] = None, *,
               kv_dtype: Optional[str] = None, max_seq_len: int = 0, partition_tokens: int = 0,
               kernel: str = "auto", k_scale: float = 1.0, v_scale: float = 1.0, schedule: str = "auto",
-              workspace: Optional[torch.Tensor] = None, events=None) -> torch.Tensor:
+              waves_per_item: int = 0, workspace: Optional[torch.Tensor] = None, events=None) -> torch.Tensor:
     """PagedAttention decode through the C ABI; returns `out`.
 
     q may be [S, H, D] (one query per sequence) or [S, q_len, H, D] (the last
@@ -188,7 +190,7 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, blo
     _validate_tensors(q, k_cache, v_cache, block_tables, seq_lens, out)
     dims = make_dims(q, k_cache, block_tables, kv_dtype=kv_dtype, max_seq_len=max_seq_len,
                      partition_tokens=partition_tokens, kernel=kernel, k_scale=k_scale, v_scale=v_scale,
-                     schedule=schedule)
+                     schedule=schedule, waves_per_item=waves_per_item)
     lib = load_library()
     stream = ctypes.c_void_p(torch.cuda.current_stream(q.device).cuda_stream)
     args = (ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_cache.data_ptr()),
@@ -219,11 +221,11 @@ class DecodeCall:
 
     def __init__(self, q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale, out, *,
                  workspace=None, kv_dtype=None, max_seq_len=0, partition_tokens=0, kernel="auto",
-                 k_scale=1.0, v_scale=1.0, schedule="auto"):
+                 k_scale=1.0, v_scale=1.0, schedule="auto", waves_per_item=0):
         _validate_tensors(q, k_cache, v_cache, block_tables, seq_lens, out)
         self.dims = make_dims(q, k_cache, block_tables, kv_dtype=kv_dtype, max_seq_len=max_seq_len,
                               partition_tokens=partition_tokens, kernel=kernel, k_scale=k_scale, v_scale=v_scale,
-                              schedule=schedule)
+                              schedule=schedule, waves_per_item=waves_per_item)
         if workspace is None:
             workspace = alloc_workspace(self.dims, num_kv_heads, q.device)
         self._keep = (q, k_cache, v_cache, block_tables, seq_lens, out, workspace)

@@ -5,6 +5,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "pa_internal.h"
 
 namespace {
@@ -27,6 +29,7 @@ struct Plan {
   int partition_tokens = 0;
   int max_parts = 1;
   int schedule = PA_SCHEDULE_GRID;
+  int waves_per_item = 1;
   size_t off_m = 0, off_l = 0, off_items = 0, off_qlen = 0, ws_bytes = 0;
   long long grid = 0, reduce_grid = 0;
 };
@@ -46,6 +49,8 @@ int check_dims(const pa_dims_t* d, int32_t hkv) {
   if (d->q_len < 0) return PA_ERR_SHAPE;
   if (d->kernel < PA_KERNEL_AUTO || d->kernel > PA_KERNEL_MFMA) return PA_ERR_UNSUPPORTED;
   if (d->schedule < PA_SCHEDULE_AUTO || d->schedule > PA_SCHEDULE_QUEUE) return PA_ERR_UNSUPPORTED;
+  if (d->waves_per_item != 0 && d->waves_per_item != 1 && d->waves_per_item != 2 && d->waves_per_item != 4)
+    return PA_ERR_UNSUPPORTED;
   if (d->block_size != pa::kBlockSize) return PA_ERR_UNSUPPORTED;
   if ((long long)d->num_seqs * hkv > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;  // grid x limit
   const int group = d->num_heads / hkv;
@@ -72,22 +77,22 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
     p->kernel = d->kernel;
   }
   p->max_len = d->max_seq_len > 0 ? d->max_seq_len : d->max_blocks_per_seq * d->block_size;
+  // Every wave keeps one 64-token tile of K and V in flight. Covering HBM
+  // latency at full bandwidth takes about 2048 waves with bf16 / fp32 tiles
+  // (32 KiB) and 4096 with fp8 tiles (16 KiB). Partitions are made as long as
+  // possible (up to 4096 tokens: start-up and merge traffic are amortised) and
+  // the waves come from splitting each item over 1, 2 or 4 waves; partitions
+  // are shortened only when even 4 waves per item would not reach the target.
+  const long long units = (long long)d->num_seqs * hkv;
+  const bool fp8 = d->kv_dtype == PA_DTYPE_FP8_E5M2 || d->kv_dtype == PA_DTYPE_FP8_E4M3;
+  const long long target_waves = fp8 ? 4096 : 2048;
+  auto items_for = [&](long long P) { return units * ((p->max_len + P - 1) / P); };
   int P = d->partition_tokens;
   if (P == 0) {
-    // Each work item (sequence, KV head, partition) is one wavefront that
-    // keeps one 64-token tile of K and V in flight. Covering HBM latency at
-    // full bandwidth takes about 32 MiB in flight, i.e. 1024 items of 32 KiB
-    // (bf16 / fp32 tiles) or 2048 of 16 KiB (fp8 tiles). Among the partition
-    // lengths that give that many items, the longest is taken: it amortises
-    // each item's start-up and shrinks the partial states the merge reads.
-    const long long units = (long long)d->num_seqs * hkv;
-    const bool fp8 = d->kv_dtype == PA_DTYPE_FP8_E5M2 || d->kv_dtype == PA_DTYPE_FP8_E4M3;
-    const long long tile_bytes = 2LL * pa::kTileTokens * d->head_dim * (fp8 ? 1 : 2);
-    const long long want = (32LL << 20) / tile_bytes;
     long long cap = 4096;
     while (cap / 2 >= p->max_len && cap > pa::kTileTokens) cap /= 2;   // no longer than the longest sequence needs
     P = (int)cap;
-    while (P > 256 && units * ((p->max_len + P - 1) / P) < want) P /= 2;
+    while (P > 256 && items_for(P) * 4 < target_waves) P /= 2;
   }
   if (d->partition_tokens == 0) {
     while ((p->max_len + (long long)P - 1) / P > kMaxParts) P *= 2;   // grid y limit
@@ -109,6 +114,24 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
     p->schedule = PA_SCHEDULE_QUEUE;
   } else {
     p->schedule = PA_SCHEDULE_GRID;
+  }
+  // Waves per item (matrix-core kernel): the list schedule splits its long
+  // items four ways so the tail is short; the grid splits items until the
+  // wave target is met, keeping at least 4 tiles per wave.
+  const int ncg = (p->group * p->q_len + 15) / 16 <= 1 ? 1 : (p->group * p->q_len <= 32 ? 2 : 4);
+  if (p->kernel != PA_KERNEL_MFMA) {
+    if (d->waves_per_item > 1) return PA_ERR_UNSUPPORTED;
+    p->waves_per_item = 1;
+  } else if (d->waves_per_item > 0) {
+    if (!pa::mfma_waves_supported(ncg, d->waves_per_item)) return PA_ERR_UNSUPPORTED;
+    p->waves_per_item = d->waves_per_item;
+  } else if (p->schedule == PA_SCHEDULE_QUEUE) {
+    p->waves_per_item = ncg == 1 ? 4 : 2;
+  } else {
+    const long long tiles = (std::min<long long>(P, p->max_len) + pa::kTileTokens - 1) / pa::kTileTokens;
+    int nw = 1;
+    while (nw < 4 && p->grid * nw < target_waves && tiles >= 4LL * 2 * nw && pa::mfma_waves_supported(ncg, 2 * nw)) nw *= 2;
+    p->waves_per_item = nw;
   }
   size_t off = 0;
   if (p->max_parts > 1) {
@@ -178,6 +201,7 @@ int run(const void* q, const void* k_cache, const void* v_cache, const int32_t* 
     a.queue_len = reinterpret_cast<const int*>(ws + p.off_qlen);
     a.queue_workgroups = (int32_t)p.grid;            // the list never holds more items than the dense grid
   }
+  a.waves_per_item = p.waves_per_item;
 
   if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return PA_ERR_HIP;
   if (p.schedule == PA_SCHEDULE_QUEUE && pa::launch_plan(a, stream) != hipSuccess) return PA_ERR_HIP;
@@ -217,6 +241,7 @@ int pa_decode_plan(const pa_dims_t* dims, int32_t num_kv_heads, pa_plan_t* plan)
   plan->grid_workgroups = (int32_t)p.grid;
   plan->reduce_workgroups = (int32_t)p.reduce_grid;
   plan->schedule = p.schedule;
+  plan->waves_per_item = p.waves_per_item;
   plan->workspace_bytes = p.ws_bytes;
   return PA_OK;
 }

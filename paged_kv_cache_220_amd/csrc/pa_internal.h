@@ -38,6 +38,7 @@ struct Args {
   const int2* queue_items;
   const int* queue_len;
   int32_t queue_workgroups;
+  int32_t waves_per_item;   // matrix-core kernel: waves sharing one work item (1, 2, 4)
 };
 
 // Host-side launchers; each returns the hipError_t of the launch.
@@ -50,6 +51,7 @@ hipError_t launch_plan(const Args& a, hipStream_t stream);
 
 bool valu_supported(int q_dtype, int kv_dtype, int head_dim, int group);
 bool mfma_supported(int q_dtype, int kv_dtype, int head_dim, int group, int block_size, int q_len);
+bool mfma_waves_supported(int ncg, int nw);
 
 constexpr int kBlockSize = 16;     // tokens per physical block handled by the kernels
 constexpr int kTileTokens = 64;    // partition lengths are multiples of this

@@ -207,7 +207,7 @@ template <> struct Mfma<kE4M3> {
   }
 };
 
-template <int KDT, int NCG>
+template <int KDT, int NCG, int NW>
 __device__ __forceinline__ void partition_item(const Args& a, int group, int s, int kvh, int part) {
   using M = Mfma<KDT>;
   using op_t = typename M::op_t;
@@ -225,7 +225,8 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   const int tok0 = part * P;
   const int tok1 = min(L, tok0 + P);
 
-  const int lane = threadIdx.x;
+  const int wave = threadIdx.x >> 6;   // NW waves share the item: wave w takes tiles w, w + NW, ...
+  const int lane = threadIdx.x & 63;
   const int c = lane >> 4;   // lane group: k slots of the operands, rows 4c..4c+3 of results
   const int n = lane & 15;   // MFMA row of A (quartet / head_dim row) and column of B (virtual head)
 
@@ -288,10 +289,11 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     idv0 = table[bv0 < nblk_part ? bv0 : b0];
     idv1 = table[bv1 < nblk_part ? bv1 : b0];
   };
-  int32_t idk, idv0, idv1;
-  tile_ids(tok0 / BS, idk, idv0, idv1);
+  int32_t idk = 0, idv0 = 0, idv1 = 0;
+  const int first = tok0 + wave * kTile;
+  if (first < tok1) tile_ids(first / BS, idk, idv0, idv1);
 
-  for (int t0 = tok0; t0 < tok1; t0 += kTile) {
+  for (int t0 = first; t0 < tok1; t0 += NW * kTile) {
     const int64_t kb_off = clamp_block(a, idk) * blk_bytes;
     const int64_t vb_offs[2] = {clamp_block(a, idv0) * blk_bytes, clamp_block(a, idv1) * blk_bytes};
 
@@ -318,7 +320,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     }
     // Next tile's block ids behind this tile's loads; all 48 K/V loads of the
     // tile are in flight before any compute is scheduled.
-    if (t0 + kTile < tok1) tile_ids((t0 + kTile) / BS, idk, idv0, idv1);
+    if (t0 + NW * kTile < tok1) tile_ids((t0 + NW * kTile) / BS, idk, idv0, idv1);
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- S^T = K^T Q^T: MFMA j covers token j of every quartet; the K operand
@@ -416,6 +418,47 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     l_tot[cg] += shfl_xor_f32(l_tot[cg], 16);
     l_tot[cg] += shfl_xor_f32(l_tot[cg], 32);
   }
+  if constexpr (NW > 1) {
+    // Waves 1.. publish their (m, l, o) in LDS; wave 0 rescales them to the
+    // common max and adds them in wave order (the merge rule of the partition
+    // states, inside the workgroup), then writes the item's result.
+    __shared__ float sm_m[NW - 1][NCG][16];
+    __shared__ float sm_l[NW - 1][NCG][16];
+    __shared__ f32x4 sm_o[NW - 1][NCG][8][64];
+    if (wave > 0) {
+#pragma unroll
+      for (int cg = 0; cg < NCG; ++cg) {
+        if (c == 0) {
+          sm_m[wave - 1][cg][n] = m_run[cg];
+          sm_l[wave - 1][cg][n] = l_tot[cg];
+        }
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) sm_o[wave - 1][cg][dt][lane] = oacc[cg][dt];
+      }
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) {
+      float M = m_run[cg];
+#pragma unroll
+      for (int w = 0; w < NW - 1; ++w) M = fmaxf(M, sm_m[w][cg][n]);
+      const float Mu = M == -INFINITY ? 0.f : M;     // no token in the whole item: all weights 0
+      const float f0 = __builtin_amdgcn_exp2f(m_run[cg] - Mu);
+      float l = l_tot[cg] * f0;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) oacc[cg][dt] *= f0;
+#pragma unroll
+      for (int w = 0; w < NW - 1; ++w) {
+        const float f = __builtin_amdgcn_exp2f(sm_m[w][cg][n] - Mu);
+        l += sm_l[w][cg][n] * f;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) oacc[cg][dt] += sm_o[w][cg][dt][lane] * f;
+      }
+      m_run[cg] = M;
+      l_tot[cg] = l;
+    }
+  }
   const int64_t slot = ((int64_t)s * a.num_kv_heads + kvh) * a.max_parts + part;
 #pragma unroll
   for (int cg = 0; cg < NCG; ++cg) {
@@ -449,29 +492,35 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
 // One column group fits two waves per SIMD (<= 256 registers per lane), so
 // one wave's compute overlaps the other's loads; more groups take one wave.
 #define PA_MFMA_KERNEL_ATTRS \
-  __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCG == 1 ? 2 : 1, 8)))
+  __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NCG == 1 ? 2 : 1, 8)))
 
 // Grid schedule: one workgroup per (KV head, sequence, partition) of the dense grid.
-template <int KDT, int NCG>
+template <int KDT, int NCG, int NW>
 PA_MFMA_KERNEL_ATTRS void mfma_partition_kernel(const Args a, int group) {
   const Item it = work_item(a);
-  partition_item<KDT, NCG>(a, group, it.s, it.kvh, it.part);
+  partition_item<KDT, NCG, NW>(a, group, it.s, it.kvh, it.part);
 }
 
 // List schedule: workgroup i takes item i of the list the plan kernel built,
 // longest first, and workgroups past its end exit at once. Workgroups are
 // dispatched in index order, so long items start first and short ones fill
 // the end; consecutive (similar) items go to consecutive XCDs.
-template <int KDT, int NCG>
+template <int KDT, int NCG, int NW>
 PA_MFMA_KERNEL_ATTRS void mfma_partition_list_kernel(const Args a, int group) {
   const int idx = blockIdx.x;
   if (idx >= *a.queue_len) return;
   const int2 w = a.queue_items[idx];
   const int s = w.x / a.num_kv_heads;
-  partition_item<KDT, NCG>(a, group, s, w.x - s * a.num_kv_heads, w.y);
+  partition_item<KDT, NCG, NW>(a, group, s, w.x - s * a.num_kv_heads, w.y);
 }
 
 }  // namespace
+
+// Waves per item: 1, 2 or 4 with one column group; 1 or 2 with more (the
+// LDS exchange holds (NW - 1) x NCG x 8 KiB).
+bool mfma_waves_supported(int ncg, int nw) {
+  return nw == 1 || nw == 2 || (nw == 4 && ncg == 1);
+}
 
 bool mfma_supported(int q_dtype, int kv_dtype, int head_dim, int group, int block_size, int q_len) {
   return q_dtype == kBF16 && (kv_dtype == kBF16 || kv_dtype == kE5M2 || kv_dtype == kE4M3) && head_dim == kD &&
@@ -485,25 +534,28 @@ hipError_t launch_mfma(const Args& a, int q_dtype, int kv_dtype, int head_dim, i
   const int ncg = gv <= 16 ? 1 : gv <= 32 ? 2 : 4;
   const bool queue = a.queue_items != nullptr;
   const dim3 grid = queue ? dim3((unsigned)a.queue_workgroups) : partition_grid(a);   // list: one per possible item
-#define PA_LAUNCH(KDT, NCG)                                                            \
-  do {                                                                                 \
-    if (queue) mfma_partition_list_kernel<KDT, NCG><<<grid, 64, 0, stream>>>(a, group);  \
-    else mfma_partition_kernel<KDT, NCG><<<grid, 64, 0, stream>>>(a, group);             \
+  const int nw = a.waves_per_item;
+  if (!mfma_waves_supported(ncg, nw)) return hipErrorInvalidValue;
+#define PA_LAUNCH3(KDT, NCG, NW)                                                                  \
+  do {                                                                                            \
+    if (queue) mfma_partition_list_kernel<KDT, NCG, NW><<<grid, 64 * NW, 0, stream>>>(a, group);   \
+    else mfma_partition_kernel<KDT, NCG, NW><<<grid, 64 * NW, 0, stream>>>(a, group);              \
   } while (0)
-  if (kv_dtype == kBF16) {
-    if (ncg == 1) PA_LAUNCH(kBF16, 1);
-    else if (ncg == 2) PA_LAUNCH(kBF16, 2);
-    else PA_LAUNCH(kBF16, 4);
-  } else if (kv_dtype == kE5M2) {
-    if (ncg == 1) PA_LAUNCH(kE5M2, 1);
-    else if (ncg == 2) PA_LAUNCH(kE5M2, 2);
-    else PA_LAUNCH(kE5M2, 4);
-  } else {
-    if (ncg == 1) PA_LAUNCH(kE4M3, 1);
-    else if (ncg == 2) PA_LAUNCH(kE4M3, 2);
-    else PA_LAUNCH(kE4M3, 4);
-  }
+#define PA_LAUNCH(KDT)                                  \
+  do {                                                  \
+    if (ncg == 1 && nw == 1) PA_LAUNCH3(KDT, 1, 1);     \
+    else if (ncg == 1 && nw == 2) PA_LAUNCH3(KDT, 1, 2); \
+    else if (ncg == 1) PA_LAUNCH3(KDT, 1, 4);           \
+    else if (ncg == 2 && nw == 1) PA_LAUNCH3(KDT, 2, 1); \
+    else if (ncg == 2) PA_LAUNCH3(KDT, 2, 2);           \
+    else if (nw == 1) PA_LAUNCH3(KDT, 4, 1);            \
+    else PA_LAUNCH3(KDT, 4, 2);                         \
+  } while (0)
+  if (kv_dtype == kBF16) PA_LAUNCH(kBF16);
+  else if (kv_dtype == kE5M2) PA_LAUNCH(kE5M2);
+  else PA_LAUNCH(kE4M3);
 #undef PA_LAUNCH
+#undef PA_LAUNCH3
   return hipGetLastError();
 }
 

@@ -37,12 +37,13 @@ def upload(w, device="cuda"):
 
 
 def run_gpu(w, dev=None, kernel="auto", partition_tokens=0, use_workspace=True, max_seq_len=None,
-            schedule="auto"):
+            schedule="auto", waves_per_item=0):
     dev = dev or upload(w)
     out = torch.empty_like(dev["q"])
     msl = w.max_seq_len if max_seq_len is None else max_seq_len
     kw = dict(kernel=kernel, partition_tokens=partition_tokens, max_seq_len=msl,
-              k_scale=float(w.k_scale), v_scale=float(w.v_scale), schedule=schedule)
+              k_scale=float(w.k_scale), v_scale=float(w.v_scale), schedule=schedule,
+              waves_per_item=waves_per_item)
     ws = None
     if use_workspace:
         dims = B.make_dims(dev["q"], dev["k"], dev["tables"], **kw)

@@ -86,6 +86,10 @@ def status_of(d, hkv=8):
     (dict(schedule=2, kernel=1), 8, B.PA_ERR_UNSUPPORTED),       # queue: matrix-core kernel only
     (dict(schedule=2, partition_tokens=16384), 8, B.PA_ERR_UNSUPPORTED),   # > 128 tiles per item
     (dict(schedule=2), 8, B.PA_OK),
+    (dict(waves_per_item=3), 8, B.PA_ERR_UNSUPPORTED),
+    (dict(waves_per_item=4, q_len=4), 8, B.PA_ERR_UNSUPPORTED),  # 4 waves with one column group only
+    (dict(waves_per_item=2, kernel=1), 8, B.PA_ERR_UNSUPPORTED),
+    (dict(waves_per_item=4), 8, B.PA_OK),
 ])
 def test_validation_statuses(kw, hkv, expect):
     assert status_of(dims(**kw), hkv) == expect
@@ -104,12 +108,17 @@ def test_plan_long_context():
     assert p["grid_workgroups"] == 8 * 8 * 16 and p["reduce_workgroups"] == 64 * 16
     items = 16 * 8 * 8 * 8
     assert p["workspace_bytes"] >= items * (128 + 2) * 4
-    # fp8 tiles are half as large, so twice the items: 2048-token partitions
+    assert p["waves_per_item"] == 2                                      # 1024 items x 2 = 2048 waves
+    # fp8 tiles are half as large, so twice the waves: 1024 items x 4 waves
     pf = B.plan(dims(num_seqs=128, max_blocks_per_seq=256, kv_dtype=B.PA_DTYPE_FP8_E5M2), 8)
-    assert pf["partition_tokens"] == 2048 and pf["grid_workgroups"] == 2 * 8 * 128
+    assert pf["partition_tokens"] == 4096 and pf["grid_workgroups"] == 8 * 128 and pf["waves_per_item"] == 4
+    # one sequence: partitions shrink until 4 waves per item would reach 2048 waves
+    p1 = B.plan(dims(num_seqs=1), 8)
+    assert p1["partition_tokens"] == 512 and p1["grid_workgroups"] == 512 and p1["waves_per_item"] == 2
     # short chat batch: one partition per sequence, no merge
     pc = B.plan(dims(num_seqs=128, max_blocks_per_seq=32, max_seq_len=507), 8)
     assert pc["partition_tokens"] == 512 and pc["max_partitions"] == 1 and pc["workspace_bytes"] == 0
+    assert pc["waves_per_item"] == 2                                     # 8 tiles: 4 per wave
     p2 = B.plan(dims(partition_tokens=1024, max_seq_len=4096), 8)
     assert p2["max_partitions"] == 4 and p2["partition_tokens"] == 1024
 
@@ -119,7 +128,7 @@ def test_plan_schedule_choice():
     assert B.plan(dims(), 8)["schedule"] == "grid"
     # 256 x 8 units x 8 partitions = 16384 >> 2048 resident workgroups: work queue
     p = B.plan(dims(num_seqs=256, max_seq_len=32657), 8)
-    assert p["schedule"] == "queue" and p["partition_tokens"] == 4096
+    assert p["schedule"] == "queue" and p["partition_tokens"] == 4096 and p["waves_per_item"] == 4
     g = B.plan(dims(num_seqs=256, max_seq_len=32657, schedule=1), 8)
     assert g["schedule"] == "grid"
     assert p["workspace_bytes"] >= g["workspace_bytes"] + 16384 * 8      # item list

@@ -46,6 +46,25 @@ def test_multi_query_parity(name, kw, ql, ptok):
     check(got, ref, w, f"multi-query {name} q_len={ql} P={ptok}")
 
 
+@pytest.mark.parametrize("ql", [2, 4])
+def test_multi_query_two_waves_per_item(ql):
+    w = W.make_workload("c5", num_seqs=3, seq_len=2500)
+    rng = np.random.default_rng([ql, 77])
+    q = W.to_storage(rng.standard_normal((w.num_seqs, ql, w.num_heads, w.head_dim), dtype=np.float32), "bf16")
+    ref = O.paged_attention_multi(q, w.k_cache, w.v_cache, w.block_tables, w.seq_lens, w.num_kv_heads, w.scale,
+                                  "bf16", w.kv_dtype)
+    qd = _dev(q, "bf16")
+    for ptok in (0, 256):
+        out = torch.empty_like(qd)
+        log(f"case multi-query two waves q_len={ql} P={ptok}")
+        B.pa_decode(qd, _dev(w.k_cache, w.kv_dtype), _dev(w.v_cache, w.kv_dtype),
+                    torch.from_numpy(w.block_tables).cuda(), torch.from_numpy(w.seq_lens).cuda(), w.num_kv_heads,
+                    float(w.scale), out, partition_tokens=ptok, max_seq_len=w.max_seq_len, kernel="mfma",
+                    waves_per_item=2)
+        torch.cuda.synchronize()
+        check(out.float().cpu().numpy().astype(np.float64), ref, w, f"multi-query 2 waves q_len={ql} P={ptok}")
+
+
 def test_query_window_longer_than_sequence():
     """Early queries of a sequence shorter than the window see no token: zero rows."""
     w = W.random_edge_workload(3, S=4, H=16, Hkv=2, D=128, seq_lens=[1, 3, 70, 0])

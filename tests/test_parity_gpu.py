@@ -171,15 +171,51 @@ QUEUE = [("c4", dict(num_seqs=40, seq_len=6000), 0), ("c4", dict(num_seqs=40, se
 
 @pytest.mark.parametrize("name,kw,ptok", QUEUE, ids=[f"{q[0]}-P{q[2]}" for q in QUEUE])
 def test_queue_schedule_matches_grid(name, kw, ptok):
-    """The work-list schedule computes every item exactly as the grid does."""
+    """With the same waves per item, the work-list schedule computes every
+    item exactly as the grid does."""
     w = W.make_workload(name, **kw)
     dev = upload(w)
     ref = oracle_full(w)
-    log(f"case queue {name}{kw} P={ptok}")
-    g = run_gpu(w, dev, kernel="mfma", partition_tokens=ptok, schedule="grid")
-    q = run_gpu(w, dev, kernel="mfma", partition_tokens=ptok, schedule="queue")
-    assert np.array_equal(g, q)
-    check(q, ref, w, f"queue {name} P={ptok}")
+    for nw in (1, 4):
+        log(f"case queue {name}{kw} P={ptok} waves={nw}")
+        g = run_gpu(w, dev, kernel="mfma", partition_tokens=ptok, schedule="grid", waves_per_item=nw)
+        q = run_gpu(w, dev, kernel="mfma", partition_tokens=ptok, schedule="queue", waves_per_item=nw)
+        assert np.array_equal(g, q)
+        check(q, ref, w, f"queue {name} P={ptok} waves={nw}")
+
+
+# ---------------------------------------------------------- waves per item --
+
+WAVES = [("c2", dict(num_seqs=12), 512), ("c3", dict(num_seqs=2, seq_len=4100), 0),
+         ("c5", dict(num_seqs=6, seq_len=1900), 1024), ("c5", dict(num_seqs=4, seq_len=700, kv_dtype="e4m3"), 0),
+         ("c4", dict(num_seqs=30, seq_len=3000), 256)]
+
+
+@pytest.mark.parametrize("name,kw,ptok", WAVES, ids=[f"{c[0]}{c[1].get('kv_dtype', '')}-P{c[2]}" for c in WAVES])
+def test_waves_per_item(name, kw, ptok):
+    """Items split over 1, 2 or 4 waves (tiles strided over the waves, states
+    merged in LDS) all match the oracle, on both schedules."""
+    w = W.make_workload(name, **kw)
+    dev = upload(w)
+    ref = oracle_full(w)
+    for nw in (1, 2, 4):
+        for sched in ("grid", "queue"):
+            log(f"case waves {name}{kw} P={ptok} waves={nw} {sched}")
+            got = run_gpu(w, dev, kernel="mfma", partition_tokens=ptok, schedule=sched, waves_per_item=nw)
+            check(got, ref, w, f"waves {name} P={ptok} waves={nw} {sched}")
+
+
+def test_waves_per_item_edge_lengths():
+    """Waves past the end of a short item contribute an empty state."""
+    w = W.random_edge_workload(41, S=10, H=16, Hkv=2, D=128,
+                               seq_lens=[0, 1, 15, 16, 17, 63, 64, 65, 129, 300])
+    ref = oracle_full(w)
+    dev = upload(w)
+    for nw in (2, 4):
+        for ptok in (64, 128, 256):
+            got = run_gpu(w, dev, kernel="mfma", partition_tokens=ptok, waves_per_item=nw)
+            check(got, ref, w, f"waves edge P={ptok} waves={nw}")
+            assert np.all(got[0] == 0)
 
 
 def test_queue_schedule_edge_lengths():
