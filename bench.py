@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--op", default="decode", choices=["decode", "append", "copy"],
                     help="decode (default): the attention hot path; append / copy: the cache writes")
     ap.add_argument("--config", default="c3", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--kv-dtype", default="", choices=["", "bf16", "e5m2", "e4m3"],
+                    help="cache type in place of the batch's own (bf16-query batches c2..c5)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--schedule", default="auto", choices=["auto", "grid", "queue"])
@@ -180,13 +182,16 @@ def main():
         torch.cuda.synchronize()
         print(f"copy probe: {n} bytes read and written per dispatch", file=sys.stderr, flush=True)
         del src, dst
-    w = W.make_workload(args.config)
+    w = W.make_workload(args.config, kv_dtype=args.kv_dtype or None)
+    batch = args.config + (f"-{args.kv_dtype}" if args.kv_dtype else "")
 
     def upload(x, dtype):
         if dtype == "f32":
             return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
         if dtype == "bf16":
             return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+        if dtype == "e4m3":
+            return torch.from_numpy(np.ascontiguousarray(x)).view(torch.float8_e4m3fn).to(dev)
         return torch.from_numpy(np.ascontiguousarray(x)).view(torch.float8_e5m2).to(dev)
 
     kv_bytes = A.algorithmic_kv_bytes(w.seq_lens, w.num_kv_heads, w.head_dim, w.kv_dtype)
@@ -265,7 +270,7 @@ def main():
     part_avg = float(np.mean(part_ms))
     achieved = kv_bytes / (part_avg * 1e-3) / 1e9
     kname = "pa_mfma_partition" if plan["kernel"] == "mfma" else "pa_valu_partition"
-    traffic = load_traffic(kname, args.config, plan)
+    traffic = load_traffic(kname, batch, plan)
     result = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -279,7 +284,8 @@ def main():
         "vs_baseline": None,
         "dtype": w.kv_dtype,
         "data": "synthetic",
-        "config": {"workload": W.CONFIG_TITLES[args.config], "name": args.config,
+        "config": {"workload": W.CONFIG_TITLES[args.config] + (f", {w.kv_dtype} KV" if args.kv_dtype else ""),
+                   "name": batch,
                    "num_seqs": w.num_seqs, "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "block_size": w.block_size, "q_dtype": w.q_dtype,
                    "kv_dtype": w.kv_dtype, "total_tokens": int(w.seq_lens.sum()),

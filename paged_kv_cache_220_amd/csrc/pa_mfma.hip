@@ -45,6 +45,7 @@
 #include "pa_device.h"
 #include "pa_internal.h"
 
+
 namespace pa {
 namespace {
 
@@ -291,38 +292,46 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   };
   int32_t idk = 0, idv0 = 0, idv1 = 0;
   const int first = tok0 + wave * kTile;
+  constexpr int kStride = NW * kTile;
   if (first < tok1) tile_ids(first / BS, idk, idv0, idv1);
 
-  for (int t0 = first; t0 < tok1; t0 += NW * kTile) {
-    const int64_t kb_off = clamp_block(a, idk) * blk_bytes;
-    const int64_t vb_offs[2] = {clamp_block(a, idv0) * blk_bytes, clamp_block(a, idv1) * blk_bytes};
-
-    // ---- K loads: 4 k-steps x 8 rows, 4 tokens each. K/V bytes are used once
-    // per call, so they are loaded non-temporally (streamed past the caches).
+  // One tile's K and V registers.
+  struct Tile {
     kload_t kr[kKSteps][8];
+    vload_t vr[8][2];
+  };
+  // K loads: 4 k-steps x 8 rows, 4 tokens each; V loads: 8 row tiles x 2
+  // token halves, 8 tokens each. K/V bytes are used once per call, so they are
+  // loaded non-temporally (streamed past the caches).
+  auto load_k = [&](Tile& T, int32_t ik) __attribute__((always_inline)) {
+    const int64_t kb_off = clamp_block(a, ik) * blk_bytes;
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int d = 32 * ks + 4 * i + c;
-        kr[ks][i] = __builtin_nontemporal_load(reinterpret_cast<const kload_t*>(kbase + kb_off + d * kRowBytes + ktok * M::kElem));
+        T.kr[ks][i] = __builtin_nontemporal_load(reinterpret_cast<const kload_t*>(kbase + kb_off + d * kRowBytes + ktok * M::kElem));
       }
     }
-    // ---- V loads: 8 row tiles x 2 token halves, 8 tokens each
-    vload_t vr[8][2];
+  };
+  auto load_v = [&](Tile& T, int32_t iv0, int32_t iv1) __attribute__((always_inline)) {
+    const int64_t vb_offs[2] = {clamp_block(a, iv0) * blk_bytes, clamp_block(a, iv1) * blk_bytes};
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const int d = 16 * dt + n;
-        vr[dt][hh] = __builtin_nontemporal_load(reinterpret_cast<const vload_t*>(vbase + vb_offs[hh] + d * kRowBytes + 8 * (c & 1) * M::kElem));
+        T.vr[dt][hh] = __builtin_nontemporal_load(reinterpret_cast<const vload_t*>(vbase + vb_offs[hh] + d * kRowBytes + 8 * (c & 1) * M::kElem));
       }
     }
-    // Next tile's block ids behind this tile's loads; all 48 K/V loads of the
-    // tile are in flight before any compute is scheduled.
-    if (t0 + NW * kTile < tok1) tile_ids((t0 + NW * kTile) / BS, idk, idv0, idv1);
-    __builtin_amdgcn_sched_barrier(0);
-
+  };
+  auto load_tile = [&](Tile& T, int32_t ik, int32_t iv0, int32_t iv1) __attribute__((always_inline)) {
+    load_k(T, ik);
+    load_v(T, iv0, iv1);
+  };
+  op_t phi[NCG][2], plo[NCG][2];   // P of the current tile (hi / lo), from qk_softmax to pv
+  auto qk_softmax = [&](Tile& T, const int t0) __attribute__((always_inline)) {
+    auto& kr = T.kr;
     // ---- S^T = K^T Q^T: MFMA j covers token j of every quartet; the K operand
     // is shared by all column groups
     f32x4 sacc[NCG][4];
@@ -338,7 +347,6 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     }
 
     // ---- online softmax per column over this tile
-    op_t phi[NCG][2], plo[NCG][2];
 #pragma unroll
     for (int cg = 0; cg < NCG; ++cg) {
       const int nval = min(tok1, lim[cg]) - t0;   // this column's tokens in the tile (may be <= 0)
@@ -385,6 +393,9 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
       }
     }
 
+  };
+  auto pv = [&](Tile& T, const int t0) __attribute__((always_inline)) {
+    auto& vr = T.vr;
     // ---- O^T += V P^T
     const int nvalid = tok1 - t0;   // tokens of this tile inside the partition (may exceed 64)
     if (nvalid < kTile) {
@@ -407,6 +418,50 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
           oacc[cg][dt] = M::mma(vop, plo[cg][hh], oacc[cg][dt]);
         }
       }
+    }
+  };
+
+  if constexpr (M::kElem == 1) {
+    // fp8: the next tile's K loads go out as soon as this tile's QK has read
+    // its K registers, and its V loads as soon as PV has read V, so loads stay
+    // in flight while the softmax and PV of this tile run. Block ids are
+    // fetched two tiles ahead, in front of the K loads that precede their use.
+    const int last_blk = nblk_part - 1;
+    auto ids_at = [&](int t, int32_t& ik, int32_t& iv0, int32_t& iv1) __attribute__((always_inline)) {
+      tile_ids(min(t / BS, last_blk), ik, iv0, iv1);
+    };
+    if (first < tok1) {
+      Tile T;
+      int32_t nk, nv0, nv1;
+      ids_at(first + kStride, nk, nv0, nv1);
+      load_tile(T, idk, idv0, idv1);
+      __builtin_amdgcn_sched_barrier(0);
+      for (int t0 = first; t0 < tok1; t0 += kStride) {
+        const bool more = t0 + kStride < tok1;
+        qk_softmax(T, t0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) {
+          ids_at(t0 + 2 * kStride, idk, idv0, idv1);
+          load_k(T, nk);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        pv(T, t0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) load_v(T, nv0, nv1);
+        __builtin_amdgcn_sched_barrier(0);
+        nk = idk; nv0 = idv0; nv1 = idv1;
+      }
+    }
+  } else {
+    for (int t0 = first; t0 < tok1; t0 += kStride) {
+      Tile T;
+      load_tile(T, idk, idv0, idv1);
+      // Next tile's block ids behind this tile's loads; all 48 K/V loads of the
+      // tile are in flight before any compute is scheduled.
+      if (t0 + kStride < tok1) tile_ids((t0 + kStride) / BS, idk, idv0, idv1);
+      __builtin_amdgcn_sched_barrier(0);
+      qk_softmax(T, t0);
+      pv(T, t0);
     }
   }
 
