@@ -329,74 +329,70 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     load_k(T, ik);
     load_v(T, iv0, iv1);
   };
-  op_t phi[NCG][2], plo[NCG][2];   // P of the current tile (hi / lo), from qk_softmax to pv
-  auto qk_softmax = [&](Tile& T, const int t0) __attribute__((always_inline)) {
-    auto& kr = T.kr;
-    // ---- S^T = K^T Q^T: MFMA j covers token j of every quartet; the K operand
-    // is shared by all column groups
-    f32x4 sacc[NCG][4];
+  // ---- S^T = K^T Q^T: MFMA j covers token j of every quartet; the K operand
+  // is shared by all column groups
+  auto qk = [&](Tile& T, f32x4 (&sacc)[NCG][4]) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) {
-        const op_t kop = M::k_operand(kr[ks], j);
+        const op_t kop = M::k_operand(T.kr[ks], j);
 #pragma unroll
         for (int cg = 0; cg < NCG; ++cg)
           sacc[cg][j] = M::mma(kop, qop[cg][ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[cg][j]);
       }
     }
-
-    // ---- online softmax per column over this tile
+  };
+  // ---- online softmax of column group cg over this tile; P leaves as two
+  // 16-bit PV operands per instruction hh (rounded weight and its residual)
+  auto softmax = [&](const int cg, const f32x4 (&sg)[4], const int t0, op_t (&phi)[2], op_t (&plo)[2])
+      __attribute__((always_inline)) {
+    const int nval = min(tok1, lim[cg]) - t0;   // this column's tokens in the tile (may be <= 0)
+    float sc[4][4];                             // [r][j]; tokens outside the window: -inf
+    float tmax = -INFINITY;
 #pragma unroll
-    for (int cg = 0; cg < NCG; ++cg) {
-      const int nval = min(tok1, lim[cg]) - t0;   // this column's tokens in the tile (may be <= 0)
-      float sc[4][4];                             // [r][j]; tokens outside the window: -inf
-      float tmax = -INFINITY;
+    for (int r = 0; r < 4; ++r) {
+      const int tt = 16 * ((c >> 1) + 2 * (r >> 1)) + 8 * (c & 1) + 4 * (r & 1);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tt = 16 * ((c >> 1) + 2 * (r >> 1)) + 8 * (c & 1) + 4 * (r & 1);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          sc[r][j] = (tt + j < nval) ? sacc[cg][j][r] * a.score_scale : -INFINITY;
-          tmax = fmaxf(tmax, sc[r][j]);
-        }
-      }
-      tmax = fmaxf(tmax, shfl_xor_f32(tmax, 16));
-      tmax = fmaxf(tmax, shfl_xor_f32(tmax, 32));
-      const float m_new = fmaxf(m_run[cg], tmax);
-      // A column with no token yet keeps m = -inf. Subtracting 0 instead of -inf
-      // then makes every weight and the rescale 2^-inf = 0, so its state stays
-      // zero and -inf - -inf is never formed.
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[cg] - m_use);
-      m_run[cg] = m_new;
-      float psum = 0.f;
-      float p[4][4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          p[r][j] = __builtin_amdgcn_exp2f(sc[r][j] - m_use);
-          psum += p[r][j];
-        }
-      }
-      l_run[cg] = l_run[cg] * alpha + psum;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) oacc[cg][dt] *= alpha;
-      // PV instruction hh takes quartets r = 2hh, 2hh+1
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        float pv[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pv[i] = p[2 * hh + (i >> 2)][i & 3];
-        M::p_operands(pv, phi[cg][hh], plo[cg][hh]);
+      for (int j = 0; j < 4; ++j) {
+        sc[r][j] = (tt + j < nval) ? sg[j][r] * a.score_scale : -INFINITY;
+        tmax = fmaxf(tmax, sc[r][j]);
       }
     }
-
+    tmax = fmaxf(tmax, shfl_xor_f32(tmax, 16));
+    tmax = fmaxf(tmax, shfl_xor_f32(tmax, 32));
+    const float m_new = fmaxf(m_run[cg], tmax);
+    // A column with no token yet keeps m = -inf. Subtracting 0 instead of -inf
+    // then makes every weight and the rescale 2^-inf = 0, so its state stays
+    // zero and -inf - -inf is never formed.
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run[cg] - m_use);
+    m_run[cg] = m_new;
+    float psum = 0.f;
+    float p[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        p[r][j] = __builtin_amdgcn_exp2f(sc[r][j] - m_use);
+        psum += p[r][j];
+      }
+    }
+    l_run[cg] = l_run[cg] * alpha + psum;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) oacc[cg][dt] *= alpha;
+    // PV instruction hh takes quartets r = 2hh, 2hh+1
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      float pv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pv[i] = p[2 * hh + (i >> 2)][i & 3];
+      M::p_operands(pv, phi[hh], plo[hh]);
+    }
   };
-  auto pv = [&](Tile& T, const int t0) __attribute__((always_inline)) {
-    auto& vr = T.vr;
-    // ---- O^T += V P^T
+  // V values of token slots at or past the partition end are zeroed: their
+  // weights are 0, but 0 * NaN would poison the sum.
+  auto mask_tail = [&](Tile& T, const int t0) __attribute__((always_inline)) {
     const int nvalid = tok1 - t0;   // tokens of this tile inside the partition (may exceed 64)
     if (nvalid < kTile) {
 #pragma unroll
@@ -404,28 +400,60 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
         const int seg = 16 * ((c >> 1) + 2 * hh) + 8 * (c & 1);
         const int nv = min(8, max(0, nvalid - seg));
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) vr[dt][hh] = M::mask_v(vr[dt][hh], nv);
+        for (int dt = 0; dt < 8; ++dt) T.vr[dt][hh] = M::mask_v(T.vr[dt][hh], nv);
       }
     }
+  };
+  // One tile: QK, then `after_qk` (the K registers are free from here on),
+  // then softmax and O^T += V P^T. With V operands used as loaded (bf16) each
+  // column group's PV follows its softmax, so only one group's P is live;
+  // widened fp8 V operands are instead shared by all groups' MFMAs.
+  auto tile_step = [&](Tile& T, const int t0, auto&& after_qk) __attribute__((always_inline)) {
+    f32x4 sacc[NCG][4];
+    qk(T, sacc);
+    after_qk();
+    mask_tail(T, t0);
+    if constexpr (M::kElem == 2) {
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
+      for (int cg = 0; cg < NCG; ++cg) {
+        op_t phi[2], plo[2];
+        softmax(cg, sacc[cg], t0, phi, plo);
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const op_t vop = M::v_operand(vr[dt][hh]);
+        for (int dt = 0; dt < 8; ++dt) {
 #pragma unroll
-        for (int cg = 0; cg < NCG; ++cg) {
-          oacc[cg][dt] = M::mma(vop, phi[cg][hh], oacc[cg][dt]);
-          oacc[cg][dt] = M::mma(vop, plo[cg][hh], oacc[cg][dt]);
+          for (int hh = 0; hh < 2; ++hh) {
+            const op_t vop = M::v_operand(T.vr[dt][hh]);
+            oacc[cg][dt] = M::mma(vop, phi[hh], oacc[cg][dt]);
+            oacc[cg][dt] = M::mma(vop, plo[hh], oacc[cg][dt]);
+          }
+        }
+      }
+    } else {
+      op_t phi[NCG][2], plo[NCG][2];
+#pragma unroll
+      for (int cg = 0; cg < NCG; ++cg) softmax(cg, sacc[cg], t0, phi[cg], plo[cg]);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const op_t vop = M::v_operand(T.vr[dt][hh]);
+#pragma unroll
+          for (int cg = 0; cg < NCG; ++cg) {
+            oacc[cg][dt] = M::mma(vop, phi[cg][hh], oacc[cg][dt]);
+            oacc[cg][dt] = M::mma(vop, plo[cg][hh], oacc[cg][dt]);
+          }
         }
       }
     }
   };
 
-  if constexpr (M::kElem == 1) {
+  if constexpr (M::kElem == 1 && NCG == 1) {
     // fp8: the next tile's K loads go out as soon as this tile's QK has read
     // its K registers, and its V loads as soon as PV has read V, so loads stay
     // in flight while the softmax and PV of this tile run. Block ids are
     // fetched two tiles ahead, in front of the K loads that precede their use.
+    // (One column group only: with more, the kernel is at one wave per SIMD
+    // and has no registers to spare for it.)
     const int last_blk = nblk_part - 1;
     auto ids_at = [&](int t, int32_t& ik, int32_t& iv0, int32_t& iv1) __attribute__((always_inline)) {
       tile_ids(min(t / BS, last_blk), ik, iv0, iv1);
@@ -438,14 +466,14 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
       __builtin_amdgcn_sched_barrier(0);
       for (int t0 = first; t0 < tok1; t0 += kStride) {
         const bool more = t0 + kStride < tok1;
-        qk_softmax(T, t0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (more) {
-          ids_at(t0 + 2 * kStride, idk, idv0, idv1);
-          load_k(T, nk);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        pv(T, t0);
+        tile_step(T, t0, [&]() __attribute__((always_inline)) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (more) {
+            ids_at(t0 + 2 * kStride, idk, idv0, idv1);
+            load_k(T, nk);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        });
         __builtin_amdgcn_sched_barrier(0);
         if (more) load_v(T, nv0, nv1);
         __builtin_amdgcn_sched_barrier(0);
@@ -460,8 +488,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
       // tile are in flight before any compute is scheduled.
       if (t0 + kStride < tok1) tile_ids((t0 + kStride) / BS, idk, idv0, idv1);
       __builtin_amdgcn_sched_barrier(0);
-      qk_softmax(T, t0);
-      pv(T, t0);
+      tile_step(T, t0, []() __attribute__((always_inline)) {});
     }
   }
 

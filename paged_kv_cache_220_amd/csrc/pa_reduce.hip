@@ -16,8 +16,9 @@
 // One workgroup of 256 threads per (sequence, query head): 8 partition
 // groups x 32 column groups of 4 output elements. Each thread walks every
 // 8th partition with 128-bit loads of o_p (a wave reads 512 contiguous bytes
-// per partition), then the 8 partial sums meet in LDS in a fixed order, so
-// the result does not depend on timing.
+// per partition), folding them into a running (m, l, o) by the same rule, so
+// all loads go out in one round trip; the 8 group states then meet in LDS in
+// a fixed order, so the result does not depend on timing.
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -45,61 +46,63 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(const Args a, int head
   const int64_t orow = (((int64_t)s * a.q_len + qi) * a.num_heads + h) * head_dim;
   const int tid = threadIdx.x;
 
-  __shared__ float red_m[kThreads / 64];
-  __shared__ float red_o[kGroups][kCols * 4];
+  __shared__ float red_m[kGroups];
   __shared__ float red_l[kGroups];
-
-  // M = max over partitions (strided over all threads, then wave and LDS reduction)
-  float mloc = -INFINITY;
-  for (int p = tid; p < nparts; p += kThreads) mloc = fmaxf(mloc, a.part_m[(item0 + p) * GV + g]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) mloc = fmaxf(mloc, shfl_xor_f32(mloc, off));
-  if ((tid & 63) == 0) red_m[tid >> 6] = mloc;
-  __syncthreads();
-  float M = red_m[0];
-#pragma unroll
-  for (int w = 1; w < kThreads / 64; ++w) M = fmaxf(M, red_m[w]);
-  if (M == -INFINITY) {
-    // no partition saw a token this query may attend (query window longer than the sequence)
-    if (tid < head_dim) store_out<QDT>(a.out, orow + tid, 0.f);
-    return;
-  }
+  __shared__ float red_o[kGroups][kCols * 4];
 
   const int pg = tid / kCols;
   const int col = (tid % kCols) * 4;
   const bool active = col < head_dim;
-  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-  float den = 0.f;
+  // Running state of this partition group. A group that has seen no token
+  // keeps m = -inf; subtracting 0 instead then gives weights 2^-inf = 0.
+  float m = -INFINITY, l = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 2
   for (int p = pg; p < nparts; p += kGroups) {
     const int64_t it = (item0 + p) * GV + g;
-    const float w = exp2f(a.part_m[it] - M);
-    den = fmaf(w, a.part_l[it], den);
-    if (active) {
-      const float4 o = *reinterpret_cast<const float4*>(a.part_o + it * head_dim + col);
-      num.x = fmaf(w, o.x, num.x);
-      num.y = fmaf(w, o.y, num.y);
-      num.z = fmaf(w, o.z, num.z);
-      num.w = fmaf(w, o.w, num.w);
-    }
+    const float mp = a.part_m[it];
+    const float lp = a.part_l[it];
+    const float4 op = active ? *reinterpret_cast<const float4*>(a.part_o + it * head_dim + col)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float mn = fmaxf(m, mp);
+    const float mu = mn == -INFINITY ? 0.f : mn;
+    const float sa = exp2f(m - mu), sb = exp2f(mp - mu);
+    l = l * sa + lp * sb;
+    o.x = o.x * sa + op.x * sb;
+    o.y = o.y * sa + op.y * sb;
+    o.z = o.z * sa + op.z * sb;
+    o.w = o.w * sa + op.w * sb;
+    m = mn;
   }
   if (active) {
-    red_o[pg][col + 0] = num.x;
-    red_o[pg][col + 1] = num.y;
-    red_o[pg][col + 2] = num.z;
-    red_o[pg][col + 3] = num.w;
+    red_o[pg][col + 0] = o.x;
+    red_o[pg][col + 1] = o.y;
+    red_o[pg][col + 2] = o.z;
+    red_o[pg][col + 3] = o.w;
   }
-  if (tid % kCols == 0) red_l[pg] = den;
+  if (tid % kCols == 0) {
+    red_m[pg] = m;
+    red_l[pg] = l;
+  }
   __syncthreads();
 
   if (tid < head_dim) {
-    float acc = 0.f, l = 0.f;
+    float M = red_m[0];
+#pragma unroll
+    for (int k = 1; k < kGroups; ++k) M = fmaxf(M, red_m[k]);
+    if (M == -INFINITY) {
+      // no partition saw a token this query may attend (query window longer than the sequence)
+      store_out<QDT>(a.out, orow + tid, 0.f);
+      return;
+    }
+    float acc = 0.f, den = 0.f;
 #pragma unroll
     for (int k = 0; k < kGroups; ++k) {
-      acc += red_o[k][tid];
-      l += red_l[k];
+      const float w = exp2f(red_m[k] - M);
+      acc += red_o[k][tid] * w;
+      den += red_l[k] * w;
     }
-    store_out<QDT>(a.out, orow + tid, acc / l);
+    store_out<QDT>(a.out, orow + tid, acc / den);
   }
 }
 

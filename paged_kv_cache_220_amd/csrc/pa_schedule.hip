@@ -45,15 +45,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const Args a) {
     *const_cast<int*>(a.queue_len) = off;
   }
   __syncthreads();
+  // Each sequence reserves its items of a bucket as one run (one LDS atomic
+  // per bucket it touches, not one per item) and fills the run in order.
   for (int s = tid; s < a.num_seqs; s += kPlanThreads) {
     const int L = clamp_len(a, s);
     const int nfull = L / P;
     const int rem = L - nfull * P;
-    const int bucket = (rem + kTileTokens - 1) / kTileTokens;
-    for (int g = 0; g < hkv; ++g) {
-      const int unit = s * hkv + g;
-      for (int p = 0; p < nfull; ++p) items[atomicAdd(&cur[full], 1)] = make_int2(unit, p);
-      if (rem > 0 || L == 0) items[atomicAdd(&cur[bucket], 1)] = make_int2(unit, nfull);
+    if (nfull > 0) {
+      int2* run = items + atomicAdd(&cur[full], nfull * hkv);
+      for (int g = 0; g < hkv; ++g)
+        for (int p = 0; p < nfull; ++p) run[g * nfull + p] = make_int2(s * hkv + g, p);
+    }
+    if (rem > 0 || L == 0) {
+      int2* run = items + atomicAdd(&cur[(rem + kTileTokens - 1) / kTileTokens], hkv);
+      for (int g = 0; g < hkv; ++g) run[g] = make_int2(s * hkv + g, nfull);
     }
   }
 }

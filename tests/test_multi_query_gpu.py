@@ -24,6 +24,8 @@ CASES = [
     ("c2", dict(num_seqs=6), 4),                   # two column groups
     ("c5", dict(num_seqs=4, seq_len=2100), 8),     # four column groups, fp8 cache
     ("c3", dict(num_seqs=2, seq_len=5000), 3),
+    ("c2", dict(num_seqs=6), 8),                   # bf16, four full column groups
+    ("c3", dict(num_seqs=2, seq_len=3000), 5),     # bf16, 40 columns: the last group part-filled
 ]
 
 
