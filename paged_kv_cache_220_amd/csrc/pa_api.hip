@@ -77,15 +77,14 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
     p->kernel = d->kernel;
   }
   p->max_len = d->max_seq_len > 0 ? d->max_seq_len : d->max_blocks_per_seq * d->block_size;
-  // Every wave keeps one 64-token tile of K and V in flight. Covering HBM
-  // latency at full bandwidth takes about 2048 waves with bf16 / fp32 tiles
-  // (32 KiB) and 4096 with fp8 tiles (16 KiB). Partitions are made as long as
+  // Every wave keeps about one 64-token tile of K and V in flight (the fp8
+  // kernel keeps its next tile in flight while computing). Covering HBM
+  // latency at full bandwidth takes about 2048 waves. Partitions are made as long as
   // possible (up to 4096 tokens: start-up and merge traffic are amortised) and
   // the waves come from splitting each item over 1, 2 or 4 waves; partitions
   // are shortened only when even 4 waves per item would not reach the target.
   const long long units = (long long)d->num_seqs * hkv;
-  const bool fp8 = d->kv_dtype == PA_DTYPE_FP8_E5M2 || d->kv_dtype == PA_DTYPE_FP8_E4M3;
-  const long long target_waves = fp8 ? 4096 : 2048;
+  const long long target_waves = 2048;
   auto items_for = [&](long long P) { return units * ((p->max_len + P - 1) / P); };
   int P = d->partition_tokens;
   if (P == 0) {

@@ -12,13 +12,15 @@
 //
 // The cache tile is [head_dim][16 tokens] with tokens fastest, which suits PV
 // directly (a 128-bit load is 8 tokens of one row) but not QK, whose operand
-// wants several head_dim values of one token per lane. The kernel gets them
-// without LDS: each lane loads 8 rows x 4 tokens (one 64-bit load per row)
-// and transposes them in registers with v_perm_b32, feeding 4 MFMAs (one per
-// token of the quartet). The MFMA k index may map to head_dim in any order as
-// long as the Q operand uses the same order, so lane group c takes rows
-// 32*kstep + 4*i + c, which makes every load instruction cover whole
-// 128-byte lines.
+// wants several head_dim values of one token per lane. Each lane takes 8
+// rows x 4 tokens and transposes them in registers with v_perm_b32, feeding
+// 4 MFMAs (one per token of the quartet). The MFMA k index may map to
+// head_dim in any order as long as the Q operand uses the same order, so lane
+// group c takes rows 32*kstep + 4*i + c. For bf16 those are 64-bit loads
+// straight from HBM, and every load instruction covers whole 128-byte lines.
+// For fp8 the 4-token pieces are only 4 bytes, so the K tile is first copied
+// into LDS as whole rows by direct global-to-LDS loads, and the pieces are
+// read from there.
 //
 // A tile is 64 tokens = 4 physical blocks. MFMA row (quartet) q = 4c + r of
 // the QK step holds block (c >> 1) + 2 * (r >> 1), tokens 8 * (c & 1) +
@@ -226,7 +228,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   const int tok0 = part * P;
   const int tok1 = min(L, tok0 + P);
 
-  const int wave = threadIdx.x >> 6;   // NW waves share the item: wave w takes tiles w, w + NW, ...
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // NW waves share the item: wave w takes tiles w, w + NW, ...
   const int lane = threadIdx.x & 63;
   const int c = lane >> 4;   // lane group: k slots of the operands, rows 4c..4c+3 of results
   const int n = lane & 15;   // MFMA row of A (quartet / head_dim row) and column of B (virtual head)
@@ -448,36 +450,73 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   };
 
   if constexpr (M::kElem == 1 && NCG == 1) {
-    // fp8: the next tile's K loads go out as soon as this tile's QK has read
-    // its K registers, and its V loads as soon as PV has read V, so loads stay
-    // in flight while the softmax and PV of this tile run. Block ids are
-    // fetched two tiles ahead, in front of the K loads that precede their use.
-    // (One column group only: with more, the kernel is at one wave per SIMD
-    // and has no registers to spare for it.)
+    // fp8, one column group. A K tile is 4 block tiles of 128 rows x 16 one-byte
+    // tokens; it lands in this wave's LDS slot through direct global-to-LDS
+    // loads of whole 16-byte rows (each instruction reads 1 KiB contiguous),
+    // and QK reads each lane's 4-token pieces back from LDS. (Loading those
+    // 4-byte pieces straight from HBM touches half of every 128-byte line per
+    // instruction and runs the memory pipeline 25 % slower.) Block slots are
+    // 64 bytes apart beyond their 2 KiB so the four blocks of a read fall in
+    // different LDS banks.
+    //
+    // Pipeline: K of the next tile is issued right after this tile's QK (its
+    // slot is free again) and V of the next tile right after PV (into the V
+    // registers PV has released). The four block ids of a tile are the same
+    // for the whole wave; they are fetched two tiles ahead.
+    typedef __attribute__((address_space(3))) void* lds_ptr_t;
+    typedef __attribute__((address_space(1))) void* gbl_ptr_t;
+    constexpr int kSlotBlk = kD * kBlockSize + 64;
+    __shared__ __attribute__((aligned(16))) uint8_t k_lds[NW][4 * kSlotBlk];
+    uint8_t* kslot = &k_lds[wave][0];
+    const uint8_t* krow = kslot + kblk * kSlotBlk + c * kBlockSize + ktok;   // + 16 * (32 ks + 4 i)
     const int last_blk = nblk_part - 1;
-    auto ids_at = [&](int t, int32_t& ik, int32_t& iv0, int32_t& iv1) __attribute__((always_inline)) {
-      tile_ids(min(t / BS, last_blk), ik, iv0, iv1);
+    auto ids_at = [&](int t, int32_t (&ib)[4]) __attribute__((always_inline)) {
+      const int b0 = min(t / BS, last_blk);
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) ib[blk] = clamp_block(a, table[b0 + blk < nblk_part ? b0 + blk : b0]);
+    };
+    auto load_k_lds = [&](const int32_t (&ib)[4]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        const char* src = kbase + ib[blk] * blk_bytes + lane * 16;
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+          __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src + half * 1024),
+                                           (lds_ptr_t)(kslot + blk * kSlotBlk + half * 1024), 16, 0, 2);
+      }
+    };
+    auto load_v_ids = [&](Tile& T, const int32_t (&ib)[4]) __attribute__((always_inline)) {
+      load_v(T, (c >> 1) == 0 ? ib[0] : ib[1], (c >> 1) == 0 ? ib[2] : ib[3]);
     };
     if (first < tok1) {
       Tile T;
-      int32_t nk, nv0, nv1;
-      ids_at(first + kStride, nk, nv0, nv1);
-      load_tile(T, idk, idv0, idv1);
+      int32_t icur[4], inext[4];
+      ids_at(first, icur);
+      ids_at(first + kStride, inext);
+      load_k_lds(icur);
+      load_v_ids(T, icur);
       __builtin_amdgcn_sched_barrier(0);
       for (int t0 = first; t0 < tok1; t0 += kStride) {
         const bool more = t0 + kStride < tok1;
+#pragma unroll
+        for (int ks = 0; ks < kKSteps; ++ks) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            T.kr[ks][i] = *reinterpret_cast<const kload_t*>(krow + (32 * ks + 4 * i) * kBlockSize);
+        }
         tile_step(T, t0, [&]() __attribute__((always_inline)) {
           __builtin_amdgcn_sched_barrier(0);
           if (more) {
-            ids_at(t0 + 2 * kStride, idk, idv0, idv1);
-            load_k(T, nk);
+            ids_at(t0 + 2 * kStride, icur);
+            load_k_lds(inext);
           }
           __builtin_amdgcn_sched_barrier(0);
         });
         __builtin_amdgcn_sched_barrier(0);
-        if (more) load_v(T, nv0, nv1);
+        if (more) load_v_ids(T, inext);
         __builtin_amdgcn_sched_barrier(0);
-        nk = idk; nv0 = idv0; nv1 = idv1;
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) inext[blk] = icur[blk];
       }
     }
   } else {

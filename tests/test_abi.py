@@ -109,9 +109,9 @@ def test_plan_long_context():
     items = 16 * 8 * 8 * 8
     assert p["workspace_bytes"] >= items * (128 + 2) * 4
     assert p["waves_per_item"] == 2                                      # 1024 items x 2 = 2048 waves
-    # fp8 tiles are half as large, so twice the waves: 1024 items x 4 waves
+    # the fp8 batch takes the same wave target: 1024 items x 2 waves
     pf = B.plan(dims(num_seqs=128, max_blocks_per_seq=256, kv_dtype=B.PA_DTYPE_FP8_E5M2), 8)
-    assert pf["partition_tokens"] == 4096 and pf["grid_workgroups"] == 8 * 128 and pf["waves_per_item"] == 4
+    assert pf["partition_tokens"] == 4096 and pf["grid_workgroups"] == 8 * 128 and pf["waves_per_item"] == 2
     # one sequence: partitions shrink until 4 waves per item would reach 2048 waves
     p1 = B.plan(dims(num_seqs=1), 8)
     assert p1["partition_tokens"] == 512 and p1["grid_workgroups"] == 512 and p1["waves_per_item"] == 2

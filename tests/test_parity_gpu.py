@@ -205,13 +205,15 @@ def test_waves_per_item(name, kw, ptok):
             check(got, ref, w, f"waves {name} P={ptok} waves={nw} {sched}")
 
 
-def test_waves_per_item_edge_lengths():
-    """Waves past the end of a short item contribute an empty state."""
-    w = W.random_edge_workload(41, S=10, H=16, Hkv=2, D=128,
+@pytest.mark.parametrize("kv_dtype", ["bf16", "e5m2", "e4m3"])
+def test_waves_per_item_edge_lengths(kv_dtype):
+    """Waves past the end of a short item contribute an empty state; partial
+    last tiles and blocks past the partition end are masked (fp8 K through LDS too)."""
+    w = W.random_edge_workload(41, S=10, H=16, Hkv=2, D=128, kv_dtype=kv_dtype,
                                seq_lens=[0, 1, 15, 16, 17, 63, 64, 65, 129, 300])
     ref = oracle_full(w)
     dev = upload(w)
-    for nw in (2, 4):
+    for nw in (1, 2, 4):
         for ptok in (64, 128, 256):
             got = run_gpu(w, dev, kernel="mfma", partition_tokens=ptok, waves_per_item=nw)
             check(got, ref, w, f"waves edge P={ptok} waves={nw}")
