@@ -77,14 +77,17 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
     p->kernel = d->kernel;
   }
   p->max_len = d->max_seq_len > 0 ? d->max_seq_len : d->max_blocks_per_seq * d->block_size;
-  // Every wave keeps about one 64-token tile of K and V in flight (the fp8
-  // kernel keeps its next tile in flight while computing). Covering HBM
-  // latency at full bandwidth takes about 2048 waves. Partitions are made as long as
+  // Every wave keeps about one 64-token tile of K and V in flight. Covering
+  // HBM latency at full bandwidth takes about as many waves as the chip holds
+  // at once: 2048 with bf16 / fp32 tiles (32 KiB, two waves per SIMD) and 3072
+  // with fp8 tiles (16 KiB; the fp8 kernel stages K in LDS and runs three
+  // waves per SIMD). Partitions are made as long as
   // possible (up to 4096 tokens: start-up and merge traffic are amortised) and
   // the waves come from splitting each item over 1, 2 or 4 waves; partitions
   // are shortened only when even 4 waves per item would not reach the target.
   const long long units = (long long)d->num_seqs * hkv;
-  const long long target_waves = 2048;
+  const bool fp8 = d->kv_dtype == PA_DTYPE_FP8_E5M2 || d->kv_dtype == PA_DTYPE_FP8_E4M3;
+  const long long target_waves = fp8 ? 3072 : 2048;
   auto items_for = [&](long long P) { return units * ((p->max_len + P - 1) / P); };
   int P = d->partition_tokens;
   if (P == 0) {
@@ -115,8 +118,8 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
     p->schedule = PA_SCHEDULE_GRID;
   }
   // Waves per item (matrix-core kernel): the list schedule splits its long
-  // items four ways so the tail is short; the grid splits items until the
-  // wave target is met, keeping at least 4 tiles per wave.
+  // items four ways so the tail is short; the grid splits items while the
+  // grid still fits the wave target, keeping at least 4 tiles per wave.
   const int ncg = (p->group * p->q_len + 15) / 16 <= 1 ? 1 : (p->group * p->q_len <= 32 ? 2 : 4);
   if (p->kernel != PA_KERNEL_MFMA) {
     if (d->waves_per_item > 1) return PA_ERR_UNSUPPORTED;
@@ -129,7 +132,7 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
   } else {
     const long long tiles = (std::min<long long>(P, p->max_len) + pa::kTileTokens - 1) / pa::kTileTokens;
     int nw = 1;
-    while (nw < 4 && p->grid * nw < target_waves && tiles >= 4LL * 2 * nw && pa::mfma_waves_supported(ncg, 2 * nw)) nw *= 2;
+    while (nw < 4 && p->grid * 2 * nw <= target_waves && tiles >= 4LL * 2 * nw && pa::mfma_waves_supported(ncg, 2 * nw)) nw *= 2;
     p->waves_per_item = nw;
   }
   size_t off = 0;

@@ -48,6 +48,7 @@
 #include "pa_internal.h"
 
 
+
 namespace pa {
 namespace {
 
@@ -297,6 +298,12 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   constexpr int kStride = NW * kTile;
   if (first < tok1) tile_ids(first / BS, idk, idv0, idv1);
 
+  // K slots in LDS (one per wave) for the kernels that stage K tiles there
+  // (fp8, one column group; see the tile loop).
+  constexpr bool kLdsK = NCG == 1 && M::kElem == 1;
+  constexpr int kTileBlk = kD * kBlockSize * M::kElem;   // one block tile of one KV head
+  constexpr int kSlotBlk = kTileBlk + 64;
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kLdsK ? NW : 1][kLdsK ? 4 * kSlotBlk : 16];
   // One tile's K and V registers.
   struct Tile {
     kload_t kr[kKSteps][8];
@@ -449,7 +456,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     }
   };
 
-  if constexpr (M::kElem == 1 && NCG == 1) {
+  if constexpr (kLdsK) {
     // fp8, one column group. A K tile is 4 block tiles of 128 rows x 16 one-byte
     // tokens; it lands in this wave's LDS slot through direct global-to-LDS
     // loads of whole 16-byte rows (each instruction reads 1 KiB contiguous),
@@ -465,10 +472,8 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     // for the whole wave; they are fetched two tiles ahead.
     typedef __attribute__((address_space(3))) void* lds_ptr_t;
     typedef __attribute__((address_space(1))) void* gbl_ptr_t;
-    constexpr int kSlotBlk = kD * kBlockSize + 64;
-    __shared__ __attribute__((aligned(16))) uint8_t k_lds[NW][4 * kSlotBlk];
     uint8_t* kslot = &k_lds[wave][0];
-    const uint8_t* krow = kslot + kblk * kSlotBlk + c * kBlockSize + ktok;   // + 16 * (32 ks + 4 i)
+    const uint8_t* krow = kslot + kblk * kSlotBlk + (c * kBlockSize + ktok) * M::kElem;   // + row bytes * (32 ks + 4 i)
     const int last_blk = nblk_part - 1;
     auto ids_at = [&](int t, int32_t (&ib)[4]) __attribute__((always_inline)) {
       const int b0 = min(t / BS, last_blk);
@@ -480,9 +485,9 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
       for (int blk = 0; blk < 4; ++blk) {
         const char* src = kbase + ib[blk] * blk_bytes + lane * 16;
 #pragma unroll
-        for (int half = 0; half < 2; ++half)
-          __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src + half * 1024),
-                                           (lds_ptr_t)(kslot + blk * kSlotBlk + half * 1024), 16, 0, 2);
+        for (int part = 0; part < kTileBlk / 1024; ++part)
+          __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src + part * 1024),
+                                           (lds_ptr_t)(kslot + blk * kSlotBlk + part * 1024), 16, 0, 2);
       }
     };
     auto load_v_ids = [&](Tile& T, const int32_t (&ib)[4]) __attribute__((always_inline)) {
@@ -502,7 +507,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
         for (int ks = 0; ks < kKSteps; ++ks) {
 #pragma unroll
           for (int i = 0; i < 8; ++i)
-            T.kr[ks][i] = *reinterpret_cast<const kload_t*>(krow + (32 * ks + 4 * i) * kBlockSize);
+            T.kr[ks][i] = *reinterpret_cast<const kload_t*>(krow + (32 * ks + 4 * i) * kBlockSize * M::kElem);
         }
         tile_step(T, t0, [&]() __attribute__((always_inline)) {
           __builtin_amdgcn_sched_barrier(0);
@@ -545,7 +550,17 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     // states, inside the workgroup), then writes the item's result.
     __shared__ float sm_m[NW - 1][NCG][16];
     __shared__ float sm_l[NW - 1][NCG][16];
-    __shared__ f32x4 sm_o[NW - 1][NCG][8][64];
+    typedef f32x4 xo_t[NCG][8][64];
+    auto xo = [&](int w) __attribute__((always_inline)) -> xo_t& {
+      if constexpr (kLdsK) {
+        // wave w + 1 publishes its o in its own K slot, which its loop no longer uses
+        static_assert(sizeof(xo_t) <= 4 * kSlotBlk, "exchange must fit a K slot");
+        return *reinterpret_cast<xo_t*>(&k_lds[w + 1][0]);
+      } else {
+        __shared__ f32x4 sm_o[NW - 1][NCG][8][64];
+        return sm_o[w];
+      }
+    };
     if (wave > 0) {
 #pragma unroll
       for (int cg = 0; cg < NCG; ++cg) {
@@ -554,7 +569,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
           sm_l[wave - 1][cg][n] = l_tot[cg];
         }
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) sm_o[wave - 1][cg][dt][lane] = oacc[cg][dt];
+        for (int dt = 0; dt < 8; ++dt) xo(wave - 1)[cg][dt][lane] = oacc[cg][dt];
       }
     }
     __syncthreads();
@@ -574,7 +589,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
         const float f = __builtin_amdgcn_exp2f(sm_m[w][cg][n] - Mu);
         l += sm_l[w][cg][n] * f;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) oacc[cg][dt] += sm_o[w][cg][dt][lane] * f;
+        for (int dt = 0; dt < 8; ++dt) oacc[cg][dt] += xo(w)[cg][dt][lane] * f;
       }
       m_run[cg] = M;
       l_tot[cg] = l;

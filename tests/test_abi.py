@@ -109,7 +109,7 @@ def test_plan_long_context():
     items = 16 * 8 * 8 * 8
     assert p["workspace_bytes"] >= items * (128 + 2) * 4
     assert p["waves_per_item"] == 2                                      # 1024 items x 2 = 2048 waves
-    # the fp8 batch takes the same wave target: 1024 items x 2 waves
+    # fp8 runs 3 waves per SIMD (3072 resident): 1024 items x 2 waves; 4 would not fit at once
     pf = B.plan(dims(num_seqs=128, max_blocks_per_seq=256, kv_dtype=B.PA_DTYPE_FP8_E5M2), 8)
     assert pf["partition_tokens"] == 4096 and pf["grid_workgroups"] == 8 * 128 and pf["waves_per_item"] == 2
     # one sequence: partitions shrink until 4 waves per item would reach 2048 waves
