@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--config", default="c3", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--kv-dtype", default="", choices=["", "bf16", "e5m2", "e4m3"],
                     help="cache type in place of the batch's own (bf16-query batches c2..c5)")
+    ap.add_argument("--q-len", type=int, default=1,
+                    help="query positions per sequence (speculative verification, chunked prefill); K/V read once")
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--schedule", default="auto", choices=["auto", "grid", "queue"])
@@ -116,7 +118,7 @@ def load_traffic(kernel_name, workload, plan):
     return e.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(w, budget_s):
+def cpu_baseline(w, budget_s, q_len=1):
     from oracle import pa_oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -129,8 +131,13 @@ def cpu_baseline(w, budget_s):
     while t_total < budget_s:
         s = n_done % w.num_seqs
         t0 = time.perf_counter()
-        O.paged_decode(w.q, w.k_cache, w.v_cache, w.block_tables, w.seq_lens, w.num_kv_heads, w.scale,
-                       w.q_dtype, w.kv_dtype, k_scale=float(w.k_scale), v_scale=float(w.v_scale), seqs=[s])
+        if q_len > 1:
+            O.paged_attention_multi(w.q[s:s + 1], w.k_cache, w.v_cache, w.block_tables[s:s + 1], w.seq_lens[s:s + 1],
+                                    w.num_kv_heads, w.scale, w.q_dtype, w.kv_dtype, k_scale=float(w.k_scale),
+                                    v_scale=float(w.v_scale))
+        else:
+            O.paged_decode(w.q, w.k_cache, w.v_cache, w.block_tables, w.seq_lens, w.num_kv_heads, w.scale,
+                           w.q_dtype, w.kv_dtype, k_scale=float(w.k_scale), v_scale=float(w.v_scale), seqs=[s])
         t_total += time.perf_counter() - t0
         n_done += 1
         bytes_done += A.algorithmic_kv_bytes(w.seq_lens[[s]], w.num_kv_heads, w.head_dim, w.kv_dtype)
@@ -138,8 +145,8 @@ def cpu_baseline(w, budget_s):
     return {"value": round(bytes_done / t_total / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{n_done} sequence passes over the {w.num_seqs}-sequence batch ({n_done / w.num_seqs:.2f}x), "
-                      f"all {w.num_heads} heads, {tokens} tokens; fp64 NumPy, {t_total:.2f} s",
-            "seq_head_per_s": round(n_done * w.num_heads / t_total, 3),
+                      f"all {w.num_heads} heads, {q_len} query row(s) each, {tokens} tokens; fp64 NumPy, {t_total:.2f} s",
+            "seq_head_per_s": round(n_done * w.num_heads * q_len / t_total, 3),
             "cpu_model": _cpu_model()}
 
 
@@ -183,7 +190,14 @@ def main():
         print(f"copy probe: {n} bytes read and written per dispatch", file=sys.stderr, flush=True)
         del src, dst
     w = W.make_workload(args.config, kv_dtype=args.kv_dtype or None)
-    batch = args.config + (f"-{args.kv_dtype}" if args.kv_dtype else "")
+    batch = args.config + (f"-{args.kv_dtype}" if args.kv_dtype else "") + (f"-q{args.q_len}" if args.q_len > 1 else "")
+    q_seed = None
+    if args.q_len > 1:
+        # q_len query rows per sequence (the last q_len tokens of each sequence), seeded apart from the batch
+        q_seed = list(w.seed) + [7, args.q_len]
+        rng = np.random.default_rng(q_seed)
+        w.q = W.to_storage(rng.standard_normal((w.num_seqs, args.q_len, w.num_heads, w.head_dim), dtype=np.float32),
+                           w.q_dtype)
 
     def upload(x, dtype):
         if dtype == "f32":
@@ -266,7 +280,7 @@ def main():
 
     ms_step = total_ms / K
     gbs = kv_bytes / (ms_step * 1e-3) / 1e9
-    seq_heads = w.num_seqs * w.num_heads
+    seq_heads = w.num_seqs * w.num_heads * args.q_len
     part_avg = float(np.mean(part_ms))
     achieved = kv_bytes / (part_avg * 1e-3) / 1e9
     kname = "pa_mfma_partition" if plan["kernel"] == "mfma" else "pa_valu_partition"
@@ -292,7 +306,7 @@ def main():
                    "max_seq_len": w.max_seq_len, "kv_bytes_per_step": kv_bytes, "replicas": R,
                    "kernel": plan["kernel"], "schedule": plan["schedule"], "partition_tokens": plan["partition_tokens"],
                    "partitions_max": plan["max_partitions"], "grid_workgroups": plan["grid_workgroups"],
-                   "waves_per_item": plan["waves_per_item"],
+                   "waves_per_item": plan["waves_per_item"], "q_len": args.q_len, "q_seed": q_seed,
                    "seed": list(w.seed), "parallelism": "single GPU"},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "seq_head_per_s": round(seq_heads / (ms_step * 1e-3), 1),
@@ -304,7 +318,7 @@ def main():
                      "traffic": traffic},
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, args.q_len)
     print(json.dumps(result), flush=True)
 
 

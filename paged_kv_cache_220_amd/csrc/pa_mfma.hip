@@ -59,6 +59,10 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;       // head_dim handled by this kernel
+// s_waitcnt operand (gfx9 encoding: vmcnt[3:0] at bits 3:0 and vmcnt[5:4] at
+// bits 15:14, expcnt at 6:4, lgkmcnt at 11:8) that waits for vmcnt == 0 and
+// leaves the other counters unconstrained.
+constexpr int kWaitVmcnt0 = (0x7 << 4) | (0xF << 8);
 constexpr int kTile = 64;     // tokens per tile
 constexpr int kKSteps = kD / 32;
 
@@ -298,9 +302,12 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   constexpr int kStride = NW * kTile;
   if (first < tok1) tile_ids(first / BS, idk, idv0, idv1);
 
-  // K slots in LDS (one per wave) for the kernels that stage K tiles there
-  // (fp8, one column group; see the tile loop).
-  constexpr bool kLdsK = NCG == 1 && M::kElem == 1;
+  // K slots in LDS (one per wave) for the kernels that stage K tiles there:
+  // fp8 (whole-row copies instead of 4-byte pieces) and two column groups
+  // (one wave per SIMD: the next tile's K copy then overlaps this tile's
+  // compute at no register cost). Four bf16 groups have no registers left
+  // for the staged loop and load K directly.
+  constexpr bool kLdsK = M::kElem == 1 || NCG == 2;
   constexpr int kTileBlk = kD * kBlockSize * M::kElem;   // one block tile of one KV head
   constexpr int kSlotBlk = kTileBlk + 64;
   __shared__ __attribute__((aligned(16))) uint8_t k_lds[kLdsK ? NW : 1][kLdsK ? 4 * kSlotBlk : 16];
@@ -457,13 +464,13 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   };
 
   if constexpr (kLdsK) {
-    // fp8, one column group. A K tile is 4 block tiles of 128 rows x 16 one-byte
-    // tokens; it lands in this wave's LDS slot through direct global-to-LDS
-    // loads of whole 16-byte rows (each instruction reads 1 KiB contiguous),
-    // and QK reads each lane's 4-token pieces back from LDS. (Loading those
+    // Staged K. A K tile is 4 block tiles of 128 rows x 16 tokens; it lands in
+    // this wave's LDS slot through direct global-to-LDS loads of whole rows
+    // (16 bytes per lane, each instruction reading 1 KiB contiguous), and QK
+    // reads each lane's 4-token pieces back from LDS. (For fp8, loading those
     // 4-byte pieces straight from HBM touches half of every 128-byte line per
     // instruction and runs the memory pipeline 25 % slower.) Block slots are
-    // 64 bytes apart beyond their 2 KiB so the four blocks of a read fall in
+    // 64 bytes apart beyond the tile so the four blocks of a read fall in
     // different LDS banks.
     //
     // Pipeline: K of the next tile is issued right after this tile's QK (its
@@ -503,6 +510,12 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
       __builtin_amdgcn_sched_barrier(0);
       for (int t0 = first; t0 < tok1; t0 += kStride) {
         const bool more = t0 + kStride < tok1;
+        // The K copy into LDS is a vector-memory operation: wait for every
+        // outstanding one (vmcnt 0) before reading the slot. The compiler's own
+        // wait insertion does not cover LDS written this way in every
+        // instantiation, so the wait is explicit.
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks < kKSteps; ++ks) {
 #pragma unroll
@@ -552,9 +565,8 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     __shared__ float sm_l[NW - 1][NCG][16];
     typedef f32x4 xo_t[NCG][8][64];
     auto xo = [&](int w) __attribute__((always_inline)) -> xo_t& {
-      if constexpr (kLdsK) {
+      if constexpr (kLdsK && sizeof(xo_t) <= 4 * kSlotBlk) {
         // wave w + 1 publishes its o in its own K slot, which its loop no longer uses
-        static_assert(sizeof(xo_t) <= 4 * kSlotBlk, "exchange must fit a K slot");
         return *reinterpret_cast<xo_t*>(&k_lds[w + 1][0]);
       } else {
         __shared__ f32x4 sm_o[NW - 1][NCG][8][64];
