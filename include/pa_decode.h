@@ -80,13 +80,14 @@ typedef enum pa_schedule {
 typedef enum pa_kernel {
   PA_KERNEL_AUTO = 0,     /* matrix-core kernel where supported, else vector kernel  */
   PA_KERNEL_VALU = 1,     /* vector-ALU kernel (every supported shape)               */
-  PA_KERNEL_MFMA = 2      /* matrix-core kernel: head_dim 128, block 16,
-                             group * q_len <= 64, q bf16 with KV bf16 or fp8          */
+  PA_KERNEL_MFMA = 2      /* matrix-core kernel: head_dim 128, block 16, any group,
+                             q_len <= 4096, q bf16 with KV bf16 or fp8                */
 } pa_kernel_t;
 
 /* Sizes and types of one call. Supported: block_size 16; head_dim 64 or 128;
- * group = num_heads / num_kv_heads in {1, 2, 4, 8, 16}; (q_dtype, kv_dtype) in
- * {(F32, F32), (BF16, BF16), (BF16, FP8_E5M2), (BF16, FP8_E4M3)}.
+ * group = num_heads / num_kv_heads in {1, 2, 4, 8, 16} (any group for the
+ * matrix-core kernel); (q_dtype, kv_dtype) in {(F32, F32), (BF16, BF16),
+ * (BF16, FP8_E5M2), (BF16, FP8_E4M3)}.
  * Non-finite K/V values in attended slots give non-finite outputs (the
  * matrix-core kernel may return NaN where exact arithmetic gives +-inf). */
 typedef struct pa_dims {
@@ -111,8 +112,11 @@ typedef struct pa_dims {
                                   query i attends tokens t < seq_lens[s] - q_len + 1 + i
                                   (the causal mask of the inference page's attention
                                   with several query rows; a query with no token gets
-                                  a zero row). Matrix-core kernel only:
-                                  group * q_len <= 64.                                  */
+                                  a zero row). Matrix-core kernel only, q_len <= 4096:
+                                  a KV head's group * q_len (position, head) pairs
+                                  are taken in blocks of up to 64 per work item, each
+                                  block reading the KV head's tiles (chunked prefill
+                                  reads them once per block).                          */
   int32_t schedule;            /* pa_schedule_t                                        */
   int32_t waves_per_item;      /* matrix-core kernel: waves that share one (sequence,
                                   KV head, partition) item and merge their states in

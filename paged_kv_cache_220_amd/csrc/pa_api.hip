@@ -25,6 +25,7 @@ struct Plan {
   int kernel = PA_KERNEL_VALU;
   int group = 1;
   int q_len = 1;
+  int q_blocks = 1;   // blocks of up to 64 (query position, head) pairs per KV head
   int max_len = 0;
   int partition_tokens = 0;
   int max_parts = 1;
@@ -52,9 +53,10 @@ int check_dims(const pa_dims_t* d, int32_t hkv) {
   if (d->waves_per_item != 0 && d->waves_per_item != 1 && d->waves_per_item != 2 && d->waves_per_item != 4)
     return PA_ERR_UNSUPPORTED;
   if (d->block_size != pa::kBlockSize) return PA_ERR_UNSUPPORTED;
-  if ((long long)d->num_seqs * hkv > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;  // grid x limit
   const int group = d->num_heads / hkv;
   const int ql = q_len_of(d);
+  const long long qblocks = ((long long)group * ql + 63) / 64;
+  if ((long long)d->num_seqs * hkv * qblocks > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;  // grid x limit
   if ((long long)d->num_heads * ql > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;   // merge grid x
   const bool valu_ok = ql == 1 && pa::valu_supported(d->q_dtype, d->kv_dtype, d->head_dim, group);
   const bool mfma_ok = pa::mfma_supported(d->q_dtype, d->kv_dtype, d->head_dim, group, d->block_size, ql);
@@ -69,6 +71,7 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
   if (st != PA_OK) return st;
   p->group = d->num_heads / hkv;
   p->q_len = q_len_of(d);
+  p->q_blocks = (p->group * p->q_len + 16 * pa::kMaxColumnGroups - 1) / (16 * pa::kMaxColumnGroups);
   if (d->kernel == PA_KERNEL_AUTO) {
     p->kernel = pa::mfma_supported(d->q_dtype, d->kv_dtype, d->head_dim, p->group, d->block_size, p->q_len)
                     ? PA_KERNEL_MFMA
@@ -85,7 +88,7 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
   // possible (up to 4096 tokens: start-up and merge traffic are amortised) and
   // the waves come from splitting each item over 1, 2 or 4 waves; partitions
   // are shortened only when even 4 waves per item would not reach the target.
-  const long long units = (long long)d->num_seqs * hkv;
+  const long long units = (long long)d->num_seqs * hkv * (p->kernel == PA_KERNEL_MFMA ? p->q_blocks : 1);
   const bool fp8 = d->kv_dtype == PA_DTYPE_FP8_E5M2 || d->kv_dtype == PA_DTYPE_FP8_E4M3;
   const long long target_waves = fp8 ? 3072 : 2048;
   auto items_for = [&](long long P) { return units * ((p->max_len + P - 1) / P); };
@@ -103,7 +106,8 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
   p->max_parts = p->max_len > 0 ? (int)((p->max_len + (long long)P - 1) / P) : 1;
   if (p->max_parts < 1) p->max_parts = 1;
   if (p->max_parts > kMaxParts) return PA_ERR_UNSUPPORTED;
-  p->grid = (long long)p->max_parts * hkv * d->num_seqs;
+  if (p->kernel != PA_KERNEL_MFMA) p->q_blocks = 1;   // the vector kernel takes one query position
+  p->grid = (long long)p->max_parts * hkv * p->q_blocks * d->num_seqs;
   p->reduce_grid = p->max_parts > 1 ? (long long)d->num_heads * p->q_len * d->num_seqs : 0;
   // List schedule: for the matrix-core kernel when asked, or when the dense
   // grid is far larger than the resident workgroups (a skewed or sparse
@@ -120,7 +124,8 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
   // Waves per item (matrix-core kernel): the list schedule splits its long
   // items four ways so the tail is short; the grid splits items while the
   // grid still fits the wave target, keeping at least 4 tiles per wave.
-  const int ncg = (p->group * p->q_len + 15) / 16 <= 1 ? 1 : (p->group * p->q_len <= 32 ? 2 : 4);
+  const int gv = p->group * p->q_len;   // (query position, head) pairs per KV head
+  const int ncg = gv <= 16 ? 1 : gv <= 32 ? 2 : 4;
   if (p->kernel != PA_KERNEL_MFMA) {
     if (d->waves_per_item > 1) return PA_ERR_UNSUPPORTED;
     p->waves_per_item = 1;
@@ -195,6 +200,7 @@ int run(const void* q, const void* k_cache, const void* v_cache, const int32_t* 
   a.score_scale = scale * dims->k_scale * 1.4426950408889634f;
   a.v_scale = dims->v_scale;
   a.q_len = p.q_len;
+  a.q_blocks = p.q_blocks;
   a.queue_items = nullptr;
   a.queue_len = nullptr;
   a.queue_workgroups = 0;

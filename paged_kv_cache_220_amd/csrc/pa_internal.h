@@ -39,6 +39,7 @@ struct Args {
   const int* queue_len;
   int32_t queue_workgroups;
   int32_t waves_per_item;   // matrix-core kernel: waves sharing one work item (1, 2, 4)
+  int32_t q_blocks;         // blocks of up to 64 (query position, head) pairs per KV head
 };
 
 // Host-side launchers; each returns the hipError_t of the launch.
@@ -55,7 +56,8 @@ bool mfma_waves_supported(int ncg, int nw);
 
 constexpr int kBlockSize = 16;     // tokens per physical block handled by the kernels
 constexpr int kTileTokens = 64;    // partition lengths are multiples of this
-constexpr int kMaxColumnGroups = 4; // matrix-core kernel: group * q_len <= 64
+constexpr int kMaxColumnGroups = 4; // matrix-core kernel: up to 64 (query position, head) pairs per work item
+constexpr int kMaxQueryLen = 4096;  // query positions per sequence
 constexpr int kMaxQueueBuckets = 129;  // queue schedule: partitions of at most 128 tiles
 constexpr int kResidentWorkgroups = 2048;  // gfx950: 256 CUs x 8 one-wave workgroups (planning)
 
@@ -75,17 +77,24 @@ __device__ __forceinline__ int clamp_len(const Args& a, int s) {
 // the deep partitions that only long sequences have start early, and the
 // first partitions, which include every short sequence, fill the tail.
 struct Item {
-  int kvh, s, part;
+  int kvh, qb, s, part;
 };
+// blockIdx.x = kvh + Hkv * (qb + q_blocks * s): the query blocks of one
+// (sequence, KV head) are Hkv workgroups apart, so with Hkv a multiple of the
+// 8 XCDs they share an XCD (and its L2 for the K/V tiles they all read) and
+// are dispatched close together.
 __device__ __forceinline__ Item work_item(const Args& a) {
   Item it;
-  it.s = blockIdx.x / a.num_kv_heads;
-  it.kvh = blockIdx.x - it.s * a.num_kv_heads;
+  const int per_seq = a.num_kv_heads * a.q_blocks;
+  it.s = blockIdx.x / per_seq;
+  const int r = blockIdx.x - it.s * per_seq;
+  it.qb = r / a.num_kv_heads;
+  it.kvh = r - it.qb * a.num_kv_heads;
   it.part = a.max_parts - 1 - (int)blockIdx.y;
   return it;
 }
 __host__ __forceinline__ dim3 partition_grid(const Args& a) {
-  return dim3((unsigned)a.num_kv_heads * (unsigned)a.num_seqs, (unsigned)a.max_parts, 1);
+  return dim3((unsigned)a.num_kv_heads * (unsigned)a.q_blocks * (unsigned)a.num_seqs, (unsigned)a.max_parts, 1);
 }
 
 // Physical block id, clamped into the pool for the same reason.

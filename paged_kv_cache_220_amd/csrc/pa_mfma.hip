@@ -215,8 +215,12 @@ template <> struct Mfma<kE4M3> {
   }
 };
 
-template <int KDT, int NCG, int NW>
-__device__ __forceinline__ void partition_item(const Args& a, int group, int s, int kvh, int part) {
+// STREAM: K/V loads bypass the caches (each tile is read once per call). Work
+// items that are one of several query blocks of a KV head (four column
+// groups) load through the caches instead, so the sibling blocks that read
+// the same tiles at about the same time on the same XCD can hit in them.
+template <int KDT, int NCG, int NW, bool STREAM>
+__device__ __forceinline__ void partition_item(const Args& a, int group, int s, int kvh, int part, int qb) {
   using M = Mfma<KDT>;
   using op_t = typename M::op_t;
   using kload_t = typename M::kload_t;
@@ -227,6 +231,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   const int L = clamp_len(a, s);
   const int QL = a.q_len;
   const int GV = group * QL;                               // virtual heads of this KV head
+  const int v0 = 16 * kMaxColumnGroups * qb;               // first virtual head of this query block
   const int P = a.partition_tokens;
   const int nparts = L > 0 ? (L + P - 1) / P : 1;
   if (part >= nparts) return;
@@ -245,7 +250,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   int lim[NCG];                // tokens the column's query may attend: t < lim
 #pragma unroll
   for (int cg = 0; cg < NCG; ++cg) {
-    const int v = 16 * cg + n;
+    const int v = v0 + 16 * cg + n;
     const bool col_ok = v < GV;
     const int qi = col_ok ? v / group : 0;
     const int h = col_ok ? v - qi * group : 0;
@@ -316,6 +321,10 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     kload_t kr[kKSteps][8];
     vload_t vr[8][2];
   };
+  auto ld = [&](auto* ptr) __attribute__((always_inline)) {
+    if constexpr (STREAM) return __builtin_nontemporal_load(ptr);
+    else return *ptr;
+  };
   // K loads: 4 k-steps x 8 rows, 4 tokens each; V loads: 8 row tiles x 2
   // token halves, 8 tokens each. K/V bytes are used once per call, so they are
   // loaded non-temporally (streamed past the caches).
@@ -326,7 +335,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int d = 32 * ks + 4 * i + c;
-        T.kr[ks][i] = __builtin_nontemporal_load(reinterpret_cast<const kload_t*>(kbase + kb_off + d * kRowBytes + ktok * M::kElem));
+        T.kr[ks][i] = ld(reinterpret_cast<const kload_t*>(kbase + kb_off + d * kRowBytes + ktok * M::kElem));
       }
     }
   };
@@ -337,7 +346,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const int d = 16 * dt + n;
-        T.vr[dt][hh] = __builtin_nontemporal_load(reinterpret_cast<const vload_t*>(vbase + vb_offs[hh] + d * kRowBytes + 8 * (c & 1) * M::kElem));
+        T.vr[dt][hh] = ld(reinterpret_cast<const vload_t*>(vbase + vb_offs[hh] + d * kRowBytes + 8 * (c & 1) * M::kElem));
       }
     }
   };
@@ -494,7 +503,8 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
 #pragma unroll
         for (int part = 0; part < kTileBlk / 1024; ++part)
           __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src + part * 1024),
-                                           (lds_ptr_t)(kslot + blk * kSlotBlk + part * 1024), 16, 0, 2);
+                                           (lds_ptr_t)(kslot + blk * kSlotBlk + part * 1024), 16, 0,
+                                           STREAM ? 2 : 0);   // 2: non-temporal
       }
     };
     auto load_v_ids = [&](Tile& T, const int32_t (&ib)[4]) __attribute__((always_inline)) {
@@ -610,7 +620,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   const int64_t slot = ((int64_t)s * a.num_kv_heads + kvh) * a.max_parts + part;
 #pragma unroll
   for (int cg = 0; cg < NCG; ++cg) {
-    const int v = 16 * cg + n;
+    const int v = v0 + 16 * cg + n;
     if (v >= GV) continue;
     if (nparts == 1) {
       const int qi = v / group;
@@ -643,23 +653,24 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NCG == 1 ? 2 : 1, 8)))
 
 // Grid schedule: one workgroup per (KV head, sequence, partition) of the dense grid.
-template <int KDT, int NCG, int NW>
+template <int KDT, int NCG, int NW, bool STREAM>
 PA_MFMA_KERNEL_ATTRS void mfma_partition_kernel(const Args a, int group) {
   const Item it = work_item(a);
-  partition_item<KDT, NCG, NW>(a, group, it.s, it.kvh, it.part);
+  partition_item<KDT, NCG, NW, STREAM>(a, group, it.s, it.kvh, it.part, it.qb);
 }
 
 // List schedule: workgroup i takes item i of the list the plan kernel built,
 // longest first, and workgroups past its end exit at once. Workgroups are
 // dispatched in index order, so long items start first and short ones fill
 // the end; consecutive (similar) items go to consecutive XCDs.
-template <int KDT, int NCG, int NW>
+template <int KDT, int NCG, int NW, bool STREAM>
 PA_MFMA_KERNEL_ATTRS void mfma_partition_list_kernel(const Args a, int group) {
   const int idx = blockIdx.x;
   if (idx >= *a.queue_len) return;
-  const int2 w = a.queue_items[idx];
-  const int s = w.x / a.num_kv_heads;
-  partition_item<KDT, NCG, NW>(a, group, s, w.x - s * a.num_kv_heads, w.y);
+  const int2 w = a.queue_items[idx];            // unit (s * q_blocks + qb) * Hkv + kvh, partition
+  const int sq = w.x / a.num_kv_heads;
+  const int s = sq / a.q_blocks;
+  partition_item<KDT, NCG, NW, STREAM>(a, group, s, w.x - sq * a.num_kv_heads, w.y, sq - s * a.q_blocks);
 }
 
 }  // namespace
@@ -672,38 +683,42 @@ bool mfma_waves_supported(int ncg, int nw) {
 
 bool mfma_supported(int q_dtype, int kv_dtype, int head_dim, int group, int block_size, int q_len) {
   return q_dtype == kBF16 && (kv_dtype == kBF16 || kv_dtype == kE5M2 || kv_dtype == kE4M3) && head_dim == kD &&
-         block_size == kBlockSize && group >= 1 && q_len >= 1 && group * q_len <= 16 * kMaxColumnGroups;
+         block_size == kBlockSize && group >= 1 && q_len >= 1 && q_len <= kMaxQueryLen;
 }
 
 hipError_t launch_mfma(const Args& a, int q_dtype, int kv_dtype, int head_dim, int group,
                        hipStream_t stream) {
   if (!mfma_supported(q_dtype, kv_dtype, head_dim, group, kBlockSize, a.q_len)) return hipErrorInvalidValue;
-  const int gv = group * a.q_len;
+  const int gv = group * a.q_len;                 // virtual heads per KV head, in blocks of up to 64
   const int ncg = gv <= 16 ? 1 : gv <= 32 ? 2 : 4;
+  if (a.q_blocks != (gv + 16 * kMaxColumnGroups - 1) / (16 * kMaxColumnGroups)) return hipErrorInvalidValue;
   const bool queue = a.queue_items != nullptr;
   const dim3 grid = queue ? dim3((unsigned)a.queue_workgroups) : partition_grid(a);   // list: one per possible item
   const int nw = a.waves_per_item;
   if (!mfma_waves_supported(ncg, nw)) return hipErrorInvalidValue;
-#define PA_LAUNCH3(KDT, NCG, NW)                                                                  \
-  do {                                                                                            \
-    if (queue) mfma_partition_list_kernel<KDT, NCG, NW><<<grid, 64 * NW, 0, stream>>>(a, group);   \
-    else mfma_partition_kernel<KDT, NCG, NW><<<grid, 64 * NW, 0, stream>>>(a, group);              \
+  const bool stream_kv = a.q_blocks == 1;         // several query blocks: share tiles through the caches
+#define PA_LAUNCH4(KDT, NCG, NW, ST)                                                                   \
+  do {                                                                                                 \
+    if (queue) mfma_partition_list_kernel<KDT, NCG, NW, ST><<<grid, 64 * NW, 0, stream>>>(a, group);   \
+    else mfma_partition_kernel<KDT, NCG, NW, ST><<<grid, 64 * NW, 0, stream>>>(a, group);              \
   } while (0)
-#define PA_LAUNCH(KDT)                                  \
-  do {                                                  \
-    if (ncg == 1 && nw == 1) PA_LAUNCH3(KDT, 1, 1);     \
-    else if (ncg == 1 && nw == 2) PA_LAUNCH3(KDT, 1, 2); \
-    else if (ncg == 1) PA_LAUNCH3(KDT, 1, 4);           \
-    else if (ncg == 2 && nw == 1) PA_LAUNCH3(KDT, 2, 1); \
-    else if (ncg == 2) PA_LAUNCH3(KDT, 2, 2);           \
-    else if (nw == 1) PA_LAUNCH3(KDT, 4, 1);            \
-    else PA_LAUNCH3(KDT, 4, 2);                         \
+#define PA_LAUNCH(KDT)                                                            \
+  do {                                                                            \
+    if (ncg == 1 && nw == 1) PA_LAUNCH4(KDT, 1, 1, true);                         \
+    else if (ncg == 1 && nw == 2) PA_LAUNCH4(KDT, 1, 2, true);                    \
+    else if (ncg == 1) PA_LAUNCH4(KDT, 1, 4, true);                               \
+    else if (ncg == 2 && nw == 1) PA_LAUNCH4(KDT, 2, 1, true);                    \
+    else if (ncg == 2) PA_LAUNCH4(KDT, 2, 2, true);                               \
+    else if (nw == 1 && stream_kv) PA_LAUNCH4(KDT, 4, 1, true);                   \
+    else if (nw == 1) PA_LAUNCH4(KDT, 4, 1, false);                               \
+    else if (stream_kv) PA_LAUNCH4(KDT, 4, 2, true);                              \
+    else PA_LAUNCH4(KDT, 4, 2, false);                                            \
   } while (0)
   if (kv_dtype == kBF16) PA_LAUNCH(kBF16);
   else if (kv_dtype == kE5M2) PA_LAUNCH(kE5M2);
   else PA_LAUNCH(kE4M3);
 #undef PA_LAUNCH
-#undef PA_LAUNCH3
+#undef PA_LAUNCH4
   return hipGetLastError();
 }
 

@@ -25,6 +25,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const Args a) {
   const int P = a.partition_tokens;
   const int full = P / kTileTokens;             // bucket of a full partition
   const int hkv = a.num_kv_heads;
+  const int qbs = a.q_blocks;
+  const int units_per_seq = hkv * qbs;   // unit = (s * q_blocks + qb) * Hkv + kvh
   int2* items = const_cast<int2*>(a.queue_items);
   for (int b = tid; b <= full; b += kPlanThreads) cnt[b] = 0;
   __syncthreads();
@@ -32,8 +34,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const Args a) {
     const int L = clamp_len(a, s);
     const int nfull = L / P;
     const int rem = L - nfull * P;
-    if (nfull > 0) atomicAdd(&cnt[full], nfull * hkv);
-    if (rem > 0 || L == 0) atomicAdd(&cnt[(rem + kTileTokens - 1) / kTileTokens], hkv);
+    if (nfull > 0) atomicAdd(&cnt[full], nfull * units_per_seq);
+    if (rem > 0 || L == 0) atomicAdd(&cnt[(rem + kTileTokens - 1) / kTileTokens], units_per_seq);
   }
   __syncthreads();
   if (tid == 0) {
@@ -52,13 +54,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const Args a) {
     const int nfull = L / P;
     const int rem = L - nfull * P;
     if (nfull > 0) {
-      int2* run = items + atomicAdd(&cur[full], nfull * hkv);
-      for (int g = 0; g < hkv; ++g)
-        for (int p = 0; p < nfull; ++p) run[g * nfull + p] = make_int2(s * hkv + g, p);
+      int2* run = items + atomicAdd(&cur[full], nfull * units_per_seq);
+      for (int u = 0; u < units_per_seq; ++u)
+        for (int p = 0; p < nfull; ++p) run[u * nfull + p] = make_int2(s * units_per_seq + u, p);
     }
     if (rem > 0 || L == 0) {
-      int2* run = items + atomicAdd(&cur[(rem + kTileTokens - 1) / kTileTokens], hkv);
-      for (int g = 0; g < hkv; ++g) run[g] = make_int2(s * hkv + g, nfull);
+      int2* run = items + atomicAdd(&cur[(rem + kTileTokens - 1) / kTileTokens], units_per_seq);
+      for (int u = 0; u < units_per_seq; ++u) run[u] = make_int2(s * units_per_seq + u, nfull);
     }
   }
 }

@@ -79,7 +79,9 @@ def status_of(d, hkv=8):
     (dict(num_seqs=300_000_000), 8, B.PA_ERR_UNSUPPORTED),       # grid x limit
     (dict(q_len=-1), 8, B.PA_ERR_SHAPE),
     (dict(q_len=8), 8, B.PA_OK),                                 # 8 heads x 8 positions: 4 column groups
-    (dict(q_len=9), 8, B.PA_ERR_UNSUPPORTED),                    # 72 virtual heads
+    (dict(q_len=9), 8, B.PA_OK),                                 # 72 virtual heads: two query blocks
+    (dict(q_len=4096, max_seq_len=4096), 8, B.PA_OK),
+    (dict(q_len=4097, max_seq_len=8192), 8, B.PA_ERR_UNSUPPORTED),
     (dict(q_len=2, kernel=1), 8, B.PA_ERR_UNSUPPORTED),          # vector kernel: one query only
     (dict(q_len=2, head_dim=64), 8, B.PA_ERR_UNSUPPORTED),
     (dict(schedule=7), 8, B.PA_ERR_UNSUPPORTED),
@@ -127,6 +129,12 @@ def test_plan_schedule_choice():
     # 16 x 8 units x 8 partitions = 1024 workgroups: dense grid
     assert B.plan(dims(), 8)["schedule"] == "grid"
     # 256 x 8 units x 8 partitions = 16384 >> 2048 resident workgroups: work queue
+    # query blocks: 8 heads x 16 positions = 128 pairs per KV head -> 2 blocks of 64
+    pq = B.plan(dims(num_seqs=4, max_seq_len=4096, q_len=16), 8)
+    assert pq["grid_workgroups"] == 4 * 8 * 2 * pq["max_partitions"]
+    # 64 heads, one KV head, 3 positions: 192 pairs -> 3 blocks
+    pm = B.plan(dims(num_seqs=2, max_seq_len=2048, q_len=3), 1)
+    assert pm["grid_workgroups"] == 2 * 1 * 3 * pm["max_partitions"]
     p = B.plan(dims(num_seqs=256, max_seq_len=32657), 8)
     assert p["schedule"] == "queue" and p["partition_tokens"] == 4096 and p["waves_per_item"] == 4
     g = B.plan(dims(num_seqs=256, max_seq_len=32657, schedule=1), 8)

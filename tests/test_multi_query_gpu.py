@@ -84,3 +84,72 @@ def test_query_window_longer_than_sequence():
         got = out.float().cpu().numpy().astype(np.float64)
         assert np.all(got[0, :3] == 0) and np.all(got[1, :1] == 0) and np.all(got[3] == 0)
         check(got, ref, w, f"short window P={ptok}")
+
+
+def _multi_ref(w, q):
+    """Oracle per sequence (keeps the fp64 work proportional to the case)."""
+    return np.concatenate([O.paged_attention_multi(q[s:s + 1], w.k_cache, w.v_cache, w.block_tables[s:s + 1],
+                                                   w.seq_lens[s:s + 1], w.num_kv_heads, w.scale, w.q_dtype,
+                                                   w.kv_dtype) for s in range(w.num_seqs)])
+
+
+QBLOCKS = [
+    ("c2", dict(num_seqs=4), 16),                       # 128 (position, head) pairs: two full blocks of 64
+    ("c3", dict(num_seqs=2, seq_len=2000), 33),         # 264 pairs: five blocks, the last with 8
+    ("c5", dict(num_seqs=2, seq_len=1500), 24),         # fp8 cache, three blocks
+]
+
+
+@pytest.mark.parametrize("name,kw,ql", QBLOCKS, ids=[f"{c[0]}-q{c[2]}" for c in QBLOCKS])
+def test_query_blocks(name, kw, ql):
+    """More (position, head) pairs than one work item holds: items cover blocks
+    of 64, each reading the KV head's tiles; grid and list schedules, 1 and 2
+    waves per item, single and split partitions."""
+    w = W.make_workload(name, **kw)
+    rng = np.random.default_rng([ql, 91])
+    q = W.to_storage(rng.standard_normal((w.num_seqs, ql, w.num_heads, w.head_dim), dtype=np.float32), "bf16")
+    ref = _multi_ref(w, q)
+    qd = _dev(q, "bf16")
+    kd, vd = _dev(w.k_cache, w.kv_dtype), _dev(w.v_cache, w.kv_dtype)
+    td, ld = torch.from_numpy(w.block_tables).cuda(), torch.from_numpy(w.seq_lens).cuda()
+    for ptok, sched, nw in ((0, "auto", 0), (256, "grid", 1), (256, "queue", 2), (4096, "grid", 2)):
+        out = torch.full_like(qd, float("nan"))
+        log(f"case query blocks {name}{kw} q_len={ql} P={ptok} {sched} waves={nw}")
+        B.pa_decode(qd, kd, vd, td, ld, w.num_kv_heads, float(w.scale), out, partition_tokens=ptok,
+                    max_seq_len=w.max_seq_len, kernel="mfma", schedule=sched, waves_per_item=nw)
+        torch.cuda.synchronize()
+        check(out.float().cpu().numpy().astype(np.float64), ref, w, f"query blocks {name} q_len={ql} P={ptok} {sched}")
+
+
+def test_query_blocks_one_kv_head():
+    """64 query heads sharing one KV head (group 64): two positions make two blocks."""
+    w = W.random_edge_workload(61, S=3, H=64, Hkv=1, D=128, seq_lens=[700, 65, 2])
+    ql = 2
+    rng = np.random.default_rng(62)
+    q = W.to_storage(rng.standard_normal((3, ql, 64, 128), dtype=np.float32), "bf16")
+    ref = _multi_ref(w, q)
+    qd = _dev(q, "bf16")
+    for ptok in (0, 128):
+        out = torch.full_like(qd, float("nan"))
+        B.pa_decode(qd, _dev(w.k_cache, "bf16"), _dev(w.v_cache, "bf16"), torch.from_numpy(w.block_tables).cuda(),
+                    torch.from_numpy(w.seq_lens).cuda(), 1, float(w.scale), out, partition_tokens=ptok,
+                    max_seq_len=w.max_seq_len)
+        torch.cuda.synchronize()
+        check(out.float().cpu().numpy().astype(np.float64), ref, w, f"one KV head, group 64, P={ptok}")
+
+
+def test_prefill_chunk():
+    """A 256-token prefill chunk of one sequence (32 query blocks) over a 1000-token cache."""
+    w = W.random_edge_workload(64, S=1, H=64, Hkv=8, D=128, seq_lens=[1000])
+    ql = 256
+    rng = np.random.default_rng(63)
+    q = W.to_storage(rng.standard_normal((1, ql, w.num_heads, w.head_dim), dtype=np.float32), "bf16")
+    ref = _multi_ref(w, q)
+    qd = _dev(q, "bf16")
+    out = torch.full_like(qd, float("nan"))
+    log(f"case prefill chunk q_len={ql} L={int(w.seq_lens[0])}")
+    B.pa_decode(qd, _dev(w.k_cache, "bf16"), _dev(w.v_cache, "bf16"), torch.from_numpy(w.block_tables).cuda(),
+                torch.from_numpy(w.seq_lens).cuda(), w.num_kv_heads, float(w.scale), out,
+                max_seq_len=int(w.seq_lens[0]))
+    torch.cuda.synchronize()
+    check(out.float().cpu().numpy().astype(np.float64), ref, w, "prefill chunk")
