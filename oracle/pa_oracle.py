@@ -47,7 +47,14 @@ Readings where the pages are silent (each is also listed with the design notes):
     the float32 value the GPU receives, widened to float64;
   * L == 0 gives a zero output row;
   * fp8 values are checked against the stored bytes decoded exactly, times the
-    per-tensor scales k_scale / v_scale.
+    per-tensor scales k_scale / v_scale;
+  * INT4 (the inference page's exercise names INT4 KV quantisation and its
+    roughly fourfold capacity over FP16, nothing more): symmetric 4-bit
+    two's-complement codes -8..7, two tokens per byte along the token axis
+    (the even token in the low nibble), one float32 scale per (physical
+    block, KV head) for K and one for V, so a value is
+    code * k_scale * k_block_scales[block, kv head]. The same per-block scales
+    may also multiply an fp8 cache.
 """
 
 from __future__ import annotations
@@ -62,6 +69,7 @@ __all__ = [
     "online_decode", "merge_partials", "dense_attention",
     "e5m2_encode", "bf16_encode", "encode_bits", "paged_append", "copy_blocks",
     "paged_attention_multi", "e4m3_value", "e4m3_encode",
+    "int4_pack", "int4_unpack", "int4_encode", "block_values",
 ]
 
 
@@ -100,8 +108,28 @@ def e4m3_value(code: int) -> float:
 _E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
 
 
+def int4_unpack(packed: np.ndarray) -> np.ndarray:
+    """Bytes [..., n] -> signed codes [..., 2n] (int8): byte j holds token 2j in
+    its low nibble and token 2j + 1 in its high nibble, two's complement."""
+    b = np.asarray(packed, dtype=np.uint8)
+    lo = (b & 0x0F).astype(np.int8)
+    hi = (b >> 4).astype(np.int8)
+    nib = np.stack([lo, hi], axis=-1).reshape(b.shape[:-1] + (2 * b.shape[-1],))
+    return np.where(nib >= 8, nib - 16, nib).astype(np.int8)
+
+
+def int4_pack(codes: np.ndarray) -> np.ndarray:
+    """Signed codes [..., 2n] in -8..7 -> bytes [..., n] (inverse of int4_unpack)."""
+    c = np.asarray(codes, dtype=np.int16)
+    if c.min(initial=0) < -8 or c.max(initial=0) > 7 or c.shape[-1] % 2:
+        raise ValueError("int4 codes must lie in -8..7, an even number per row")
+    u = (c & 0x0F).astype(np.uint8).reshape(c.shape[:-1] + (c.shape[-1] // 2, 2))
+    return (u[..., 0] | (u[..., 1] << 4)).astype(np.uint8)
+
+
 def decode_bits(bits: np.ndarray, dtype: str) -> np.ndarray:
-    """Storage bits -> float64 values, exactly."""
+    """Storage bits -> float64 values, exactly. For int4 the last axis is
+    packed (two tokens per byte) and comes back unpacked, as the codes."""
     if dtype == "f32":
         return np.asarray(bits, dtype=np.float32).astype(np.float64)
     if dtype == "bf16":
@@ -112,7 +140,25 @@ def decode_bits(bits: np.ndarray, dtype: str) -> np.ndarray:
         return _E5M2_TABLE[np.asarray(bits, dtype=np.uint8)]
     if dtype == "e4m3":
         return _E4M3_TABLE[np.asarray(bits, dtype=np.uint8)]
+    if dtype == "int4":
+        return int4_unpack(bits).astype(np.float64)
     raise ValueError(dtype)
+
+
+def _tokens_per_row(cache_bits: np.ndarray, dtype: str) -> int:
+    return cache_bits.shape[3] * (2 if dtype == "int4" else 1)
+
+
+def block_values(cache_bits: np.ndarray, b: int, g: int, dtype: str, elem_scale: float = 1.0,
+                 block_scales: Optional[np.ndarray] = None) -> np.ndarray:
+    """Values of physical block b, KV head g: float64 [D, block_size], the stored
+    codes times the per-tensor scale and, if given, the block's own scale."""
+    out = decode_bits(cache_bits[b, g], dtype)
+    if elem_scale != 1.0:
+        out = out * float(elem_scale)
+    if block_scales is not None:
+        out = out * float(np.float32(block_scales[b, g]))
+    return out
 
 
 # ----------------------------------------------------------------------------
@@ -120,21 +166,22 @@ def decode_bits(bits: np.ndarray, dtype: str) -> np.ndarray:
 # ----------------------------------------------------------------------------
 
 def logical_kv(cache_bits: np.ndarray, block_tables: np.ndarray, s: int, L: int, kvh: int,
-               dtype: str, elem_scale: float = 1.0) -> np.ndarray:
+               dtype: str, elem_scale: float = 1.0, block_scales: Optional[np.ndarray] = None) -> np.ndarray:
     """K or V of sequence s, KV head kvh, in logical token order: float64 [L, D].
 
     Token t is read from physical block block_tables[s, t // bs], slot t % bs.
     Only the ceil(L / bs) table entries that hold tokens are read.
     """
-    bs = cache_bits.shape[3]
+    bs = _tokens_per_row(cache_bits, dtype)
     D = cache_bits.shape[2]
     if L == 0:
         return np.zeros((0, D), dtype=np.float64)
     nblk = (L + bs - 1) // bs
     ids = np.asarray(block_tables[s, :nblk], dtype=np.int64)
-    tiles = cache_bits[ids, kvh]                      # [nblk, D, bs]
-    tokens = np.transpose(tiles, (0, 2, 1)).reshape(nblk * bs, D)[:L]
-    out = decode_bits(tokens, dtype)
+    tiles = decode_bits(cache_bits[ids, kvh], dtype)  # [nblk, D, bs]
+    if block_scales is not None:
+        tiles = tiles * np.asarray(block_scales, dtype=np.float32)[ids, kvh].astype(np.float64)[:, None, None]
+    out = np.transpose(tiles, (0, 2, 1)).reshape(nblk * bs, D)[:L]
     if elem_scale != 1.0:
         out = out * float(elem_scale)
     return out
@@ -167,7 +214,8 @@ def _check_shapes(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads):
 
 def paged_decode_rows(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale,
                       q_dtype: str, kv_dtype: str, rows: Iterable[Tuple[int, int]],
-                      k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
+                      k_scale: float = 1.0, v_scale: float = 1.0, k_block_scales=None,
+                      v_block_scales=None) -> np.ndarray:
     """out[s, h, :] for the listed (s, h) pairs only: float64 [len(rows), D]."""
     S, H, D, G = _check_shapes(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads)
     sc64 = float(np.float32(scale))
@@ -180,8 +228,8 @@ def paged_decode_rows(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads,
         if key not in cache:
             cache.clear()
             L = int(seq_lens[s])
-            cache[key] = (logical_kv(k_cache, block_tables, s, L, g, kv_dtype, k_scale),
-                          logical_kv(v_cache, block_tables, s, L, g, kv_dtype, v_scale))
+            cache[key] = (logical_kv(k_cache, block_tables, s, L, g, kv_dtype, k_scale, k_block_scales),
+                          logical_kv(v_cache, block_tables, s, L, g, kv_dtype, v_scale, v_block_scales))
         K, V = cache[key]
         out[i] = dense_attention(decode_bits(q[s, h], q_dtype), K, V, sc64)
     return out
@@ -189,7 +237,7 @@ def paged_decode_rows(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads,
 
 def paged_decode(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale,
                  q_dtype: str, kv_dtype: str, k_scale: float = 1.0, v_scale: float = 1.0,
-                 seqs: Optional[Sequence[int]] = None) -> np.ndarray:
+                 seqs: Optional[Sequence[int]] = None, k_block_scales=None, v_block_scales=None) -> np.ndarray:
     """Full output float64 [S, H, D] (rows of sequences not in `seqs` stay zero).
 
     All query heads of one KV head are done together: scores [G, L] = q_g @ K^T.
@@ -202,8 +250,8 @@ def paged_decode(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scal
         if L == 0:
             continue
         for g in range(num_kv_heads):
-            K = logical_kv(k_cache, block_tables, s, L, g, kv_dtype, k_scale)
-            V = logical_kv(v_cache, block_tables, s, L, g, kv_dtype, v_scale)
+            K = logical_kv(k_cache, block_tables, s, L, g, kv_dtype, k_scale, k_block_scales)
+            V = logical_kv(v_cache, block_tables, s, L, g, kv_dtype, v_scale, v_block_scales)
             qg = decode_bits(q[s, g * G:(g + 1) * G], q_dtype)          # [G, D]
             sc = sc64 * (qg @ K.T)                                        # [G, L]
             w = np.exp(sc - sc.max(axis=1, keepdims=True))
@@ -216,7 +264,7 @@ def paged_decode(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scal
 # ----------------------------------------------------------------------------
 
 def _online_partition(qv, k_cache, v_cache, table_row, L, g, first_block, last_block, bs,
-                      kv_dtype, scale, k_scale, v_scale):
+                      kv_dtype, scale, k_scale, v_scale, k_block_scales=None, v_block_scales=None):
     """Online softmax over logical blocks [first_block, last_block) of one sequence.
 
     Per block: scores = scale * q . K_block; m_new = max(m, max scores);
@@ -230,8 +278,8 @@ def _online_partition(qv, k_cache, v_cache, table_row, L, g, first_block, last_b
         n_valid = min(bs, L - j * bs)
         if n_valid <= 0:
             break
-        Kb = decode_bits(k_cache[b, g][:, :n_valid], kv_dtype) * k_scale    # [D, n]
-        Vb = decode_bits(v_cache[b, g][:, :n_valid], kv_dtype) * v_scale
+        Kb = block_values(k_cache, b, g, kv_dtype, k_scale, k_block_scales)[:, :n_valid]    # [D, n]
+        Vb = block_values(v_cache, b, g, kv_dtype, v_scale, v_block_scales)[:, :n_valid]
         scores = scale * (qv @ Kb)
         m_new = max(m, float(scores.max()))
         alpha = math.exp(m - m_new) if m != -math.inf else 0.0
@@ -259,11 +307,12 @@ def merge_partials(parts: List[Tuple[float, float, np.ndarray]]) -> np.ndarray:
 
 def online_decode(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale,
                   q_dtype: str, kv_dtype: str, partition_blocks: Optional[int] = None,
-                  k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
+                  k_scale: float = 1.0, v_scale: float = 1.0, k_block_scales=None,
+                  v_block_scales=None) -> np.ndarray:
     """Block-by-block online softmax, optionally split into partitions of
     `partition_blocks` logical blocks whose states are merged at the end."""
     S, H, D, G = _check_shapes(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads)
-    bs = k_cache.shape[3]
+    bs = _tokens_per_row(k_cache, kv_dtype)
     sc64 = float(np.float32(scale))
     out = np.zeros((S, H, D), dtype=np.float64)
     for s in range(S):
@@ -274,7 +323,8 @@ def online_decode(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, sca
             g = h // G
             qv = decode_bits(q[s, h], q_dtype)
             parts = [_online_partition(qv, k_cache, v_cache, block_tables[s], L, g, b0,
-                                       min(nblk, b0 + step), bs, kv_dtype, sc64, k_scale, v_scale)
+                                       min(nblk, b0 + step), bs, kv_dtype, sc64, k_scale, v_scale,
+                                       k_block_scales, v_block_scales)
                      for b0 in range(0, nblk, step)]
             out[s, h] = merge_partials(parts) if parts else 0.0
     return out
@@ -380,31 +430,60 @@ def bf16_encode(x) -> np.ndarray:
     return bits.astype(np.uint16)
 
 
+def int4_encode(y) -> np.ndarray:
+    """Values (already divided by their scale) -> int4 codes (int8, unpacked):
+    the nearest integer, ties to even, held to -8..7; NaN gives 0."""
+    y = np.asarray(y, dtype=np.float64)
+    r = np.rint(np.where(np.isnan(y), 0.0, y))
+    return np.clip(r, -8, 7).astype(np.int8)
+
+
 def encode_bits(values_f32: np.ndarray, dtype: str, scale: float = 1.0) -> np.ndarray:
-    """float32 values -> cache storage bits. The fp8 code is taken of value / scale,
-    the division done in float32 (one correctly rounded division)."""
+    """float32 values -> cache storage bits. The fp8 and int4 codes are taken of
+    value / scale, the division done in float32 (one correctly rounded
+    division). int4 codes come back unpacked (int8, one per value)."""
     v = np.asarray(values_f32, dtype=np.float32)
     if dtype == "f32":
         return v.copy()
     if dtype == "bf16":
         return bf16_encode(v)
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        y = (v / np.float32(scale)).astype(np.float64)
     if dtype == "e5m2":
-        return e5m2_encode((v / np.float32(scale)).astype(np.float64))
+        return e5m2_encode(y)
     if dtype == "e4m3":
-        return e4m3_encode((v / np.float32(scale)).astype(np.float64))
+        return e4m3_encode(y)
+    if dtype == "int4":
+        return int4_encode(y)
     raise ValueError(dtype)
 
 
+def _write_token(cache, blk, slot, codes, dtype):
+    """Store one token's codes [Hkv, D] at (blk, slot); int4 replaces one nibble."""
+    if dtype != "int4":
+        cache[blk, :, :, slot] = codes
+        return
+    byte = cache[blk, :, :, slot // 2]
+    nib = (np.asarray(codes, dtype=np.int16) & 0x0F).astype(np.uint8)
+    if slot % 2 == 0:
+        cache[blk, :, :, slot // 2] = (byte & 0xF0) | nib
+    else:
+        cache[blk, :, :, slot // 2] = (byte & 0x0F) | (nib << 4)
+
+
 def paged_append(k_new, v_new, k_cache, v_cache, block_tables, token_seq, token_pos,
-                 in_dtype: str, kv_dtype: str, k_scale: float = 1.0, v_scale: float = 1.0):
+                 in_dtype: str, kv_dtype: str, k_scale: float = 1.0, v_scale: float = 1.0,
+                 k_block_scales=None, v_block_scales=None):
     """Write new tokens into copies of the caches; returns (k_cache', v_cache').
 
     Token i (K/V rows [num_kv_heads, head_dim] in k_new[i], v_new[i]) belongs to
     sequence token_seq[i] at logical position token_pos[i] >= 0; a negative
-    position marks a padding entry that writes nothing.
+    position marks a padding entry that writes nothing. With per-block scales
+    the code of KV head g is taken of value / (k_scale * k_block_scales[blk, g]),
+    the product rounded to float32 first.
     """
     k_out, v_out = k_cache.copy(), v_cache.copy()
-    bs = k_cache.shape[3]
+    bs = _tokens_per_row(k_cache, kv_dtype)
     for i in range(len(token_seq)):
         pos = int(token_pos[i])
         if pos < 0:
@@ -412,18 +491,31 @@ def paged_append(k_new, v_new, k_cache, v_cache, block_tables, token_seq, token_
         blk = int(block_tables[int(token_seq[i]), pos // bs])
         kv = decode_bits(k_new[i], in_dtype).astype(np.float32)    # [Hkv, D], exact
         vv = decode_bits(v_new[i], in_dtype).astype(np.float32)
-        k_out[blk, :, :, pos % bs] = encode_bits(kv, kv_dtype, k_scale)
-        v_out[blk, :, :, pos % bs] = encode_bits(vv, kv_dtype, v_scale)
+        for cache_out, x, sc, bsc in ((k_out, kv, k_scale, k_block_scales), (v_out, vv, v_scale, v_block_scales)):
+            if bsc is None:
+                codes = encode_bits(x, kv_dtype, sc)
+            else:
+                per_head = np.float32(sc) * np.asarray(bsc, dtype=np.float32)[blk]          # [Hkv], float32
+                codes = np.stack([encode_bits(x[g], kv_dtype, per_head[g]) for g in range(x.shape[0])])
+            _write_token(cache_out, blk, pos % bs, codes, kv_dtype)
     return k_out, v_out
 
 
-def copy_blocks(k_cache, v_cache, src, dst):
-    """Copies of the caches with physical block dst[i] replaced by block src[i]."""
+def copy_blocks(k_cache, v_cache, src, dst, k_block_scales=None, v_block_scales=None):
+    """Copies of the caches with physical block dst[i] replaced by block src[i].
+    With per-block scales, returns them copied alike as a third and fourth item."""
     k_out, v_out = k_cache.copy(), v_cache.copy()
+    ks_out = None if k_block_scales is None else np.array(k_block_scales, copy=True)
+    vs_out = None if v_block_scales is None else np.array(v_block_scales, copy=True)
     for a, b in zip(np.asarray(src), np.asarray(dst)):
         k_out[int(b)] = k_cache[int(a)]
         v_out[int(b)] = v_cache[int(a)]
-    return k_out, v_out
+        if ks_out is not None:
+            ks_out[int(b)] = k_block_scales[int(a)]
+            vs_out[int(b)] = v_block_scales[int(a)]
+    if ks_out is None:
+        return k_out, v_out
+    return k_out, v_out, ks_out, vs_out
 
 
 # ----------------------------------------------------------------------------
@@ -440,7 +532,8 @@ def copy_blocks(k_cache, v_cache, src, dst):
 # is this computation over the paged cache.
 
 def paged_attention_multi(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale,
-                          q_dtype: str, kv_dtype: str, k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
+                          q_dtype: str, kv_dtype: str, k_scale: float = 1.0, v_scale: float = 1.0,
+                          k_block_scales=None, v_block_scales=None) -> np.ndarray:
     """q [S, q_len, H, D] -> float64 [S, q_len, H, D].
 
     seq_lens[s] counts every token in the cache, the q_len new ones included.
@@ -457,8 +550,8 @@ def paged_attention_multi(q, k_cache, v_cache, block_tables, seq_lens, num_kv_he
         if L == 0:
             continue
         for g in range(num_kv_heads):
-            K = logical_kv(k_cache, block_tables, s, L, g, kv_dtype, k_scale)
-            V = logical_kv(v_cache, block_tables, s, L, g, kv_dtype, v_scale)
+            K = logical_kv(k_cache, block_tables, s, L, g, kv_dtype, k_scale, k_block_scales)
+            V = logical_kv(v_cache, block_tables, s, L, g, kv_dtype, v_scale, v_block_scales)
             for i in range(QL):
                 n = L - QL + 1 + i
                 if n <= 0:

@@ -11,7 +11,8 @@ from __future__ import annotations
 
 import numpy as np
 
-ELEM_BYTES = {"f32": 4, "bf16": 2, "e5m2": 1, "e4m3": 1}
+ELEM_BYTES = {"f32": 4, "bf16": 2, "e5m2": 1, "e4m3": 1, "int4": 0.5}
+BLOCK_SCALE_BYTES = 4   # one float32 scale per (block, KV head) for K and one for V (int4)
 
 
 def kv_cache_bytes(num_layers: int, num_kv_heads: int, head_dim: int, seq_len: int, elem_bytes: int) -> int:
@@ -20,12 +21,17 @@ def kv_cache_bytes(num_layers: int, num_kv_heads: int, head_dim: int, seq_len: i
 
 
 def kv_bytes_per_token_layer(num_kv_heads: int, head_dim: int, kv_dtype: str) -> int:
-    return 2 * num_kv_heads * head_dim * ELEM_BYTES[kv_dtype]
+    return int(2 * num_kv_heads * head_dim * ELEM_BYTES[kv_dtype])
 
 
-def algorithmic_kv_bytes(seq_lens, num_kv_heads: int, head_dim: int, kv_dtype: str) -> int:
-    """Token-exact K+V bytes one decode call must read (logical tokens)."""
-    return int(np.asarray(seq_lens, dtype=np.int64).sum()) * kv_bytes_per_token_layer(num_kv_heads, head_dim, kv_dtype)
+def algorithmic_kv_bytes(seq_lens, num_kv_heads: int, head_dim: int, kv_dtype: str, block_size: int = 16) -> int:
+    """Token-exact K+V bytes one decode call must read (logical tokens); an int4
+    cache adds its K and V scale of every logical block it reads."""
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    total = int(lens.sum()) * kv_bytes_per_token_layer(num_kv_heads, head_dim, kv_dtype)
+    if kv_dtype == "int4":
+        total += int(((lens + block_size - 1) // block_size).sum()) * 2 * num_kv_heads * BLOCK_SCALE_BYTES
+    return total
 
 
 def unique_kv_bytes(seq_lens, block_tables, num_kv_heads: int, head_dim: int, block_size: int, kv_dtype: str) -> int:

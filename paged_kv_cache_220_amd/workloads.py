@@ -13,7 +13,9 @@ Shapes follow the pages:
   * seq_lens     [num_seqs]
 
 Every array is returned as its raw storage bits (float32, uint16 for bf16,
-uint8 for fp8-e5m2) so that both sides see exactly the same bytes.
+uint8 for fp8, packed uint8 for int4: two tokens per byte, the even token in
+the low nibble) so that both sides see exactly the same bytes. An int4 batch
+also carries float32 scales per (physical block, KV head) for K and V.
 
 Seeds: workload ``cN`` uses ``numpy.random.default_rng([220, N])`` for the
 sequence lengths, the pool placement and q (drawn in that order); K and V are
@@ -39,9 +41,10 @@ F32 = "f32"
 BF16 = "bf16"
 E5M2 = "e5m2"
 E4M3 = "e4m3"
+INT4 = "int4"
 
-_NP_STORAGE = {F32: np.float32, BF16: np.uint16, E5M2: np.uint8, E4M3: np.uint8}
-ELEM_BYTES = {F32: 4, BF16: 2, E5M2: 1, E4M3: 1}
+_NP_STORAGE = {F32: np.float32, BF16: np.uint16, E5M2: np.uint8, E4M3: np.uint8, INT4: np.uint8}
+ELEM_BYTES = {F32: 4, BF16: 2, E5M2: 1, E4M3: 1, INT4: 0.5}
 
 # Quiet-NaN bit patterns used to poison memory the kernel must never read.
 NAN_BITS = {F32: np.uint32(0x7FC00000).view(np.float32), BF16: np.uint16(0x7FC0), E5M2: np.uint8(0x7F),
@@ -70,6 +73,8 @@ class Workload:
     v_cache: np.ndarray         # storage bits [NB, Hkv, D, bs]
     seed: tuple = ()
     poisoned: bool = False
+    k_block_scales: Optional[np.ndarray] = None   # float32 [NB, Hkv] (int4 caches)
+    v_block_scales: Optional[np.ndarray] = None
 
     @property
     def num_blocks(self) -> int:
@@ -138,6 +143,32 @@ def _normal_chunked(shape, seed_root, stream: int, dtype: str) -> np.ndarray:
         with ThreadPoolExecutor(workers) as ex:
             list(ex.map(fill, range(nchunks)))
     return out.reshape(shape)
+
+
+def _pack_int4(codes: np.ndarray) -> np.ndarray:
+    """Signed codes -8..7 [..., 2n] -> bytes [..., n], the even token in the low nibble."""
+    u = (codes.astype(np.int16) & 0x0F).astype(np.uint8)
+    return (u[..., 0::2] | (u[..., 1::2] << 4)).astype(np.uint8)
+
+
+def _int4_chunked(shape, seed_root, stream: int) -> np.ndarray:
+    """int4 codes for a pool of `shape` [NB, Hkv, D, bs] (packed on the last axis).
+
+    Each code is an N(0,1) draw times 7/3, rounded to the nearest integer and
+    held to -8..7 (about three standard deviations fill the code range), drawn
+    chunk by chunk like the float pools. Synthetic storage only: the values a
+    cache would hold are code * scale, with the scales drawn separately.
+    """
+    flat = _normal_chunked(shape, seed_root, stream, F32).reshape(shape)
+    codes = np.clip(np.rint(flat * np.float32(7.0 / 3.0)), -8, 7).astype(np.int8)
+    return _pack_int4(codes)
+
+
+def _block_scales(nb: int, hkv: int, seed_root, stream: int) -> np.ndarray:
+    """float32 scales per (block, KV head), log-uniform in [1/8, 1/2]: blocks
+    differ, so a scale applied to the wrong block shows in the output."""
+    rng = np.random.default_rng(list(seed_root) + [stream, 1 << 20])
+    return np.exp2(rng.uniform(-3.0, -1.0, size=(nb, hkv))).astype(np.float32)
 
 
 def _blocks_needed(seq_lens: np.ndarray, bs: int) -> np.ndarray:
@@ -244,7 +275,7 @@ def make_workload(name: str, *, num_seqs: Optional[int] = None, seq_len: Optiona
     else:
         H, Hkv, D, qd, kvd = 64, 8, 128, BF16, BF16
     if kv_dtype is not None:
-        if qd != BF16 or kv_dtype not in (BF16, E5M2, E4M3):
+        if qd != BF16 or kv_dtype not in (BF16, E5M2, E4M3, INT4):
             raise ValueError(f"{name} cannot take a {kv_dtype} cache")
         kvd = kv_dtype
 
@@ -275,40 +306,63 @@ def make_workload(name: str, *, num_seqs: Optional[int] = None, seq_len: Optiona
 
     q_f = rng.standard_normal((S, H, D), dtype=np.float32)
     q = to_storage(q_f, qd)
-    k = _normal_chunked((pool, Hkv, D, bs), seed_root, 1, kvd)
-    v = _normal_chunked((pool, Hkv, D, bs), seed_root, 2, kvd)
+    ks = vs = None
+    if kvd == INT4:
+        k = _int4_chunked((pool, Hkv, D, bs), seed_root, 1)
+        v = _int4_chunked((pool, Hkv, D, bs), seed_root, 2)
+        ks = _block_scales(pool, Hkv, seed_root, 1)
+        vs = _block_scales(pool, Hkv, seed_root, 2)
+    else:
+        k = _normal_chunked((pool, Hkv, D, bs), seed_root, 1, kvd)
+        v = _normal_chunked((pool, Hkv, D, bs), seed_root, 2, kvd)
 
     if poison:
-        _apply_poison(tables, seq_lens, need, k, v, kvd, bs, poison_block=pool - 1)
+        _apply_poison(tables, seq_lens, need, k, v, kvd, bs, poison_block=pool - 1, k_scales=ks, v_scales=vs)
 
     one = np.float32(1.0)
     return Workload(name=name, num_seqs=S, num_heads=H, num_kv_heads=Hkv, head_dim=D, block_size=bs,
                     q_dtype=qd, kv_dtype=kvd, scale=np.float32(1.0 / math.sqrt(D)), k_scale=one,
                     v_scale=one, seq_lens=seq_lens, block_tables=tables, q=q, k_cache=k, v_cache=v,
-                    seed=seed_root, poisoned=poison)
+                    seed=seed_root, poisoned=poison, k_block_scales=ks, v_block_scales=vs)
 
 
-def _apply_poison(tables, seq_lens, need, k, v, kvd, bs, poison_block):
-    nan = NAN_BITS[kvd]
+def _apply_poison(tables, seq_lens, need, k, v, kvd, bs, poison_block, k_scales=None, v_scales=None):
     referenced = np.zeros(k.shape[0], dtype=bool)
     for s, n in enumerate(need):
         referenced[tables[s, :n]] = True
     unref = ~referenced
-    k[unref] = nan
-    v[unref] = nan
+    if kvd == INT4:
+        # int4 codes have no NaN: unread blocks get NaN scales and the most
+        # negative code; tail slots get the most negative code (0x8 nibbles)
+        k_scales[unref] = np.nan
+        v_scales[unref] = np.nan
+        k[unref] = 0x88
+        v[unref] = 0x88
+    else:
+        nan = NAN_BITS[kvd]
+        k[unref] = nan
+        v[unref] = nan
     for s, (L, n) in enumerate(zip(seq_lens, need)):
         tables[s, n:] = poison_block
         if n > 0 and L % bs:
             last = tables[s, n - 1]
-            k[last, :, :, L % bs:] = nan
-            v[last, :, :, L % bs:] = nan
+            if kvd == INT4:
+                t0 = L % bs
+                for t in range(t0, bs):
+                    mask = np.uint8(0x0F if t % 2 == 0 else 0xF0)
+                    k[last, :, :, t // 2] = (k[last, :, :, t // 2] & ~mask) | (np.uint8(0x88) & mask)
+                    v[last, :, :, t // 2] = (v[last, :, :, t // 2] & ~mask) | (np.uint8(0x88) & mask)
+            else:
+                k[last, :, :, L % bs:] = nan
+                v[last, :, :, L % bs:] = nan
     # A shared block may be the partial last block of one sequence and a full
     # block of another; poisoning its tail then changes valid data. The
     # placements here never do that (shared prefixes are whole blocks).
 
 
 def workload_from_arrays(name, q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads,
-                         q_dtype, kv_dtype, scale=None, block_size=BLOCK_SIZE_DEFAULT) -> Workload:
+                         q_dtype, kv_dtype, scale=None, block_size=BLOCK_SIZE_DEFAULT,
+                         k_block_scales=None, v_block_scales=None) -> Workload:
     """Wrap hand-built arrays (edge cases) in a Workload."""
     S, H, D = q.shape
     one = np.float32(1.0)
@@ -317,7 +371,7 @@ def workload_from_arrays(name, q, k_cache, v_cache, block_tables, seq_lens, num_
                     block_size=block_size, q_dtype=q_dtype, kv_dtype=kv_dtype, scale=sc, k_scale=one,
                     v_scale=one, seq_lens=np.asarray(seq_lens, dtype=np.int32),
                     block_tables=np.asarray(block_tables, dtype=np.int32), q=q, k_cache=k_cache,
-                    v_cache=v_cache)
+                    v_cache=v_cache, k_block_scales=k_block_scales, v_block_scales=v_block_scales)
 
 
 def random_edge_workload(seed: int, S: int, H: int, Hkv: int, D: int, seq_lens, q_dtype=BF16,
@@ -330,6 +384,13 @@ def random_edge_workload(seed: int, S: int, H: int, Hkv: int, D: int, seq_lens, 
     pool = int(need.sum()) + extra_pool
     tables = _scatter_tables(rng, seq_lens, bs, pool, max_blocks)
     q = to_storage(rng.standard_normal((S, H, D), dtype=np.float32), q_dtype)
+    if kv_dtype == INT4:
+        seed_root = (220, 99, seed)
+        k = _int4_chunked((pool, Hkv, D, bs), seed_root, 1)
+        v = _int4_chunked((pool, Hkv, D, bs), seed_root, 2)
+        return workload_from_arrays(f"edge{seed}", q, k, v, tables, seq_lens, Hkv, q_dtype, kv_dtype,
+                                    k_block_scales=_block_scales(pool, Hkv, seed_root, 1),
+                                    v_block_scales=_block_scales(pool, Hkv, seed_root, 2))
     k = to_storage(rng.standard_normal((pool, Hkv, D, bs), dtype=np.float32), kv_dtype)
     v = to_storage(rng.standard_normal((pool, Hkv, D, bs), dtype=np.float32), kv_dtype)
     return workload_from_arrays(f"edge{seed}", q, k, v, tables, seq_lens, Hkv, q_dtype, kv_dtype)
@@ -344,5 +405,11 @@ def permute_pool(w: Workload, seed: int) -> Workload:
     v = np.empty_like(w.v_cache)
     k[pi] = w.k_cache
     v[pi] = w.v_cache
-    return dataclasses.replace(w, name=w.name + "-perm", k_cache=k, v_cache=v,
-                               block_tables=pi[w.block_tables].astype(np.int32))
+    ks = vs = None
+    if w.k_block_scales is not None:
+        ks = np.empty_like(w.k_block_scales)
+        vs = np.empty_like(w.v_block_scales)
+        ks[pi] = w.k_block_scales
+        vs[pi] = w.v_block_scales
+    return dataclasses.replace(w, name=w.name + "-perm", k_cache=k, v_cache=v, k_block_scales=ks,
+                               v_block_scales=vs, block_tables=pi[w.block_tables].astype(np.int32))
