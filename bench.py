@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--op", default="decode", choices=["decode", "append", "copy"],
                     help="decode (default): the attention hot path; append / copy: the cache writes")
     ap.add_argument("--config", default="c3", choices=["c1", "c2", "c3", "c4", "c5"])
-    ap.add_argument("--kv-dtype", default="", choices=["", "bf16", "e5m2", "e4m3"],
+    ap.add_argument("--kv-dtype", default="", choices=["", "bf16", "e5m2", "e4m3", "int4"],
                     help="cache type in place of the batch's own (bf16-query batches c2..c5)")
     ap.add_argument("--q-len", type=int, default=1,
                     help="query positions per sequence (speculative verification, chunked prefill); K/V read once")
@@ -134,10 +134,12 @@ def cpu_baseline(w, budget_s, q_len=1):
         if q_len > 1:
             O.paged_attention_multi(w.q[s:s + 1], w.k_cache, w.v_cache, w.block_tables[s:s + 1], w.seq_lens[s:s + 1],
                                     w.num_kv_heads, w.scale, w.q_dtype, w.kv_dtype, k_scale=float(w.k_scale),
-                                    v_scale=float(w.v_scale))
+                                    v_scale=float(w.v_scale), k_block_scales=w.k_block_scales,
+                                    v_block_scales=w.v_block_scales)
         else:
             O.paged_decode(w.q, w.k_cache, w.v_cache, w.block_tables, w.seq_lens, w.num_kv_heads, w.scale,
-                           w.q_dtype, w.kv_dtype, k_scale=float(w.k_scale), v_scale=float(w.v_scale), seqs=[s])
+                           w.q_dtype, w.kv_dtype, k_scale=float(w.k_scale), v_scale=float(w.v_scale), seqs=[s],
+                           k_block_scales=w.k_block_scales, v_block_scales=w.v_block_scales)
         t_total += time.perf_counter() - t0
         n_done += 1
         bytes_done += A.algorithmic_kv_bytes(w.seq_lens[[s]], w.num_kv_heads, w.head_dim, w.kv_dtype)
@@ -206,6 +208,8 @@ def main():
             return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
         if dtype == "e4m3":
             return torch.from_numpy(np.ascontiguousarray(x)).view(torch.float8_e4m3fn).to(dev)
+        if dtype == "int4":
+            return torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).to(dev)     # packed codes
         return torch.from_numpy(np.ascontiguousarray(x)).view(torch.float8_e5m2).to(dev)
 
     kv_bytes = A.algorithmic_kv_bytes(w.seq_lens, w.num_kv_heads, w.head_dim, w.kv_dtype)
@@ -216,9 +220,13 @@ def main():
     seq_lens = torch.from_numpy(w.seq_lens).to(dev)
     caches = [(upload(w.k_cache, w.kv_dtype), upload(w.v_cache, w.kv_dtype)) for _ in range(R)]
     out = torch.empty_like(q)
+    scales = {}
+    if w.k_block_scales is not None:   # int4: per-(block, KV head) scales, shared by the replicas
+        scales = dict(k_block_scales=torch.from_numpy(w.k_block_scales).to(dev),
+                      v_block_scales=torch.from_numpy(w.v_block_scales).to(dev))
     kw = dict(kernel=args.kernel, partition_tokens=args.partition_tokens, max_seq_len=w.max_seq_len,
               k_scale=float(w.k_scale), v_scale=float(w.v_scale), schedule=args.schedule,
-              waves_per_item=args.waves_per_item)
+              waves_per_item=args.waves_per_item, **scales)
     dims = B.make_dims(q, caches[0][0], tables, **kw)
     plan = B.plan(dims, w.num_kv_heads)
     ws = B.alloc_workspace(dims, w.num_kv_heads, dev)

@@ -66,7 +66,15 @@ typedef enum pa_dtype {
   PA_DTYPE_F32 = 0,
   PA_DTYPE_BF16 = 1,      /* bfloat16; outputs rounded to nearest even              */
   PA_DTYPE_FP8_E5M2 = 2,  /* OCP E5M2 (bias 15, IEEE-style inf/NaN); KV cache only  */
-  PA_DTYPE_FP8_E4M3 = 3   /* OCP E4M3 (bias 7, no inf, S.1111.111 NaN); KV cache only */
+  PA_DTYPE_FP8_E4M3 = 3,  /* OCP E4M3 (bias 7, no inf, S.1111.111 NaN); KV cache only */
+  PA_DTYPE_INT4 = 4       /* two's-complement codes -8..7, two tokens per byte (the
+                             even token in the low nibble), so a block row of 16
+                             tokens is 8 bytes; values are code * k_scale (v_scale) *
+                             the block's scale (k_block_scales / v_block_scales,
+                             required). KV cache only, matrix-core kernel. The
+                             inference page's exercise names INT4 KV quantisation and
+                             its fourfold capacity over FP16; format and scale
+                             granularity are this library's reading.             */
 } pa_dtype_t;
 
 typedef enum pa_schedule {
@@ -122,6 +130,13 @@ typedef struct pa_dims {
                                   KV head, partition) item and merge their states in
                                   LDS: 1, 2 or 4 (4 only with group * q_len <= 16);
                                   0 = chosen by the library                          */
+  const float* k_block_scales; /* device, [num_blocks][num_kv_heads] float32: the K
+                                  values of physical block b, KV head g are multiplied
+                                  by k_block_scales[b * num_kv_heads + g]. Required for
+                                  INT4, optional (NULL) for FP8, NULL otherwise; only
+                                  entries of blocks the tables reference are read
+                                  (matrix-core kernel). 4-byte aligned.              */
+  const float* v_block_scales; /* the same for V                                      */
 } pa_dims_t;
 
 /* Decode with a workspace the library takes from the stream-ordered allocator

@@ -18,7 +18,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libpadecode.so")
 
 PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_ALIGN, PA_ERR_WORKSPACE, PA_ERR_HIP = range(7)
-PA_DTYPE_F32, PA_DTYPE_BF16, PA_DTYPE_FP8_E5M2, PA_DTYPE_FP8_E4M3 = 0, 1, 2, 3
+PA_DTYPE_F32, PA_DTYPE_BF16, PA_DTYPE_FP8_E5M2, PA_DTYPE_FP8_E4M3, PA_DTYPE_INT4 = 0, 1, 2, 3, 4
 KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
 KERNEL_NAMES = {v: k for k, v in KERNELS.items()}
 SCHEDULES = {"auto": 0, "grid": 1, "queue": 2}
@@ -36,7 +36,8 @@ class PaDims(ctypes.Structure):
                 ("kv_dtype", ctypes.c_int32), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
                 ("max_seq_len", ctypes.c_int32), ("partition_tokens", ctypes.c_int32),
                 ("kernel", ctypes.c_int32), ("q_len", ctypes.c_int32), ("schedule", ctypes.c_int32),
-                ("waves_per_item", ctypes.c_int32)]
+                ("waves_per_item", ctypes.c_int32), ("k_block_scales", ctypes.c_void_p),
+                ("v_block_scales", ctypes.c_void_p)]
 
 
 class PaPlan(ctypes.Structure):
@@ -102,7 +103,8 @@ def _check(rc: int):
 
 
 _TORCH_DTYPES = {torch.float32: PA_DTYPE_F32, torch.bfloat16: PA_DTYPE_BF16}
-_KV_NAMES = {"f32": PA_DTYPE_F32, "bf16": PA_DTYPE_BF16, "e5m2": PA_DTYPE_FP8_E5M2, "e4m3": PA_DTYPE_FP8_E4M3}
+_KV_NAMES = {"f32": PA_DTYPE_F32, "bf16": PA_DTYPE_BF16, "e5m2": PA_DTYPE_FP8_E5M2, "e4m3": PA_DTYPE_FP8_E4M3,
+             "int4": PA_DTYPE_INT4}
 
 
 def _kv_dtype_code(t: torch.Tensor, kv_dtype: Optional[str]) -> int:
@@ -112,15 +114,34 @@ def _kv_dtype_code(t: torch.Tensor, kv_dtype: Optional[str]) -> int:
         return PA_DTYPE_FP8_E5M2
     if t.dtype == torch.float8_e4m3fn:
         return PA_DTYPE_FP8_E4M3
+    if t.dtype == torch.uint8:
+        return PA_DTYPE_INT4          # packed int4 codes, two tokens per byte
     if t.dtype in _TORCH_DTYPES:
         return _TORCH_DTYPES[t.dtype]
     raise TypeError(f"unsupported KV cache dtype {t.dtype}; pass kv_dtype for raw byte views")
 
 
+def _tokens_per_row(k_cache: torch.Tensor, kv_code: int) -> int:
+    return k_cache.shape[3] * (2 if kv_code == PA_DTYPE_INT4 else 1)
+
+
+def _scale_ptr(t: Optional[torch.Tensor], k_cache: torch.Tensor, name: str):
+    """Device pointer of a [num_blocks, num_kv_heads] float32 scale array, or None."""
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or not t.is_contiguous() or t.device != k_cache.device:
+        raise ValueError(f"{name}: contiguous float32 on the caches' device expected")
+    if tuple(t.shape) != (k_cache.shape[0], k_cache.shape[1]):
+        raise ValueError(f"{name}: shape [num_blocks, num_kv_heads] expected")
+    return t.data_ptr()
+
+
 def make_dims(q: torch.Tensor, k_cache: torch.Tensor, block_tables: torch.Tensor, *,
               kv_dtype: Optional[str] = None, max_seq_len: int = 0, partition_tokens: int = 0,
               kernel: str = "auto", k_scale: float = 1.0, v_scale: float = 1.0,
-              schedule: str = "auto", waves_per_item: int = 0) -> PaDims:
+              schedule: str = "auto", waves_per_item: int = 0,
+              k_block_scales: Optional[torch.Tensor] = None,
+              v_block_scales: Optional[torch.Tensor] = None) -> PaDims:
     if q.dim() not in (3, 4) or k_cache.dim() != 4 or block_tables.dim() != 2:
         raise ValueError("q [S,H,D] or [S,q_len,H,D], k_cache [NB,Hkv,D,bs], block_tables [S,max_blocks] expected")
     if q.dtype not in _TORCH_DTYPES:
@@ -129,12 +150,15 @@ def make_dims(q: torch.Tensor, k_cache: torch.Tensor, block_tables: torch.Tensor
         S, QL, H, D = q.shape
     else:
         (S, H, D), QL = q.shape, 1
-    NB, _, _, bs = k_cache.shape
-    return PaDims(num_seqs=S, num_heads=H, head_dim=D, num_blocks=NB, block_size=bs,
+    kv_code = _kv_dtype_code(k_cache, kv_dtype)
+    NB = k_cache.shape[0]
+    return PaDims(num_seqs=S, num_heads=H, head_dim=D, num_blocks=NB, block_size=_tokens_per_row(k_cache, kv_code),
                   max_blocks_per_seq=block_tables.shape[1], q_dtype=_TORCH_DTYPES[q.dtype],
-                  kv_dtype=_kv_dtype_code(k_cache, kv_dtype), k_scale=k_scale, v_scale=v_scale,
+                  kv_dtype=kv_code, k_scale=k_scale, v_scale=v_scale,
                   max_seq_len=max_seq_len, partition_tokens=partition_tokens, kernel=KERNELS[kernel], q_len=QL,
-                  schedule=SCHEDULES[schedule], waves_per_item=waves_per_item)
+                  schedule=SCHEDULES[schedule], waves_per_item=waves_per_item,
+                  k_block_scales=_scale_ptr(k_block_scales, k_cache, "k_block_scales"),
+                  v_block_scales=_scale_ptr(v_block_scales, k_cache, "v_block_scales"))
 
 
 def plan(dims: PaDims, num_kv_heads: int) -> dict:
@@ -175,7 +199,9 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, blo
               seq_lens: torch.Tensor, num_kv_heads: int, scale: float, out: Optional[torch.Tensor] = None, *,
               kv_dtype: Optional[str] = None, max_seq_len: int = 0, partition_tokens: int = 0,
               kernel: str = "auto", k_scale: float = 1.0, v_scale: float = 1.0, schedule: str = "auto",
-              waves_per_item: int = 0, workspace: Optional[torch.Tensor] = None, events=None) -> torch.Tensor:
+              waves_per_item: int = 0, workspace: Optional[torch.Tensor] = None, events=None,
+              k_block_scales: Optional[torch.Tensor] = None,
+              v_block_scales: Optional[torch.Tensor] = None) -> torch.Tensor:
     """PagedAttention decode through the C ABI; returns `out`.
 
     q may be [S, H, D] (one query per sequence) or [S, q_len, H, D] (the last
@@ -190,7 +216,8 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, blo
     _validate_tensors(q, k_cache, v_cache, block_tables, seq_lens, out)
     dims = make_dims(q, k_cache, block_tables, kv_dtype=kv_dtype, max_seq_len=max_seq_len,
                      partition_tokens=partition_tokens, kernel=kernel, k_scale=k_scale, v_scale=v_scale,
-                     schedule=schedule, waves_per_item=waves_per_item)
+                     schedule=schedule, waves_per_item=waves_per_item, k_block_scales=k_block_scales,
+                     v_block_scales=v_block_scales)
     lib = load_library()
     stream = ctypes.c_void_p(torch.cuda.current_stream(q.device).cuda_stream)
     args = (ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_cache.data_ptr()),
@@ -221,11 +248,14 @@ class DecodeCall:
 
     def __init__(self, q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale, out, *,
                  workspace=None, kv_dtype=None, max_seq_len=0, partition_tokens=0, kernel="auto",
-                 k_scale=1.0, v_scale=1.0, schedule="auto", waves_per_item=0):
+                 k_scale=1.0, v_scale=1.0, schedule="auto", waves_per_item=0, k_block_scales=None,
+                 v_block_scales=None):
         _validate_tensors(q, k_cache, v_cache, block_tables, seq_lens, out)
         self.dims = make_dims(q, k_cache, block_tables, kv_dtype=kv_dtype, max_seq_len=max_seq_len,
                               partition_tokens=partition_tokens, kernel=kernel, k_scale=k_scale, v_scale=v_scale,
-                              schedule=schedule, waves_per_item=waves_per_item)
+                              schedule=schedule, waves_per_item=waves_per_item,
+                              k_block_scales=k_block_scales, v_block_scales=v_block_scales)
+        self._scales = (k_block_scales, v_block_scales)   # keep the tensors alive with the pointers
         if workspace is None:
             workspace = alloc_workspace(self.dims, num_kv_heads, q.device)
         self._keep = (q, k_cache, v_cache, block_tables, seq_lens, out, workspace)
@@ -253,18 +283,22 @@ def alloc_workspace(dims: PaDims, num_kv_heads: int, device) -> torch.Tensor:
 
 
 def _cache_dims(k_cache: torch.Tensor, block_tables: Optional[torch.Tensor], kv_dtype: Optional[str],
-                k_scale: float, v_scale: float) -> PaDims:
-    NB, _, D, bs = k_cache.shape
+                k_scale: float, v_scale: float, k_block_scales=None, v_block_scales=None) -> PaDims:
+    NB, _, D, _ = k_cache.shape
+    kv_code = _kv_dtype_code(k_cache, kv_dtype)
     S, MB = (block_tables.shape if block_tables is not None else (1, 1))
-    return PaDims(num_seqs=S, num_heads=k_cache.shape[1], head_dim=D, num_blocks=NB, block_size=bs,
-                  max_blocks_per_seq=MB, q_dtype=PA_DTYPE_BF16, kv_dtype=_kv_dtype_code(k_cache, kv_dtype),
-                  k_scale=k_scale, v_scale=v_scale, max_seq_len=0, partition_tokens=0, kernel=0, q_len=0,
-                  schedule=0)
+    return PaDims(num_seqs=S, num_heads=k_cache.shape[1], head_dim=D, num_blocks=NB,
+                  block_size=_tokens_per_row(k_cache, kv_code), max_blocks_per_seq=MB, q_dtype=PA_DTYPE_BF16,
+                  kv_dtype=kv_code, k_scale=k_scale, v_scale=v_scale, max_seq_len=0, partition_tokens=0, kernel=0,
+                  q_len=0, schedule=0, k_block_scales=_scale_ptr(k_block_scales, k_cache, "k_block_scales"),
+                  v_block_scales=_scale_ptr(v_block_scales, k_cache, "v_block_scales"))
 
 
 def pa_cache_append(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                     block_tables: torch.Tensor, token_seq: torch.Tensor, token_pos: torch.Tensor, *,
-                    kv_dtype: Optional[str] = None, k_scale: float = 1.0, v_scale: float = 1.0) -> None:
+                    kv_dtype: Optional[str] = None, k_scale: float = 1.0, v_scale: float = 1.0,
+                    k_block_scales: Optional[torch.Tensor] = None,
+                    v_block_scales: Optional[torch.Tensor] = None) -> None:
     """Write new tokens' K/V ([num_tokens, num_kv_heads, head_dim]) into the paged caches in place."""
     for name, t in (("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache), ("v_cache", v_cache),
                     ("block_tables", block_tables), ("token_seq", token_seq), ("token_pos", token_pos)):
@@ -275,7 +309,7 @@ def pa_cache_append(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Ten
     if token_seq.dtype != torch.int32 or token_pos.dtype != torch.int32 or block_tables.dtype != torch.int32:
         raise TypeError("block_tables, token_seq and token_pos must be int32")
     n, hkv, _ = k_new.shape
-    dims = _cache_dims(k_cache, block_tables, kv_dtype, k_scale, v_scale)
+    dims = _cache_dims(k_cache, block_tables, kv_dtype, k_scale, v_scale, k_block_scales, v_block_scales)
     stream = ctypes.c_void_p(torch.cuda.current_stream(k_cache.device).cuda_stream)
     rc = load_library().pa_cache_append(
         ctypes.c_void_p(k_new.data_ptr()), ctypes.c_void_p(v_new.data_ptr()), ctypes.c_void_p(k_cache.data_ptr()),
@@ -286,14 +320,17 @@ def pa_cache_append(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Ten
 
 
 def pa_cache_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, src_blocks: torch.Tensor,
-                         dst_blocks: torch.Tensor, *, kv_dtype: Optional[str] = None) -> None:
-    """Copy physical blocks src_blocks[i] -> dst_blocks[i] in both caches (in place)."""
+                         dst_blocks: torch.Tensor, *, kv_dtype: Optional[str] = None,
+                         k_block_scales: Optional[torch.Tensor] = None,
+                         v_block_scales: Optional[torch.Tensor] = None) -> None:
+    """Copy physical blocks src_blocks[i] -> dst_blocks[i] in both caches (in place), and
+    their per-block scales when given."""
     for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("src_blocks", src_blocks), ("dst_blocks", dst_blocks)):
         if t.device != k_cache.device or not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous on the caches' device")
     if src_blocks.dtype != torch.int32 or dst_blocks.dtype != torch.int32 or src_blocks.shape != dst_blocks.shape:
         raise TypeError("src_blocks / dst_blocks: int32 of the same length")
-    dims = _cache_dims(k_cache, None, kv_dtype, 1.0, 1.0)
+    dims = _cache_dims(k_cache, None, kv_dtype, 1.0, 1.0, k_block_scales, v_block_scales)
     stream = ctypes.c_void_p(torch.cuda.current_stream(k_cache.device).cuda_stream)
     rc = load_library().pa_cache_copy_blocks(
         ctypes.c_void_p(k_cache.data_ptr()), ctypes.c_void_p(v_cache.data_ptr()),

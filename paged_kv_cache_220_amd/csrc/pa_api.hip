@@ -48,6 +48,12 @@ int check_dims(const pa_dims_t* d, int32_t hkv) {
   if (d->partition_tokens % pa::kTileTokens != 0) return PA_ERR_SHAPE;
   if (!isfinite(d->k_scale) || !isfinite(d->v_scale)) return PA_ERR_SHAPE;
   if (d->q_len < 0) return PA_ERR_SHAPE;
+  // per-block scales: both or neither; required for int4, allowed for fp8
+  const bool fp8 = d->kv_dtype == PA_DTYPE_FP8_E5M2 || d->kv_dtype == PA_DTYPE_FP8_E4M3;
+  if ((d->k_block_scales == nullptr) != (d->v_block_scales == nullptr)) return PA_ERR_NULL;
+  if (d->kv_dtype == PA_DTYPE_INT4 && d->k_block_scales == nullptr) return PA_ERR_NULL;
+  if (d->k_block_scales != nullptr && d->kv_dtype != PA_DTYPE_INT4 && !fp8) return PA_ERR_UNSUPPORTED;
+  if (!aligned(d->k_block_scales, 4) || !aligned(d->v_block_scales, 4)) return PA_ERR_ALIGN;
   if (d->kernel < PA_KERNEL_AUTO || d->kernel > PA_KERNEL_MFMA) return PA_ERR_UNSUPPORTED;
   if (d->schedule < PA_SCHEDULE_AUTO || d->schedule > PA_SCHEDULE_QUEUE) return PA_ERR_UNSUPPORTED;
   if (d->waves_per_item != 0 && d->waves_per_item != 1 && d->waves_per_item != 2 && d->waves_per_item != 4)
@@ -58,7 +64,8 @@ int check_dims(const pa_dims_t* d, int32_t hkv) {
   const long long qblocks = ((long long)group * ql + 63) / 64;
   if ((long long)d->num_seqs * hkv * qblocks > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;  // grid x limit
   if ((long long)d->num_heads * ql > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;   // merge grid x
-  const bool valu_ok = ql == 1 && pa::valu_supported(d->q_dtype, d->kv_dtype, d->head_dim, group);
+  const bool valu_ok = ql == 1 && d->k_block_scales == nullptr &&
+                       pa::valu_supported(d->q_dtype, d->kv_dtype, d->head_dim, group);
   const bool mfma_ok = pa::mfma_supported(d->q_dtype, d->kv_dtype, d->head_dim, group, d->block_size, ql);
   if (d->kernel == PA_KERNEL_VALU && !valu_ok) return PA_ERR_UNSUPPORTED;
   if (d->kernel == PA_KERNEL_MFMA && !mfma_ok) return PA_ERR_UNSUPPORTED;
@@ -75,7 +82,7 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
   if (d->kernel == PA_KERNEL_AUTO) {
     p->kernel = pa::mfma_supported(d->q_dtype, d->kv_dtype, d->head_dim, p->group, d->block_size, p->q_len)
                     ? PA_KERNEL_MFMA
-                    : PA_KERNEL_VALU;
+                    : PA_KERNEL_VALU;   // check_dims guarantees the vector kernel takes what the other does not
   } else {
     p->kernel = d->kernel;
   }
@@ -83,14 +90,16 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
   // Every wave keeps about one 64-token tile of K and V in flight. Covering
   // HBM latency at full bandwidth takes about as many waves as the chip holds
   // at once: 2048 with bf16 / fp32 tiles (32 KiB, two waves per SIMD) and 3072
-  // with fp8 tiles (16 KiB; the fp8 kernel stages K in LDS and runs three
-  // waves per SIMD). Partitions are made as long as
+  // with fp8 and int4 tiles (16 / 8 KiB; those kernels stage K in LDS and run
+  // three waves per SIMD, fp8 with per-block scales two). Partitions are made as long as
   // possible (up to 4096 tokens: start-up and merge traffic are amortised) and
   // the waves come from splitting each item over 1, 2 or 4 waves; partitions
   // are shortened only when even 4 waves per item would not reach the target.
   const long long units = (long long)d->num_seqs * hkv * (p->kernel == PA_KERNEL_MFMA ? p->q_blocks : 1);
+  // three waves per SIMD: fp8 without per-block scales and int4 (with them)
   const bool fp8 = d->kv_dtype == PA_DTYPE_FP8_E5M2 || d->kv_dtype == PA_DTYPE_FP8_E4M3;
-  const long long target_waves = fp8 ? 3072 : 2048;
+  const bool three_waves = (fp8 && d->k_block_scales == nullptr) || d->kv_dtype == PA_DTYPE_INT4;
+  const long long target_waves = three_waves ? 3072 : 2048;
   auto items_for = [&](long long P) { return units * ((p->max_len + P - 1) / P); };
   int P = d->partition_tokens;
   if (P == 0) {
@@ -201,6 +210,8 @@ int run(const void* q, const void* k_cache, const void* v_cache, const int32_t* 
   a.v_scale = dims->v_scale;
   a.q_len = p.q_len;
   a.q_blocks = p.q_blocks;
+  a.k_bscale = dims->k_block_scales;
+  a.v_bscale = dims->v_block_scales;
   a.queue_items = nullptr;
   a.queue_len = nullptr;
   a.queue_workgroups = 0;

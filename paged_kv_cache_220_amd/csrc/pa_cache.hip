@@ -44,6 +44,13 @@ __device__ __forceinline__ uint8_t f32_to_e4m3(float x) {
   return static_cast<uint8_t>(sign | static_cast<uint32_t>(q));
 }
 
+// float -> int4 code: nearest integer, ties to even, held to -8..7; NaN gives 0.
+__device__ __forceinline__ uint32_t f32_to_int4_nibble(float y) {
+  if (y != y) return 0u;
+  const float r = fminf(fmaxf(rintf(y), -8.0f), 7.0f);
+  return static_cast<uint32_t>(static_cast<int>(r)) & 0xFu;
+}
+
 template <int IN> __device__ __forceinline__ float load_in(const void* p, int64_t i);
 template <> __device__ __forceinline__ float load_in<kF32>(const void* p, int64_t i) {
   return static_cast<const float*>(p)[i];
@@ -65,6 +72,17 @@ template <> __device__ __forceinline__ void store_kv<kE5M2>(void* cache, int64_t
 template <> __device__ __forceinline__ void store_kv<kE4M3>(void* cache, int64_t i, float x, float scale) {
   static_cast<uint8_t*>(cache)[i] = f32_to_e4m3(x / scale);
 }
+// int4: element i is nibble i & 1 of byte i / 2. Another token of the same call
+// may own the other nibble (or a neighbouring byte of the same word), so the
+// nibble is cleared and set with two atomics on its 32-bit word, which leave
+// every other nibble alone.
+template <> __device__ __forceinline__ void store_kv<kI4>(void* cache, int64_t i, float x, float scale) {
+  const int64_t byte = i >> 1;
+  unsigned int* word = reinterpret_cast<unsigned int*>(static_cast<uint8_t*>(cache) + (byte & ~int64_t(3)));
+  const uint32_t shift = uint32_t(byte & 3) * 8u + uint32_t(i & 1) * 4u;
+  atomicAnd(word, ~(0xFu << shift));
+  atomicOr(word, f32_to_int4_nibble(x / scale) << shift);
+}
 
 struct AppendArgs {
   const void* k_new;
@@ -76,6 +94,8 @@ struct AppendArgs {
   const int32_t* token_pos;
   int32_t num_tokens, num_kv_heads, head_dim, num_seqs, max_blocks, num_blocks;
   float k_scale, v_scale;
+  const float* k_bscale;   // per-(block, KV head) scales, or null
+  const float* v_bscale;
 };
 
 // One wavefront per (token, KV head); lane d writes rows d and d + 64.
@@ -90,10 +110,14 @@ __global__ __launch_bounds__(64) void append_kernel(const AppendArgs a) {
   id = min(max(id, 0), a.num_blocks - 1);
   const int slot = pos % kBlockSize;
   const int64_t src = ((int64_t)i * a.num_kv_heads + g) * a.head_dim;
-  const int64_t dst = (((int64_t)id * a.num_kv_heads + g) * a.head_dim) * kBlockSize + slot;
+  const int64_t dst = (((int64_t)id * a.num_kv_heads + g) * a.head_dim) * kBlockSize + slot;   // in elements
+  // code of value / scale, the scale being k_scale times the block's own
+  // (rounded to float32 first) when the cache has per-block scales
+  const float ks = a.k_bscale ? a.k_scale * a.k_bscale[(int64_t)id * a.num_kv_heads + g] : a.k_scale;
+  const float vs = a.v_bscale ? a.v_scale * a.v_bscale[(int64_t)id * a.num_kv_heads + g] : a.v_scale;
   for (int d = threadIdx.x; d < a.head_dim; d += 64) {
-    store_kv<KV>(a.k_cache, dst + (int64_t)d * kBlockSize, load_in<IN>(a.k_new, src + d), a.k_scale);
-    store_kv<KV>(a.v_cache, dst + (int64_t)d * kBlockSize, load_in<IN>(a.v_new, src + d), a.v_scale);
+    store_kv<KV>(a.k_cache, dst + (int64_t)d * kBlockSize, load_in<IN>(a.k_new, src + d), ks);
+    store_kv<KV>(a.v_cache, dst + (int64_t)d * kBlockSize, load_in<IN>(a.v_new, src + d), vs);
   }
 }
 
@@ -104,6 +128,9 @@ struct CopyArgs {
   const int32_t* dst;
   int64_t block_bytes;   // one physical block, all KV heads
   int32_t num_blocks;
+  int32_t num_kv_heads;
+  float* k_bscale;       // per-(block, KV head) scales copied with their blocks, or null
+  float* v_bscale;
 };
 
 constexpr int kCopyThreads = 256;
@@ -119,20 +146,31 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(const CopyArg
   char* base = blockIdx.z == 0 ? a.k_cache : a.v_cache;
   const uint4 x = *reinterpret_cast<const uint4*>(base + sb * a.block_bytes + off);
   *reinterpret_cast<uint4*>(base + db * a.block_bytes + off) = x;
+  if (a.k_bscale != nullptr && blockIdx.y == 0) {
+    float* sc = blockIdx.z == 0 ? a.k_bscale : a.v_bscale;
+    for (int g = threadIdx.x; g < a.num_kv_heads; g += kCopyThreads)
+      sc[db * a.num_kv_heads + g] = sc[sb * a.num_kv_heads + g];
+  }
 }
 
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
 
-int elem_bytes(int dtype) { return dtype == kF32 ? 4 : dtype == kBF16 ? 2 : 1; }
+int elem_bits(int dtype) { return dtype == kF32 ? 32 : dtype == kBF16 ? 16 : dtype == kI4 ? 4 : 8; }
 
 int check_cache_dims(const pa_dims_t* d, int32_t hkv) {
   if (d == nullptr) return PA_ERR_NULL;
   if (d->head_dim <= 0 || d->num_blocks <= 0 || d->block_size <= 0 || hkv <= 0) return PA_ERR_SHAPE;
   if (d->block_size != kBlockSize) return PA_ERR_UNSUPPORTED;
   if (d->head_dim != 64 && d->head_dim != 128) return PA_ERR_UNSUPPORTED;
-  if (d->kv_dtype != kF32 && d->kv_dtype != kBF16 && d->kv_dtype != kE5M2 && d->kv_dtype != kE4M3)
+  if (d->kv_dtype != kF32 && d->kv_dtype != kBF16 && d->kv_dtype != kE5M2 && d->kv_dtype != kE4M3 &&
+      d->kv_dtype != kI4)
     return PA_ERR_UNSUPPORTED;
   if (hkv > 65535) return PA_ERR_UNSUPPORTED;
+  // per-block scales: both or neither; required for int4, allowed for fp8
+  if ((d->k_block_scales == nullptr) != (d->v_block_scales == nullptr)) return PA_ERR_NULL;
+  if (d->kv_dtype == kI4 && d->k_block_scales == nullptr) return PA_ERR_NULL;
+  if (d->k_block_scales != nullptr && (d->kv_dtype == kF32 || d->kv_dtype == kBF16)) return PA_ERR_UNSUPPORTED;
+  if (!aligned(d->k_block_scales, 4) || !aligned(d->v_block_scales, 4)) return PA_ERR_ALIGN;
   return PA_OK;
 }
 
@@ -149,7 +187,7 @@ extern "C" int pa_cache_append(const void* k_new, const void* v_new, void* k_cac
   if (st != PA_OK) return st;
   if (num_tokens < 0 || dims->num_seqs <= 0 || dims->max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
   const int kv = dims->kv_dtype;
-  const bool fp8 = kv == kE5M2 || kv == kE4M3;
+  const bool fp8 = kv == kE5M2 || kv == kE4M3 || kv == kI4;   // coded caches: value / scale is encoded
   const bool combo = (in_dtype == kF32 && (kv == kF32 || kv == kBF16 || fp8)) || (in_dtype == kBF16 && (kv == kBF16 || fp8));
   if (!combo) return PA_ERR_UNSUPPORTED;
   if (!isfinite(dims->k_scale) || !isfinite(dims->v_scale) || dims->k_scale == 0.f || dims->v_scale == 0.f)
@@ -176,6 +214,8 @@ extern "C" int pa_cache_append(const void* k_new, const void* v_new, void* k_cac
   a.num_blocks = dims->num_blocks;
   a.k_scale = dims->k_scale;
   a.v_scale = dims->v_scale;
+  a.k_bscale = dims->k_block_scales;
+  a.v_bscale = dims->v_block_scales;
   const dim3 grid(num_tokens, num_kv_heads);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (in_dtype == kF32 && kv == kF32) append_kernel<kF32, kF32><<<grid, 64, 0, s>>>(a);
@@ -184,7 +224,9 @@ extern "C" int pa_cache_append(const void* k_new, const void* v_new, void* k_cac
   else if (in_dtype == kBF16 && kv == kBF16) append_kernel<kBF16, kBF16><<<grid, 64, 0, s>>>(a);
   else if (in_dtype == kF32 && kv == kE4M3) append_kernel<kF32, kE4M3><<<grid, 64, 0, s>>>(a);
   else if (in_dtype == kBF16 && kv == kE5M2) append_kernel<kBF16, kE5M2><<<grid, 64, 0, s>>>(a);
-  else append_kernel<kBF16, kE4M3><<<grid, 64, 0, s>>>(a);
+  else if (in_dtype == kBF16 && kv == kE4M3) append_kernel<kBF16, kE4M3><<<grid, 64, 0, s>>>(a);
+  else if (in_dtype == kF32 && kv == kI4) append_kernel<kF32, kI4><<<grid, 64, 0, s>>>(a);
+  else append_kernel<kBF16, kI4><<<grid, 64, 0, s>>>(a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -203,8 +245,12 @@ extern "C" int pa_cache_copy_blocks(void* k_cache, void* v_cache, const int32_t*
   a.v_cache = static_cast<char*>(v_cache);
   a.src = src_blocks;
   a.dst = dst_blocks;
-  a.block_bytes = (int64_t)num_kv_heads * dims->head_dim * dims->block_size * elem_bytes(dims->kv_dtype);
+  a.block_bytes = (int64_t)num_kv_heads * dims->head_dim * dims->block_size * elem_bits(dims->kv_dtype) / 8;
   a.num_blocks = dims->num_blocks;
+  a.num_kv_heads = num_kv_heads;
+  // the scale arrays travel with their blocks; the copy writes them
+  a.k_bscale = const_cast<float*>(dims->k_block_scales);
+  a.v_bscale = const_cast<float*>(dims->v_block_scales);
   const dim3 grid(num_pairs, (unsigned)((a.block_bytes + kCopyChunk - 1) / kCopyChunk), 2);
   copy_blocks_kernel<<<grid, kCopyThreads, 0, static_cast<hipStream_t>(stream)>>>(a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;

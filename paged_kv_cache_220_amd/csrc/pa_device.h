@@ -7,7 +7,7 @@
 namespace pa {
 
 // Storage-type tags (match pa_dtype_t).
-enum : int { kF32 = 0, kBF16 = 1, kE5M2 = 2, kE4M3 = 3 };
+enum : int { kF32 = 0, kBF16 = 1, kE5M2 = 2, kE4M3 = 3, kI4 = 4 };
 
 template <int T> struct Storage;
 template <> struct Storage<kF32> { using type = float; };

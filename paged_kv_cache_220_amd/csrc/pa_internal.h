@@ -40,6 +40,8 @@ struct Args {
   int32_t queue_workgroups;
   int32_t waves_per_item;   // matrix-core kernel: waves sharing one work item (1, 2, 4)
   int32_t q_blocks;         // blocks of up to 64 (query position, head) pairs per KV head
+  const float* k_bscale;    // per-(block, KV head) scales [num_blocks][num_kv_heads], or null
+  const float* v_bscale;
 };
 
 // Host-side launchers; each returns the hipError_t of the launch.

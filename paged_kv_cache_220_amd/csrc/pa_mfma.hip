@@ -72,7 +72,7 @@ template <> struct Mfma<kBF16> {
   using op_t = bf16x8;
   using kload_t = u32x2;   // 4 tokens of one row
   using vload_t = u32x4;   // 8 tokens of one row
-  static constexpr int kElem = 2;
+  static constexpr int kBits = 16;   // storage bits per value
   static __device__ __forceinline__ f32x4 mma(op_t a, op_t b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
@@ -121,7 +121,7 @@ template <> struct Mfma<kE5M2> {
   using op_t = f16x8;
   using kload_t = uint32_t;  // 4 tokens of one row
   using vload_t = u32x2;     // 8 tokens of one row
-  static constexpr int kElem = 1;
+  static constexpr int kBits = 8;
   static __device__ __forceinline__ f32x4 mma(op_t a, op_t b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
@@ -169,6 +169,54 @@ template <> struct Mfma<kE5M2> {
   }
 };
 
+// int4 KV: two's-complement codes, two tokens per byte (the even token in the
+// low nibble), so a K piece of 4 tokens is 2 bytes and a V piece of 8 tokens
+// 4 bytes. Widening is exact: with u = code ^ 8 (code + 8, 0..15), the
+// binary16 bit pattern 0x6400 | u is 1024 + u, and one packed binary16
+// subtraction of 1032 gives the code, two values per 32-bit word. The
+// per-block scales are applied to the scores (K) and to P (V) instead.
+template <> struct Mfma<kI4> {
+  using op_t = f16x8;
+  using kload_t = uint16_t;  // 4 tokens of one row
+  using vload_t = uint32_t;  // 8 tokens of one row
+  static constexpr int kBits = 4;
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ uint32_t widen2(uint32_t u) {   // nibble values at bits 0..3 and 16..19
+    const f16x2 v = __builtin_bit_cast(f16x2, u | 0x64006400u) - f16x2{(_Float16)1032.0f, (_Float16)1032.0f};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  static __device__ __forceinline__ f32x4 mma(op_t a, op_t b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  // token j of rows 2p (low half) and 2p + 1 (high half)
+  static __device__ __forceinline__ op_t k_operand(const kload_t (&r)[8], int j) {
+    u32x4 x;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t w = (uint32_t(r[2 * p]) | (uint32_t(r[2 * p + 1]) << 16)) ^ 0x88888888u;
+      x[p] = widen2((w >> (4 * j)) & 0x000F000Fu);
+    }
+    return __builtin_bit_cast(op_t, x);
+  }
+  static __device__ __forceinline__ op_t v_operand(vload_t x) {
+    const uint32_t w = x ^ 0x88888888u;
+    const uint32_t lo = w & 0x0F0F0F0Fu;          // even tokens, one per byte
+    const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;   // odd tokens
+    u32x4 y;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      y[p] = widen2(__builtin_amdgcn_perm(hi, lo, uint32_t(p) | (0x0Cu << 8) | (uint32_t(4 + p) << 16) | (0x0Cu << 24)));
+    return __builtin_bit_cast(op_t, y);
+  }
+  static __device__ __forceinline__ vload_t mask_v(vload_t x, int nvalid) {
+    return nvalid >= 8 ? x : (nvalid <= 0 ? 0u : x & ((1u << (4 * nvalid)) - 1u));   // code 0 = value 0
+  }
+  static __device__ __forceinline__ op_t q_operand(const uint32_t (&qb)[8]) { return Mfma<kE5M2>::q_operand(qb); }
+  static __device__ __forceinline__ void p_operands(const float (&p)[8], op_t& hi, op_t& lo) {
+    Mfma<kE5M2>::p_operands(p, hi, lo);
+  }
+};
+
 // Query columns. Query position qi (0 <= qi < q_len) of query head kvh*G + h
 // is "virtual head" v = qi*G + h, placed on MFMA column v % 16 of column group
 // v / 16; NCG groups cover G * q_len <= 16 * NCG. All groups share each K and
@@ -182,7 +230,7 @@ template <> struct Mfma<kE4M3> {
   using op_t = f16x8;
   using kload_t = uint32_t;  // 4 tokens of one row
   using vload_t = u32x2;     // 8 tokens of one row
-  static constexpr int kElem = 1;
+  static constexpr int kBits = 8;
   typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
   template <bool kHiWord>   // codes in bytes 2, 3 (else 0, 1) -> two binary16 values
   static __device__ __forceinline__ uint32_t cvt2(uint32_t x) {
@@ -219,14 +267,16 @@ template <> struct Mfma<kE4M3> {
 // items that are one of several query blocks of a KV head (four column
 // groups) load through the caches instead, so the sibling blocks that read
 // the same tiles at about the same time on the same XCD can hit in them.
-template <int KDT, int NCG, int NW, bool STREAM>
+// BSCALE: the cache carries per-(block, KV head) scales (int4 always, fp8
+// optionally); the kernel without them keeps the registers their products take.
+template <int KDT, int NCG, int NW, bool STREAM, bool BSCALE>
 __device__ __forceinline__ void partition_item(const Args& a, int group, int s, int kvh, int part, int qb) {
   using M = Mfma<KDT>;
   using op_t = typename M::op_t;
   using kload_t = typename M::kload_t;
   using vload_t = typename M::vload_t;
   constexpr int BS = kBlockSize;
-  constexpr int64_t kRowBytes = BS * M::kElem;             // one head_dim row of a block tile
+  constexpr int64_t kRowBytes = BS * M::kBits / 8;         // one head_dim row of a block tile
 
   const int L = clamp_len(a, s);
   const int QL = a.q_len;
@@ -276,7 +326,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   const int ktok = 8 * ((n >> 2) & 1) + 4 * (n & 1);
   // Byte offsets inside a block tile of this KV head.
   const int64_t head_off = (int64_t)kvh * kD * kRowBytes;
-  const int64_t blk_bytes = a.block_stride * M::kElem;
+  const int64_t blk_bytes = a.block_stride * M::kBits / 8;
   const char* kbase = static_cast<const char*>(a.k) + head_off;
   const char* vbase = static_cast<const char*>(a.v) + head_off;
   const int32_t* table = a.tables + (int64_t)s * a.max_blocks;
@@ -312,8 +362,8 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   // (one wave per SIMD: the next tile's K copy then overlaps this tile's
   // compute at no register cost). Four bf16 groups have no registers left
   // for the staged loop and load K directly.
-  constexpr bool kLdsK = M::kElem == 1 || NCG == 2;
-  constexpr int kTileBlk = kD * kBlockSize * M::kElem;   // one block tile of one KV head
+  constexpr bool kLdsK = M::kBits < 16 || NCG == 2;
+  constexpr int kTileBlk = kD * kRowBytes;   // one block tile of one KV head
   constexpr int kSlotBlk = kTileBlk + 64;
   __shared__ __attribute__((aligned(16))) uint8_t k_lds[kLdsK ? NW : 1][kLdsK ? 4 * kSlotBlk : 16];
   // One tile's K and V registers.
@@ -335,7 +385,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int d = 32 * ks + 4 * i + c;
-        T.kr[ks][i] = ld(reinterpret_cast<const kload_t*>(kbase + kb_off + d * kRowBytes + ktok * M::kElem));
+        T.kr[ks][i] = ld(reinterpret_cast<const kload_t*>(kbase + kb_off + d * kRowBytes + ktok * M::kBits / 8));
       }
     }
   };
@@ -346,7 +396,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const int d = 16 * dt + n;
-        T.vr[dt][hh] = ld(reinterpret_cast<const vload_t*>(vbase + vb_offs[hh] + d * kRowBytes + 8 * (c & 1) * M::kElem));
+        T.vr[dt][hh] = ld(reinterpret_cast<const vload_t*>(vbase + vb_offs[hh] + d * kRowBytes + 8 * (c & 1) * M::kBits / 8));
       }
     }
   };
@@ -370,7 +420,11 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   };
   // ---- online softmax of column group cg over this tile; P leaves as two
   // 16-bit PV operands per instruction hh (rounded weight and its residual)
-  auto softmax = [&](const int cg, const f32x4 (&sg)[4], const int t0, op_t (&phi)[2], op_t (&plo)[2])
+  // ksc[x] / vsc[x]: per-block K / V scale of the tile's block (c >> 1) + 2x
+  // (1 without per-block scales); quartets r = 2x, 2x + 1 and PV instruction x
+  // of this lane lie in that block.
+  auto softmax = [&](const int cg, const f32x4 (&sg)[4], const int t0, op_t (&phi)[2], op_t (&plo)[2],
+                     const float (&ksc)[2], const float (&vsc)[2])
       __attribute__((always_inline)) {
     const int nval = min(tok1, lim[cg]) - t0;   // this column's tokens in the tile (may be <= 0)
     float sc[4][4];                             // [r][j]; tokens outside the window: -inf
@@ -380,7 +434,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
       const int tt = 16 * ((c >> 1) + 2 * (r >> 1)) + 8 * (c & 1) + 4 * (r & 1);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        sc[r][j] = (tt + j < nval) ? sg[j][r] * a.score_scale : -INFINITY;
+        sc[r][j] = (tt + j < nval) ? sg[j][r] * (a.score_scale * ksc[r >> 1]) : -INFINITY;
         tmax = fmaxf(tmax, sc[r][j]);
       }
     }
@@ -411,7 +465,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     for (int hh = 0; hh < 2; ++hh) {
       float pv[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pv[i] = p[2 * hh + (i >> 2)][i & 3];
+      for (int i = 0; i < 8; ++i) pv[i] = p[2 * hh + (i >> 2)][i & 3] * vsc[hh];
       M::p_operands(pv, phi[hh], plo[hh]);
     }
   };
@@ -433,16 +487,17 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   // then softmax and O^T += V P^T. With V operands used as loaded (bf16) each
   // column group's PV follows its softmax, so only one group's P is live;
   // widened fp8 V operands are instead shared by all groups' MFMAs.
-  auto tile_step = [&](Tile& T, const int t0, auto&& after_qk) __attribute__((always_inline)) {
+  auto tile_step = [&](Tile& T, const int t0, auto&& after_qk, const float (&ksc)[2], const float (&vsc)[2])
+      __attribute__((always_inline)) {
     f32x4 sacc[NCG][4];
     qk(T, sacc);
     after_qk();
     mask_tail(T, t0);
-    if constexpr (M::kElem == 2) {
+    if constexpr (M::kBits == 16) {
 #pragma unroll
       for (int cg = 0; cg < NCG; ++cg) {
         op_t phi[2], plo[2];
-        softmax(cg, sacc[cg], t0, phi, plo);
+        softmax(cg, sacc[cg], t0, phi, plo, ksc, vsc);
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
 #pragma unroll
@@ -456,7 +511,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     } else {
       op_t phi[NCG][2], plo[NCG][2];
 #pragma unroll
-      for (int cg = 0; cg < NCG; ++cg) softmax(cg, sacc[cg], t0, phi[cg], plo[cg]);
+      for (int cg = 0; cg < NCG; ++cg) softmax(cg, sacc[cg], t0, phi[cg], plo[cg], ksc, vsc);
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
 #pragma unroll
@@ -489,7 +544,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     typedef __attribute__((address_space(3))) void* lds_ptr_t;
     typedef __attribute__((address_space(1))) void* gbl_ptr_t;
     uint8_t* kslot = &k_lds[wave][0];
-    const uint8_t* krow = kslot + kblk * kSlotBlk + (c * kBlockSize + ktok) * M::kElem;   // + row bytes * (32 ks + 4 i)
+    const uint8_t* krow = kslot + kblk * kSlotBlk + c * kRowBytes + ktok * M::kBits / 8;   // + row bytes * (32 ks + 4 i)
     const int last_blk = nblk_part - 1;
     auto ids_at = [&](int t, int32_t (&ib)[4]) __attribute__((always_inline)) {
       const int b0 = min(t / BS, last_blk);
@@ -510,16 +565,35 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     auto load_v_ids = [&](Tile& T, const int32_t (&ib)[4]) __attribute__((always_inline)) {
       load_v(T, (c >> 1) == 0 ? ib[0] : ib[1], (c >> 1) == 0 ? ib[2] : ib[3]);
     };
+    // Per-block scales of a tile (the same for the whole wave), then this
+    // lane's two: block (c >> 1) + 2x for x = 0, 1.
+    constexpr bool bscaled = BSCALE;
+    auto uniform_f = [](float x) __attribute__((always_inline)) {   // keep wave-uniform values in scalar registers
+      return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+    };
+    auto scales_at = [&](const int32_t (&ib)[4], float (&kb)[4], float (&vb)[4]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        const int64_t at = (int64_t)__builtin_amdgcn_readfirstlane(ib[blk]) * a.num_kv_heads + kvh;
+        kb[blk] = bscaled ? uniform_f(a.k_bscale[at]) : 1.f;
+        vb[blk] = bscaled ? uniform_f(a.v_bscale[at]) : 1.f;
+      }
+    };
     if (first < tok1) {
       Tile T;
       int32_t icur[4], inext[4];
+      float kb_cur[4], vb_cur[4], kb_next[4], vb_next[4];
       ids_at(first, icur);
       ids_at(first + kStride, inext);
+      scales_at(icur, kb_cur, vb_cur);
       load_k_lds(icur);
       load_v_ids(T, icur);
       __builtin_amdgcn_sched_barrier(0);
       for (int t0 = first; t0 < tok1; t0 += kStride) {
         const bool more = t0 + kStride < tok1;
+        scales_at(inext, kb_next, vb_next);   // the next tile's, a tile ahead of use
+        const float ksc[2] = {(c >> 1) == 0 ? kb_cur[0] : kb_cur[1], (c >> 1) == 0 ? kb_cur[2] : kb_cur[3]};
+        const float vsc[2] = {(c >> 1) == 0 ? vb_cur[0] : vb_cur[1], (c >> 1) == 0 ? vb_cur[2] : vb_cur[3]};
         // The K copy into LDS is a vector-memory operation: wait for every
         // outstanding one (vmcnt 0) before reading the slot. The compiler's own
         // wait insertion does not cover LDS written this way in every
@@ -530,7 +604,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
         for (int ks = 0; ks < kKSteps; ++ks) {
 #pragma unroll
           for (int i = 0; i < 8; ++i)
-            T.kr[ks][i] = *reinterpret_cast<const kload_t*>(krow + (32 * ks + 4 * i) * kBlockSize * M::kElem);
+            T.kr[ks][i] = *reinterpret_cast<const kload_t*>(krow + (32 * ks + 4 * i) * kRowBytes);
         }
         tile_step(T, t0, [&]() __attribute__((always_inline)) {
           __builtin_amdgcn_sched_barrier(0);
@@ -539,12 +613,16 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
             load_k_lds(inext);
           }
           __builtin_amdgcn_sched_barrier(0);
-        });
+        }, ksc, vsc);
         __builtin_amdgcn_sched_barrier(0);
         if (more) load_v_ids(T, inext);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) inext[blk] = icur[blk];
+        for (int blk = 0; blk < 4; ++blk) {
+          inext[blk] = icur[blk];
+          kb_cur[blk] = kb_next[blk];
+          vb_cur[blk] = vb_next[blk];
+        }
       }
     }
   } else {
@@ -555,7 +633,8 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
       // tile are in flight before any compute is scheduled.
       if (t0 + kStride < tok1) tile_ids((t0 + kStride) / BS, idk, idv0, idv1);
       __builtin_amdgcn_sched_barrier(0);
-      tile_step(T, t0, []() __attribute__((always_inline)) {});
+      constexpr float kOnes[2] = {1.f, 1.f};
+      tile_step(T, t0, []() __attribute__((always_inline)) {}, kOnes, kOnes);
     }
   }
 
@@ -653,24 +732,24 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NCG == 1 ? 2 : 1, 8)))
 
 // Grid schedule: one workgroup per (KV head, sequence, partition) of the dense grid.
-template <int KDT, int NCG, int NW, bool STREAM>
+template <int KDT, int NCG, int NW, bool STREAM, bool BSCALE>
 PA_MFMA_KERNEL_ATTRS void mfma_partition_kernel(const Args a, int group) {
   const Item it = work_item(a);
-  partition_item<KDT, NCG, NW, STREAM>(a, group, it.s, it.kvh, it.part, it.qb);
+  partition_item<KDT, NCG, NW, STREAM, BSCALE>(a, group, it.s, it.kvh, it.part, it.qb);
 }
 
 // List schedule: workgroup i takes item i of the list the plan kernel built,
 // longest first, and workgroups past its end exit at once. Workgroups are
 // dispatched in index order, so long items start first and short ones fill
 // the end; consecutive (similar) items go to consecutive XCDs.
-template <int KDT, int NCG, int NW, bool STREAM>
+template <int KDT, int NCG, int NW, bool STREAM, bool BSCALE>
 PA_MFMA_KERNEL_ATTRS void mfma_partition_list_kernel(const Args a, int group) {
   const int idx = blockIdx.x;
   if (idx >= *a.queue_len) return;
   const int2 w = a.queue_items[idx];            // unit (s * q_blocks + qb) * Hkv + kvh, partition
   const int sq = w.x / a.num_kv_heads;
   const int s = sq / a.q_blocks;
-  partition_item<KDT, NCG, NW, STREAM>(a, group, s, w.x - sq * a.num_kv_heads, w.y, sq - s * a.q_blocks);
+  partition_item<KDT, NCG, NW, STREAM, BSCALE>(a, group, s, w.x - sq * a.num_kv_heads, w.y, sq - s * a.q_blocks);
 }
 
 }  // namespace
@@ -682,9 +761,42 @@ bool mfma_waves_supported(int ncg, int nw) {
 }
 
 bool mfma_supported(int q_dtype, int kv_dtype, int head_dim, int group, int block_size, int q_len) {
-  return q_dtype == kBF16 && (kv_dtype == kBF16 || kv_dtype == kE5M2 || kv_dtype == kE4M3) && head_dim == kD &&
+  return q_dtype == kBF16 && (kv_dtype == kBF16 || kv_dtype == kE5M2 || kv_dtype == kE4M3 || kv_dtype == kI4) &&
+         head_dim == kD &&
          block_size == kBlockSize && group >= 1 && q_len >= 1 && q_len <= kMaxQueryLen;
 }
+
+namespace {
+
+template <int KDT, int NCG, int NW, bool ST, bool BS>
+void launch_one(const Args& a, int group, dim3 grid, bool queue, hipStream_t stream) {
+  if (queue) mfma_partition_list_kernel<KDT, NCG, NW, ST, BS><<<grid, 64 * NW, 0, stream>>>(a, group);
+  else mfma_partition_kernel<KDT, NCG, NW, ST, BS><<<grid, 64 * NW, 0, stream>>>(a, group);
+}
+
+template <int KDT, int NCG, int NW, bool ST>
+void launch_scaled(const Args& a, int group, dim3 grid, bool queue, hipStream_t stream) {
+  if constexpr (KDT == kBF16) launch_one<KDT, NCG, NW, ST, false>(a, group, grid, queue, stream);
+  else if constexpr (KDT == kI4) launch_one<KDT, NCG, NW, ST, true>(a, group, grid, queue, stream);
+  else if (a.k_bscale != nullptr) launch_one<KDT, NCG, NW, ST, true>(a, group, grid, queue, stream);
+  else launch_one<KDT, NCG, NW, ST, false>(a, group, grid, queue, stream);
+}
+
+template <int KDT>
+void launch_kdt(const Args& a, int group, int ncg, int nw, dim3 grid, bool queue, hipStream_t stream) {
+  const bool st = a.q_blocks == 1;   // several query blocks: share tiles through the caches
+  if (ncg == 1 && nw == 1) launch_scaled<KDT, 1, 1, true>(a, group, grid, queue, stream);
+  else if (ncg == 1 && nw == 2) launch_scaled<KDT, 1, 2, true>(a, group, grid, queue, stream);
+  else if (ncg == 1) launch_scaled<KDT, 1, 4, true>(a, group, grid, queue, stream);
+  else if (ncg == 2 && nw == 1) launch_scaled<KDT, 2, 1, true>(a, group, grid, queue, stream);
+  else if (ncg == 2) launch_scaled<KDT, 2, 2, true>(a, group, grid, queue, stream);
+  else if (nw == 1 && st) launch_scaled<KDT, 4, 1, true>(a, group, grid, queue, stream);
+  else if (nw == 1) launch_scaled<KDT, 4, 1, false>(a, group, grid, queue, stream);
+  else if (st) launch_scaled<KDT, 4, 2, true>(a, group, grid, queue, stream);
+  else launch_scaled<KDT, 4, 2, false>(a, group, grid, queue, stream);
+}
+
+}  // namespace
 
 hipError_t launch_mfma(const Args& a, int q_dtype, int kv_dtype, int head_dim, int group,
                        hipStream_t stream) {
@@ -692,33 +804,17 @@ hipError_t launch_mfma(const Args& a, int q_dtype, int kv_dtype, int head_dim, i
   const int gv = group * a.q_len;                 // virtual heads per KV head, in blocks of up to 64
   const int ncg = gv <= 16 ? 1 : gv <= 32 ? 2 : 4;
   if (a.q_blocks != (gv + 16 * kMaxColumnGroups - 1) / (16 * kMaxColumnGroups)) return hipErrorInvalidValue;
+  if ((kv_dtype == kI4) != (a.k_bscale != nullptr && a.v_bscale != nullptr) && kv_dtype != kE5M2 &&
+      kv_dtype != kE4M3)
+    return hipErrorInvalidValue;                  // int4 needs both scale arrays; bf16 takes none
   const bool queue = a.queue_items != nullptr;
   const dim3 grid = queue ? dim3((unsigned)a.queue_workgroups) : partition_grid(a);   // list: one per possible item
   const int nw = a.waves_per_item;
   if (!mfma_waves_supported(ncg, nw)) return hipErrorInvalidValue;
-  const bool stream_kv = a.q_blocks == 1;         // several query blocks: share tiles through the caches
-#define PA_LAUNCH4(KDT, NCG, NW, ST)                                                                   \
-  do {                                                                                                 \
-    if (queue) mfma_partition_list_kernel<KDT, NCG, NW, ST><<<grid, 64 * NW, 0, stream>>>(a, group);   \
-    else mfma_partition_kernel<KDT, NCG, NW, ST><<<grid, 64 * NW, 0, stream>>>(a, group);              \
-  } while (0)
-#define PA_LAUNCH(KDT)                                                            \
-  do {                                                                            \
-    if (ncg == 1 && nw == 1) PA_LAUNCH4(KDT, 1, 1, true);                         \
-    else if (ncg == 1 && nw == 2) PA_LAUNCH4(KDT, 1, 2, true);                    \
-    else if (ncg == 1) PA_LAUNCH4(KDT, 1, 4, true);                               \
-    else if (ncg == 2 && nw == 1) PA_LAUNCH4(KDT, 2, 1, true);                    \
-    else if (ncg == 2) PA_LAUNCH4(KDT, 2, 2, true);                               \
-    else if (nw == 1 && stream_kv) PA_LAUNCH4(KDT, 4, 1, true);                   \
-    else if (nw == 1) PA_LAUNCH4(KDT, 4, 1, false);                               \
-    else if (stream_kv) PA_LAUNCH4(KDT, 4, 2, true);                              \
-    else PA_LAUNCH4(KDT, 4, 2, false);                                            \
-  } while (0)
-  if (kv_dtype == kBF16) PA_LAUNCH(kBF16);
-  else if (kv_dtype == kE5M2) PA_LAUNCH(kE5M2);
-  else PA_LAUNCH(kE4M3);
-#undef PA_LAUNCH
-#undef PA_LAUNCH4
+  if (kv_dtype == kBF16) launch_kdt<kBF16>(a, group, ncg, nw, grid, queue, stream);
+  else if (kv_dtype == kE5M2) launch_kdt<kE5M2>(a, group, ncg, nw, grid, queue, stream);
+  else if (kv_dtype == kE4M3) launch_kdt<kE4M3>(a, group, ncg, nw, grid, queue, stream);
+  else launch_kdt<kI4>(a, group, ncg, nw, grid, queue, stream);
   return hipGetLastError();
 }
 

@@ -4,6 +4,7 @@ any HIP call. No call here reaches a kernel launch."""
 
 import ctypes
 import os
+import subprocess
 import re
 
 import pytest
@@ -92,6 +93,19 @@ def status_of(d, hkv=8):
     (dict(waves_per_item=4, q_len=4), 8, B.PA_ERR_UNSUPPORTED),  # 4 waves with one column group only
     (dict(waves_per_item=2, kernel=1), 8, B.PA_ERR_UNSUPPORTED),
     (dict(waves_per_item=4), 8, B.PA_OK),
+    # int4 cache and per-(block, KV head) scales
+    (dict(kv_dtype=B.PA_DTYPE_INT4, k_block_scales=4096, v_block_scales=8192), 8, B.PA_OK),
+    (dict(kv_dtype=B.PA_DTYPE_INT4), 8, B.PA_ERR_NULL),                          # scales required
+    (dict(kv_dtype=B.PA_DTYPE_INT4, k_block_scales=4096), 8, B.PA_ERR_NULL),     # both or neither
+    (dict(kv_dtype=B.PA_DTYPE_INT4, k_block_scales=4098, v_block_scales=8192), 8, B.PA_ERR_ALIGN),
+    (dict(kv_dtype=B.PA_DTYPE_INT4, k_block_scales=4096, v_block_scales=8192, kernel=1), 8, B.PA_ERR_UNSUPPORTED),
+    (dict(kv_dtype=B.PA_DTYPE_INT4, k_block_scales=4096, v_block_scales=8192, head_dim=64), 8,
+     B.PA_ERR_UNSUPPORTED),
+    (dict(kv_dtype=B.PA_DTYPE_INT4, k_block_scales=4096, v_block_scales=8192, q_len=4), 8, B.PA_OK),
+    (dict(k_block_scales=4096, v_block_scales=8192), 8, B.PA_ERR_UNSUPPORTED),  # bf16 takes no scales
+    (dict(kv_dtype=B.PA_DTYPE_FP8_E5M2, k_block_scales=4096, v_block_scales=8192), 8, B.PA_OK),
+    (dict(kv_dtype=B.PA_DTYPE_FP8_E5M2, k_block_scales=4096, v_block_scales=8192, kernel=1), 8,
+     B.PA_ERR_UNSUPPORTED),                                                      # vector kernel: no block scales
 ])
 def test_validation_statuses(kw, hkv, expect):
     assert status_of(dims(**kw), hkv) == expect
@@ -200,9 +214,19 @@ def _append(d, n=4, in_dtype=B.PA_DTYPE_BF16, ptrs=(256,) * 7, hkv=8):
     (dict(k_scale=2.0), B.PA_DTYPE_BF16, B.PA_ERR_UNSUPPORTED),       # scales only for fp8 caches
     (dict(kv_dtype=B.PA_DTYPE_FP8_E5M2, v_scale=0.0), B.PA_DTYPE_BF16, B.PA_ERR_SHAPE),
     (dict(num_blocks=0), B.PA_DTYPE_BF16, B.PA_ERR_SHAPE),
+    (dict(kv_dtype=B.PA_DTYPE_INT4), B.PA_DTYPE_BF16, B.PA_ERR_NULL),             # int4 needs its scales
+    (dict(kv_dtype=B.PA_DTYPE_BF16, k_block_scales=4096, v_block_scales=8192), B.PA_DTYPE_BF16,
+     B.PA_ERR_UNSUPPORTED),
 ])
 def test_append_validation(kw, in_dtype, expect):
     assert _append(cdims(**kw), in_dtype=in_dtype) == expect
+
+
+@pytest.mark.parametrize("in_dtype", [B.PA_DTYPE_BF16, B.PA_DTYPE_F32])
+def test_append_int4_accepted(in_dtype):
+    # valid arguments with no token to write: every check runs, nothing is launched
+    d = cdims(kv_dtype=B.PA_DTYPE_INT4, k_block_scales=4096, v_block_scales=8192)
+    assert _append(d, n=0, in_dtype=in_dtype) == B.PA_OK
 
 
 def test_append_pointer_checks_and_empty_call():
@@ -223,3 +247,27 @@ def test_copy_blocks_validation():
     assert call(2, (256, 0, 256, 256)) == B.PA_ERR_NULL
     assert call(2, (256, 256, 258, 256)) == B.PA_ERR_ALIGN
     assert call(2, (256,) * 4, hkv=0) == B.PA_ERR_SHAPE
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """ctypes mirrors of pa_dims_t / pa_plan_t: sizes and the offsets of the fields
+    after which padding could differ, as the C compiler lays them out."""
+    src = tmp_path / "layout.c"
+    src.write_text("""
+#include <stddef.h>
+#include <stdio.h>
+#include "pa_decode.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu %zu\\n", sizeof(pa_dims_t), offsetof(pa_dims_t, waves_per_item),
+         offsetof(pa_dims_t, k_block_scales), offsetof(pa_dims_t, v_block_scales), sizeof(pa_plan_t),
+         offsetof(pa_plan_t, workspace_bytes));
+  return 0;
+}
+""")
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run(["gcc", "-I", inc, str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    exp = [ctypes.sizeof(B.PaDims), B.PaDims.waves_per_item.offset, B.PaDims.k_block_scales.offset,
+           B.PaDims.v_block_scales.offset, ctypes.sizeof(B.PaPlan), B.PaPlan.workspace_bytes.offset]
+    assert got == exp

@@ -21,6 +21,8 @@ def _to_dev(bits, dtype):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
     if dtype == "e4m3":
         return torch.from_numpy(np.ascontiguousarray(bits)).view(torch.float8_e4m3fn).cuda()
+    if dtype == "int4":
+        return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint8)).cuda()
     return torch.from_numpy(np.ascontiguousarray(bits)).view(torch.float8_e5m2).cuda()
 
 
@@ -154,3 +156,105 @@ def test_append_then_decode(kv_dtype):
     got = out.float().cpu().numpy().astype(np.float64)
     wk = W.workload_from_arrays("appended", w.q, k2, v2, tables, new_lens, Hkv, "bf16", kv_dtype)
     check(got, ref, wk, f"append+decode {kv_dtype}")
+
+
+# ---------------------------------------------------------------------- int4 --
+
+def _scales_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
+def test_int4_append_byte_exact(in_dtype):
+    """Bulk append: 40 consecutive tokens of one sequence (two per byte, eight per
+    word, written concurrently), one token for each of the others, padding
+    entries; values at exact ties, beyond the code range, infinite and NaN."""
+    rng = np.random.default_rng([31, len(in_dtype)])
+    S, Hkv, D = 6, 2, 128
+    w = W.random_edge_workload(41, S=S, H=8, Hkv=Hkv, D=D, seq_lens=[0, 5, 17, 32, 100, 3], kv_dtype="int4",
+                               extra_pool=30)
+    w.k_block_scales[:] = 0.25
+    w.v_block_scales[:] = np.exp2(rng.integers(-3, 0, w.v_block_scales.shape)).astype(np.float32)
+    need = (w.seq_lens + 40 + 15) // 16
+    tables = np.zeros((S, int(need.max())), np.int32)
+    tables[:, :w.block_tables.shape[1]] = w.block_tables
+    used = set(np.concatenate([w.block_tables[s, :(w.seq_lens[s] + 15) // 16] for s in range(S)]).tolist())
+    free = [b for b in range(w.num_blocks) if b not in used]
+    for s_ in range(S):
+        for j in range((w.seq_lens[s_] + 15) // 16, need[s_]):
+            tables[s_, j] = free.pop()
+    token_seq = np.concatenate([np.zeros(40, np.int32), np.arange(1, S, dtype=np.int32), [2, 4]]).astype(np.int32)
+    token_pos = np.concatenate([np.arange(40), w.seq_lens[1:], [-1, -7]]).astype(np.int32)
+    n = len(token_seq)
+    x = rng.standard_normal((n, Hkv, D)).astype(np.float32)
+    flat = x.reshape(-1)
+    ties = (np.arange(-9, 9) + 0.5) * 0.25
+    extra = np.concatenate([ties, [1e6, -1e6, np.inf, -np.inf, np.nan, 2.0, -2.0, 1.875, -2.125, 0.0, -0.0]])
+    flat[rng.permutation(flat.size)[:len(extra)]] = extra
+    kn = x if in_dtype == "f32" else W.to_storage(x, "bf16")
+    vn = W.to_storage(rng.standard_normal((n, Hkv, D)).astype(np.float32), in_dtype) if in_dtype == "bf16" \
+        else rng.standard_normal((n, Hkv, D)).astype(np.float32)
+    k_ref, v_ref = O.paged_append(kn, vn, w.k_cache, w.v_cache, tables, token_seq, token_pos, in_dtype, "int4",
+                                  k_block_scales=w.k_block_scales, v_block_scales=w.v_block_scales)
+    kd, vd = _to_dev(w.k_cache, "int4"), _to_dev(w.v_cache, "int4")
+    log(f"case int4 append from {in_dtype}")
+    B.pa_cache_append(_to_dev(kn, in_dtype), _to_dev(vn, in_dtype), kd, vd, torch.from_numpy(tables).cuda(),
+                      torch.from_numpy(token_seq).cuda(), torch.from_numpy(token_pos).cuda(),
+                      k_block_scales=_scales_dev(w.k_block_scales), v_block_scales=_scales_dev(w.v_block_scales))
+    torch.cuda.synchronize()
+    assert np.array_equal(kd.cpu().numpy(), k_ref)
+    assert np.array_equal(vd.cpu().numpy(), v_ref)
+
+
+def test_int4_copy_blocks_with_scales():
+    w = W.make_workload("c2", num_seqs=8, kv_dtype="int4")
+    rng = np.random.default_rng(32)
+    perm = rng.permutation(w.num_blocks)
+    src, dst = perm[:9].astype(np.int32), perm[9:18].astype(np.int32)
+    k_ref, v_ref, ks_ref, vs_ref = O.copy_blocks(w.k_cache, w.v_cache, src, dst, w.k_block_scales, w.v_block_scales)
+    kd, vd = _to_dev(w.k_cache, "int4"), _to_dev(w.v_cache, "int4")
+    ksd, vsd = _scales_dev(w.k_block_scales), _scales_dev(w.v_block_scales)
+    B.pa_cache_copy_blocks(kd, vd, torch.from_numpy(src).cuda(), torch.from_numpy(dst).cuda(),
+                           k_block_scales=ksd, v_block_scales=vsd)
+    torch.cuda.synchronize()
+    assert np.array_equal(kd.cpu().numpy(), k_ref) and np.array_equal(vd.cpu().numpy(), v_ref)
+    assert np.array_equal(ksd.cpu().numpy(), ks_ref) and np.array_equal(vsd.cpu().numpy(), vs_ref)
+
+
+def test_int4_append_then_decode():
+    rng = np.random.default_rng(33)
+    S, H, Hkv, D = 16, 64, 8, 128
+    lens = rng.integers(1, 600, S)
+    lens[0] = 16 * 7
+    w = W.random_edge_workload(34, S=S, H=H, Hkv=Hkv, D=D, seq_lens=lens.tolist(), kv_dtype="int4", extra_pool=40)
+    need = (w.seq_lens + 1 + 15) // 16
+    tables = np.zeros((S, int(need.max())), np.int32)
+    tables[:, :w.block_tables.shape[1]] = w.block_tables
+    used = set(np.concatenate([w.block_tables[s, :(w.seq_lens[s] + 15) // 16] for s in range(S)]).tolist())
+    free = [b for b in range(w.num_blocks) if b not in used]
+    for s_ in range(S):
+        if w.seq_lens[s_] % 16 == 0:
+            tables[s_, w.seq_lens[s_] // 16] = free.pop()
+    kn = W.to_storage(rng.standard_normal((S, Hkv, D)).astype(np.float32), "bf16")
+    vn = W.to_storage(rng.standard_normal((S, Hkv, D)).astype(np.float32), "bf16")
+    token_seq = np.arange(S, dtype=np.int32)
+    token_pos = w.seq_lens.astype(np.int32)
+    k2, v2 = O.paged_append(kn, vn, w.k_cache, w.v_cache, tables, token_seq, token_pos, "bf16", "int4",
+                            k_block_scales=w.k_block_scales, v_block_scales=w.v_block_scales)
+    new_lens = (w.seq_lens + 1).astype(np.int32)
+    ref = O.paged_decode(w.q, k2, v2, tables, new_lens, Hkv, w.scale, "bf16", "int4",
+                         k_block_scales=w.k_block_scales, v_block_scales=w.v_block_scales)
+    kd, vd = _to_dev(w.k_cache, "int4"), _to_dev(w.v_cache, "int4")
+    ksd, vsd = _scales_dev(w.k_block_scales), _scales_dev(w.v_block_scales)
+    td = torch.from_numpy(tables).cuda()
+    B.pa_cache_append(_to_dev(kn, "bf16"), _to_dev(vn, "bf16"), kd, vd, td, torch.from_numpy(token_seq).cuda(),
+                      torch.from_numpy(token_pos).cuda(), k_block_scales=ksd, v_block_scales=vsd)
+    q = _to_dev(w.q, "bf16")
+    out = torch.empty_like(q)
+    B.pa_decode(q, kd, vd, td, torch.from_numpy(new_lens).cuda(), Hkv, float(w.scale), out,
+                max_seq_len=int(new_lens.max()), k_block_scales=ksd, v_block_scales=vsd)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    wk = W.workload_from_arrays("appended", w.q, k2, v2, tables, new_lens, Hkv, "bf16", "int4",
+                                k_block_scales=w.k_block_scales, v_block_scales=w.v_block_scales)
+    check(got, ref, wk, "append+decode int4")

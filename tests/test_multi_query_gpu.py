@@ -153,3 +153,27 @@ def test_prefill_chunk():
                 max_seq_len=int(w.seq_lens[0]))
     torch.cuda.synchronize()
     check(out.float().cpu().numpy().astype(np.float64), ref, w, "prefill chunk")
+
+
+@pytest.mark.parametrize("ql", [2, 4, 8, 12])
+def test_multi_query_int4(ql):
+    """int4 cache with per-block scales, 1, 2 and 4 column groups and two query blocks."""
+    w = W.make_workload("c2", num_seqs=5, kv_dtype="int4")
+    rng = np.random.default_rng([ql, 95])
+    q = W.to_storage(rng.standard_normal((w.num_seqs, ql, w.num_heads, w.head_dim), dtype=np.float32), "bf16")
+    ref = np.concatenate([O.paged_attention_multi(q[s:s + 1], w.k_cache, w.v_cache, w.block_tables[s:s + 1],
+                                                  w.seq_lens[s:s + 1], w.num_kv_heads, w.scale, "bf16", "int4",
+                                                  k_block_scales=w.k_block_scales, v_block_scales=w.v_block_scales)
+                          for s in range(w.num_seqs)])
+    qd = _dev(q, "bf16")
+    sc = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    kd = torch.from_numpy(np.ascontiguousarray(w.k_cache)).cuda()
+    vd = torch.from_numpy(np.ascontiguousarray(w.v_cache)).cuda()
+    for ptok in (0, 128):
+        out = torch.full_like(qd, float("nan"))
+        log(f"case multi-query int4 q_len={ql} P={ptok}")
+        B.pa_decode(qd, kd, vd, torch.from_numpy(w.block_tables).cuda(), torch.from_numpy(w.seq_lens).cuda(),
+                    w.num_kv_heads, float(w.scale), out, partition_tokens=ptok, max_seq_len=w.max_seq_len,
+                    k_block_scales=sc(w.k_block_scales), v_block_scales=sc(w.v_block_scales))
+        torch.cuda.synchronize()
+        check(out.float().cpu().numpy().astype(np.float64), ref, w, f"multi-query int4 q_len={ql} P={ptok}")

@@ -20,19 +20,21 @@ pytestmark = pytest.mark.gpu
 
 
 def kernels_for(w):
+    """Kernels that take this batch (planning only reads the scale pointers' presence)."""
     ks = []
+    sc = dict(k_block_scales=4096, v_block_scales=8192) if w.k_block_scales is not None else {}
     try:
         B.plan(B.PaDims(num_seqs=w.num_seqs, num_heads=w.num_heads, head_dim=w.head_dim, num_blocks=w.num_blocks,
                         block_size=w.block_size, max_blocks_per_seq=w.max_blocks_per_seq,
                         q_dtype=B._KV_NAMES[w.q_dtype], kv_dtype=B._KV_NAMES[w.kv_dtype], k_scale=1.0, v_scale=1.0,
-                        max_seq_len=0, partition_tokens=0, kernel=B.KERNELS["valu"]), w.num_kv_heads)
+                        max_seq_len=0, partition_tokens=0, kernel=B.KERNELS["valu"], **sc), w.num_kv_heads)
         ks.append("valu")
     except B.PagedAttentionError:
         pass
     dims = B.PaDims(num_seqs=w.num_seqs, num_heads=w.num_heads, head_dim=w.head_dim, num_blocks=w.num_blocks,
                     block_size=w.block_size, max_blocks_per_seq=w.max_blocks_per_seq,
                     q_dtype=B._KV_NAMES[w.q_dtype], kv_dtype=B._KV_NAMES[w.kv_dtype], k_scale=1.0, v_scale=1.0,
-                    max_seq_len=0, partition_tokens=0, kernel=B.KERNELS["mfma"])
+                    max_seq_len=0, partition_tokens=0, kernel=B.KERNELS["mfma"], **sc)
     try:
         B.plan(dims, w.num_kv_heads)
         ks.append("mfma")
@@ -43,7 +45,9 @@ def kernels_for(w):
 
 SMALL = [("c1", {}), ("c2", dict(num_seqs=12)), ("c3", dict(num_seqs=2, seq_len=3000)),
          ("c4", dict(num_seqs=20, seq_len=5000)), ("c5", dict(num_seqs=4, seq_len=2100)),
-         ("c5", dict(num_seqs=4, seq_len=2100, kv_dtype="e4m3"))]
+         ("c5", dict(num_seqs=4, seq_len=2100, kv_dtype="e4m3")),
+         ("c2", dict(num_seqs=12, kv_dtype="int4")), ("c3", dict(num_seqs=2, seq_len=3000, kv_dtype="int4")),
+         ("c4", dict(num_seqs=20, seq_len=5000, kv_dtype="int4"))]
 
 
 @pytest.mark.parametrize("name,kw", SMALL, ids=[s[0] + s[1].get("kv_dtype", "") for s in SMALL])
@@ -71,6 +75,8 @@ EDGE = [
     ("e5m2 G8 D128", dict(S=5, H=16, Hkv=2, D=128, seq_lens=[1, 16, 17, 64, 333], kv_dtype="e5m2")),
     ("e5m2 G4 D64", dict(S=3, H=8, Hkv=2, D=64, seq_lens=[9, 80, 260], kv_dtype="e5m2")),
     ("e4m3 G8 D128", dict(S=5, H=16, Hkv=2, D=128, seq_lens=[1, 16, 17, 64, 333], kv_dtype="e4m3")),
+    ("int4 G8 D128", dict(S=9, H=16, Hkv=2, D=128, seq_lens=[0, 1, 15, 16, 17, 63, 64, 65, 333], kv_dtype="int4")),
+    ("int4 G3 D128", dict(S=3, H=6, Hkv=2, D=128, seq_lens=[7, 64, 450], kv_dtype="int4")),
     ("e4m3 G4 D64", dict(S=3, H=8, Hkv=2, D=64, seq_lens=[9, 80, 260], kv_dtype="e4m3")),
 ]
 
@@ -100,7 +106,8 @@ def test_library_workspace_path_matches_caller_workspace():
 
 @pytest.mark.parametrize("name,kw", [("c1", {}), ("c2", dict(num_seqs=8)), ("c4", dict(num_seqs=12, seq_len=3000)),
                                      ("c5", dict(num_seqs=3, seq_len=1500)),
-                                     ("c5", dict(num_seqs=3, seq_len=1500, kv_dtype="e4m3"))])
+                                     ("c5", dict(num_seqs=3, seq_len=1500, kv_dtype="e4m3")),
+                                     ("c4", dict(num_seqs=12, seq_len=3000, kv_dtype="int4"))])
 def test_bitwise_repeat_relabel_poison(name, kw):
     w = W.make_workload(name, **kw)
     wp = W.permute_pool(w, 5)
@@ -188,7 +195,7 @@ def test_queue_schedule_matches_grid(name, kw, ptok):
 
 WAVES = [("c2", dict(num_seqs=12), 512), ("c3", dict(num_seqs=2, seq_len=4100), 0),
          ("c5", dict(num_seqs=6, seq_len=1900), 1024), ("c5", dict(num_seqs=4, seq_len=700, kv_dtype="e4m3"), 0),
-         ("c4", dict(num_seqs=30, seq_len=3000), 256)]
+         ("c4", dict(num_seqs=30, seq_len=3000), 256), ("c5", dict(num_seqs=4, seq_len=900, kv_dtype="int4"), 0)]
 
 
 @pytest.mark.parametrize("name,kw,ptok", WAVES, ids=[f"{c[0]}{c[1].get('kv_dtype', '')}-P{c[2]}" for c in WAVES])
@@ -252,3 +259,56 @@ def test_every_fp8_code_decodes_exactly(kv_dtype):
                 fin = np.isfinite(want[s])
                 assert np.array_equal(got[s, h][fin], want[s][fin]), (kern, s)
                 assert not np.isfinite(got[s, h][~fin]).any(), (kern, s)
+
+
+# ------------------------------------------------------------- int4 / scales --
+
+def test_every_int4_code_decodes_exactly():
+    """One-token sequences return their V row: code * v_block_scale, with power-of-two
+    scales exact in bf16. Rows hold all 16 codes; K codes and scales vary too."""
+    S, H, Hkv, D = 16, 16, 2, 128
+    w = W.random_edge_workload(21, S=S, H=H, Hkv=Hkv, D=D, seq_lens=[1] * S, kv_dtype="int4")
+    rng = np.random.default_rng(22)
+    codes = (np.arange(D)[None, None, :] + np.arange(S)[:, None, None] + np.arange(Hkv)[None, :, None]) % 16 - 8
+    for s_ in range(S):
+        b = int(w.block_tables[s_, 0])
+        for g in range(Hkv):
+            row = O.int4_unpack(w.v_cache[b, g])                     # [D, 16]
+            row[:, 0] = codes[s_, g]
+            w.v_cache[b, g] = O.int4_pack(row)
+    w.v_block_scales[:] = np.exp2(rng.integers(-4, 3, w.v_block_scales.shape)).astype(np.float32)
+    got = run_gpu(w)
+    for s_ in range(S):
+        b = int(w.block_tables[s_, 0])
+        for h in range(H):
+            g = h // (H // Hkv)
+            assert np.array_equal(got[s_, h], codes[s_, g].astype(np.float64) * float(w.v_block_scales[b, g]))
+
+
+@pytest.mark.parametrize("kv_dtype", ["e5m2", "e4m3"])
+def test_fp8_with_block_scales(kv_dtype):
+    """fp8 caches with per-(block, KV head) scales on top of the per-tensor ones."""
+    w = W.make_workload("c5", num_seqs=6, seq_len=1300, kv_dtype=kv_dtype)
+    rng = np.random.default_rng(23)
+    w.k_block_scales = np.exp2(rng.uniform(-2, 2, (w.num_blocks, w.num_kv_heads))).astype(np.float32)
+    w.v_block_scales = np.exp2(rng.uniform(-2, 2, (w.num_blocks, w.num_kv_heads))).astype(np.float32)
+    w.k_scale, w.v_scale = np.float32(0.75), np.float32(1.25)
+    ref = oracle_full(w)
+    dev = upload(w)
+    for ptok, nw in ((0, 0), (256, 2), (64, 4)):
+        log(f"case fp8 block scales {kv_dtype} P={ptok} waves={nw}")
+        check(run_gpu(w, dev, kernel="mfma", partition_tokens=ptok, waves_per_item=nw), ref, w,
+              f"{kv_dtype} block scales P={ptok}")
+
+
+def test_int4_full_size_sampled():
+    """The int4 form of the long-context batch at full size, sampled sequences."""
+    w = W.make_workload("c3", kv_dtype="int4")
+    seqs = [0, 9]
+    rows = [(s_, h) for s_ in seqs for h in range(w.num_heads)]
+    ref = oracle_rows(w, rows).reshape(len(seqs), w.num_heads, w.head_dim)
+    dev = upload(w)
+    log("case full c3 int4 (default plan)")
+    got = run_gpu(w, dev)
+    assert np.isfinite(got).all()
+    check(got[seqs], ref, w, "full c3 int4")
