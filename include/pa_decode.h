@@ -89,7 +89,7 @@ typedef enum pa_kernel {
   PA_KERNEL_AUTO = 0,     /* matrix-core kernel where supported, else vector kernel  */
   PA_KERNEL_VALU = 1,     /* vector-ALU kernel (every supported shape)               */
   PA_KERNEL_MFMA = 2      /* matrix-core kernel: head_dim 128, block 16, any group,
-                             q_len <= 4096, q bf16 with KV bf16 or fp8                */
+                             q_len <= 4096, q bf16 with KV bf16, fp8 or int4        */
 } pa_kernel_t;
 
 /* Sizes and types of one call. Supported: block_size 16; head_dim 64 or 128;
@@ -122,14 +122,20 @@ typedef struct pa_dims {
                                   with several query rows; a query with no token gets
                                   a zero row). Matrix-core kernel only, q_len <= 4096:
                                   a KV head's group * q_len (position, head) pairs
-                                  are taken in blocks of up to 64 per work item, each
-                                  block reading the KV head's tiles (chunked prefill
-                                  reads them once per block).                          */
+                                  are taken in blocks of up to 64. With more than one
+                                  block, the waves of a work item take one block each
+                                  and read every K/V tile once, through LDS (see
+                                  waves_per_item).                                   */
   int32_t schedule;            /* pa_schedule_t                                        */
   int32_t waves_per_item;      /* matrix-core kernel: waves that share one (sequence,
-                                  KV head, partition) item and merge their states in
-                                  LDS: 1, 2 or 4 (4 only with group * q_len <= 16);
-                                  0 = chosen by the library                          */
+                                  KV head, partition) item; 0 = chosen by the library.
+                                  group * q_len <= 64: the waves split the item's
+                                  tiles and merge their states in LDS: 1, 2 or 4 (4
+                                  only with group * q_len <= 16). group * q_len > 64:
+                                  2 or 4 waves take 2 or 4 query blocks of 64 pairs
+                                  each and share every K/V tile (default: 2 for two
+                                  blocks, else 4); 1 gives one block per item, each
+                                  reading the tiles itself.                          */
   const float* k_block_scales; /* device, [num_blocks][num_kv_heads] float32: the K
                                   values of physical block b, KV head g are multiplied
                                   by k_block_scales[b * num_kv_heads + g]. Required for

@@ -78,7 +78,6 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
   if (st != PA_OK) return st;
   p->group = d->num_heads / hkv;
   p->q_len = q_len_of(d);
-  p->q_blocks = (p->group * p->q_len + 16 * pa::kMaxColumnGroups - 1) / (16 * pa::kMaxColumnGroups);
   if (d->kernel == PA_KERNEL_AUTO) {
     p->kernel = pa::mfma_supported(d->q_dtype, d->kv_dtype, d->head_dim, p->group, d->block_size, p->q_len)
                     ? PA_KERNEL_MFMA
@@ -87,6 +86,20 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
     p->kernel = d->kernel;
   }
   p->max_len = d->max_seq_len > 0 ? d->max_seq_len : d->max_blocks_per_seq * d->block_size;
+  // Query blocks (up to 64 (query position, head) pairs each). With more than
+  // one, the matrix-core kernel by default gives an item 2 or 4 of them, one
+  // per wave, and the waves share every K/V tile; waves_per_item = 1 keeps
+  // one block per item.
+  const int gv = p->group * p->q_len;   // (query position, head) pairs per KV head
+  const int ncg = gv <= 16 ? 1 : gv <= 32 ? 2 : 4;
+  const int blocks64 = (gv + 16 * pa::kMaxColumnGroups - 1) / (16 * pa::kMaxColumnGroups);
+  const bool mfma = p->kernel == PA_KERNEL_MFMA;
+  int share_nw = 0;   // waves per item when they share tiles
+  if (mfma && blocks64 > 1 && d->waves_per_item != 1) {
+    share_nw = d->waves_per_item > 0 ? d->waves_per_item : (blocks64 == 2 ? 2 : 4);
+    if (!pa::mfma_share_tiles(p->group, p->q_len, share_nw)) return PA_ERR_UNSUPPORTED;
+  }
+  p->q_blocks = mfma ? pa::mfma_item_blocks(p->group, p->q_len, share_nw > 0 ? share_nw : 1) : 1;
   // Every wave keeps about one 64-token tile of K and V in flight. Covering
   // HBM latency at full bandwidth takes about as many waves as the chip holds
   // at once: 2048 with bf16 / fp32 tiles (32 KiB, two waves per SIMD) and 3072
@@ -96,17 +109,20 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
   // the waves come from splitting each item over 1, 2 or 4 waves; partitions
   // are shortened only when even 4 waves per item would not reach the target.
   const long long units = (long long)d->num_seqs * hkv * (p->kernel == PA_KERNEL_MFMA ? p->q_blocks : 1);
-  // three waves per SIMD: fp8 without per-block scales and int4 (with them)
+  // three waves per SIMD: fp8 without per-block scales and int4 (with them).
+  // The tile-sharing kernels run one wave per SIMD (1024 on the chip); their
+  // target is two rounds of items.
   const bool fp8 = d->kv_dtype == PA_DTYPE_FP8_E5M2 || d->kv_dtype == PA_DTYPE_FP8_E4M3;
   const bool three_waves = (fp8 && d->k_block_scales == nullptr) || d->kv_dtype == PA_DTYPE_INT4;
-  const long long target_waves = three_waves ? 3072 : 2048;
+  const long long target_waves = share_nw > 0 ? 2048 : three_waves ? 3072 : 2048;
+  const int max_item_waves = share_nw > 0 ? share_nw : 4;
   auto items_for = [&](long long P) { return units * ((p->max_len + P - 1) / P); };
   int P = d->partition_tokens;
   if (P == 0) {
     long long cap = 4096;
     while (cap / 2 >= p->max_len && cap > pa::kTileTokens) cap /= 2;   // no longer than the longest sequence needs
     P = (int)cap;
-    while (P > 256 && items_for(P) * 4 < target_waves) P /= 2;
+    while (P > 256 && items_for(P) * max_item_waves < target_waves) P /= 2;
   }
   if (d->partition_tokens == 0) {
     while ((p->max_len + (long long)P - 1) / P > kMaxParts) P *= 2;   // grid y limit
@@ -115,7 +131,6 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
   p->max_parts = p->max_len > 0 ? (int)((p->max_len + (long long)P - 1) / P) : 1;
   if (p->max_parts < 1) p->max_parts = 1;
   if (p->max_parts > kMaxParts) return PA_ERR_UNSUPPORTED;
-  if (p->kernel != PA_KERNEL_MFMA) p->q_blocks = 1;   // the vector kernel takes one query position
   p->grid = (long long)p->max_parts * hkv * p->q_blocks * d->num_seqs;
   p->reduce_grid = p->max_parts > 1 ? (long long)d->num_heads * p->q_len * d->num_seqs : 0;
   // List schedule: for the matrix-core kernel when asked, or when the dense
@@ -133,20 +148,22 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
   // Waves per item (matrix-core kernel): the list schedule splits its long
   // items four ways so the tail is short; the grid splits items while the
   // grid still fits the wave target, keeping at least 4 tiles per wave.
-  const int gv = p->group * p->q_len;   // (query position, head) pairs per KV head
-  const int ncg = gv <= 16 ? 1 : gv <= 32 ? 2 : 4;
   if (p->kernel != PA_KERNEL_MFMA) {
     if (d->waves_per_item > 1) return PA_ERR_UNSUPPORTED;
     p->waves_per_item = 1;
+  } else if (share_nw > 0) {
+    p->waves_per_item = share_nw;
   } else if (d->waves_per_item > 0) {
-    if (!pa::mfma_waves_supported(ncg, d->waves_per_item)) return PA_ERR_UNSUPPORTED;
+    if (!pa::mfma_waves_supported(p->group, p->q_len, d->waves_per_item)) return PA_ERR_UNSUPPORTED;
     p->waves_per_item = d->waves_per_item;
   } else if (p->schedule == PA_SCHEDULE_QUEUE) {
     p->waves_per_item = ncg == 1 ? 4 : 2;
   } else {
     const long long tiles = (std::min<long long>(P, p->max_len) + pa::kTileTokens - 1) / pa::kTileTokens;
     int nw = 1;
-    while (nw < 4 && p->grid * 2 * nw <= target_waves && tiles >= 4LL * 2 * nw && pa::mfma_waves_supported(ncg, 2 * nw)) nw *= 2;
+    while (nw < 4 && p->grid * 2 * nw <= target_waves && tiles >= 4LL * 2 * nw &&
+           pa::mfma_waves_supported(p->group, p->q_len, 2 * nw))
+      nw *= 2;
     p->waves_per_item = nw;
   }
   size_t off = 0;

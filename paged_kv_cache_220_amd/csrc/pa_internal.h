@@ -39,7 +39,8 @@ struct Args {
   const int* queue_len;
   int32_t queue_workgroups;
   int32_t waves_per_item;   // matrix-core kernel: waves sharing one work item (1, 2, 4)
-  int32_t q_blocks;         // blocks of up to 64 (query position, head) pairs per KV head
+  int32_t q_blocks;         // work items per (sequence, KV head): query blocks of up to 64 (query
+                            // position, head) pairs, or groups of waves_per_item blocks that share tiles
   const float* k_bscale;    // per-(block, KV head) scales [num_blocks][num_kv_heads], or null
   const float* v_bscale;
 };
@@ -54,7 +55,12 @@ hipError_t launch_plan(const Args& a, hipStream_t stream);
 
 bool valu_supported(int q_dtype, int kv_dtype, int head_dim, int group);
 bool mfma_supported(int q_dtype, int kv_dtype, int head_dim, int group, int block_size, int q_len);
-bool mfma_waves_supported(int ncg, int nw);
+bool mfma_waves_supported(int group, int q_len, int nw);
+// Tile sharing: with more than one query block per KV head and nw > 1, the nw
+// waves of a work item take one query block each and share every K/V tile.
+bool mfma_share_tiles(int group, int q_len, int nw);
+// Work items per (sequence, KV head) of the matrix-core kernel (Args::q_blocks).
+int mfma_item_blocks(int group, int q_len, int nw);
 
 constexpr int kBlockSize = 16;     // tokens per physical block handled by the kernels
 constexpr int kTileTokens = 64;    // partition lengths are multiples of this

@@ -57,12 +57,17 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kD = 128;       // head_dim handled by this kernel
 // s_waitcnt operand (gfx9 encoding: vmcnt[3:0] at bits 3:0 and vmcnt[5:4] at
 // bits 15:14, expcnt at 6:4, lgkmcnt at 11:8) that waits for vmcnt == 0 and
 // leaves the other counters unconstrained.
 constexpr int kWaitVmcnt0 = (0x7 << 4) | (0xF << 8);
+// The same operand waiting for vmcnt <= n (n < 64).
+constexpr int vmcnt_wait(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 constexpr int kTile = 64;     // tokens per tile
 constexpr int kKSteps = kD / 32;
 
@@ -107,13 +112,20 @@ template <> struct Mfma<kBF16> {
   }
   // P as a sum of two operands: hi = round(p), lo = round(p - hi), so the PV
   // product keeps about 16 significant bits of each weight.
+  // Pairs are rounded together (one packed conversion each for hi and lo);
+  // the rounded pair widens back to float by bit placement.
   static __device__ __forceinline__ void p_operands(const float (&p)[8], op_t& hi, op_t& lo) {
+    u32x4 h, l;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const __bf16 h = static_cast<__bf16>(p[i]);
-      hi[i] = h;
-      lo[i] = static_cast<__bf16>(p[i] - static_cast<float>(h));
+    for (int i = 0; i < 4; ++i) {
+      const f32x2 x = {p[2 * i], p[2 * i + 1]};
+      const uint32_t hw = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+      const f32x2 hx = {__builtin_bit_cast(float, hw << 16), __builtin_bit_cast(float, hw & 0xFFFF0000u)};
+      h[i] = hw;
+      l[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x - hx, bf16x2));
     }
+    hi = __builtin_bit_cast(op_t, h);
+    lo = __builtin_bit_cast(op_t, l);
   }
 };
 
@@ -160,12 +172,16 @@ template <> struct Mfma<kE5M2> {
     return o;
   }
   static __device__ __forceinline__ void p_operands(const float (&p)[8], op_t& hi, op_t& lo) {
+    u32x4 h, l;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const _Float16 h = static_cast<_Float16>(p[i]);
-      hi[i] = h;
-      lo[i] = static_cast<_Float16>(p[i] - static_cast<float>(h));
+    for (int i = 0; i < 4; ++i) {
+      const f32x2 x = {p[2 * i], p[2 * i + 1]};
+      const half2_t hh = __builtin_convertvector(x, half2_t);
+      h[i] = __builtin_bit_cast(uint32_t, hh);
+      l[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x - __builtin_convertvector(hh, f32x2), half2_t));
     }
+    hi = __builtin_bit_cast(op_t, h);
+    lo = __builtin_bit_cast(op_t, l);
   }
 };
 
@@ -269,7 +285,12 @@ template <> struct Mfma<kE4M3> {
 // the same tiles at about the same time on the same XCD can hit in them.
 // BSCALE: the cache carries per-(block, KV head) scales (int4 always, fp8
 // optionally); the kernel without them keeps the registers their products take.
-template <int KDT, int NCG, int NW, bool STREAM, bool BSCALE>
+// STAGES > 0: tile sharing. The NW waves of the workgroup take NW consecutive
+// query blocks of the item (query block qb * NW + wave) and walk the same
+// tiles; each K/V tile is copied once into a ring of STAGES LDS stages by all
+// waves together and every wave reads its operands from there. STAGES == 0:
+// the NW waves split the tiles of one query block and merge their states.
+template <int KDT, int NCG, int NW, bool STREAM, bool BSCALE, int STAGES>
 __device__ __forceinline__ void partition_item(const Args& a, int group, int s, int kvh, int part, int qb) {
   using M = Mfma<KDT>;
   using op_t = typename M::op_t;
@@ -281,14 +302,16 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   const int L = clamp_len(a, s);
   const int QL = a.q_len;
   const int GV = group * QL;                               // virtual heads of this KV head
-  const int v0 = 16 * kMaxColumnGroups * qb;               // first virtual head of this query block
+  constexpr bool kShare = STAGES > 0;
   const int P = a.partition_tokens;
   const int nparts = L > 0 ? (L + P - 1) / P : 1;
   if (part >= nparts) return;
   const int tok0 = part * P;
   const int tok1 = min(L, tok0 + P);
 
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // NW waves share the item: wave w takes tiles w, w + NW, ...
+  // NW waves share the item: without tile sharing wave w takes tiles w, w + NW, ...
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int v0 = 16 * kMaxColumnGroups * (kShare ? qb * NW + wave : qb);   // first virtual head of this query block
   const int lane = threadIdx.x & 63;
   const int c = lane >> 4;   // lane group: k slots of the operands, rows 4c..4c+3 of results
   const int n = lane & 15;   // MFMA row of A (quartet / head_dim row) and column of B (virtual head)
@@ -353,8 +376,8 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     idv1 = table[bv1 < nblk_part ? bv1 : b0];
   };
   int32_t idk = 0, idv0 = 0, idv1 = 0;
-  const int first = tok0 + wave * kTile;
-  constexpr int kStride = NW * kTile;
+  const int first = tok0 + (kShare ? 0 : wave) * kTile;
+  constexpr int kStride = (kShare ? 1 : NW) * kTile;
   if (first < tok1) tile_ids(first / BS, idk, idv0, idv1);
 
   // K slots in LDS (one per wave) for the kernels that stage K tiles there:
@@ -362,10 +385,12 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   // (one wave per SIMD: the next tile's K copy then overlaps this tile's
   // compute at no register cost). Four bf16 groups have no registers left
   // for the staged loop and load K directly.
-  constexpr bool kLdsK = M::kBits < 16 || NCG == 2;
+  constexpr bool kLdsK = !kShare && (M::kBits < 16 || NCG == 2);
   constexpr int kTileBlk = kD * kRowBytes;   // one block tile of one KV head
   constexpr int kSlotBlk = kTileBlk + 64;
   __shared__ __attribute__((aligned(16))) uint8_t k_lds[kLdsK ? NW : 1][kLdsK ? 4 * kSlotBlk : 16];
+  // Tile sharing: stage x holds the K tile (4 block slots) then the V tile.
+  __shared__ __attribute__((aligned(16))) uint8_t kv_lds[kShare ? STAGES : 1][kShare ? 8 * kSlotBlk : 16];
   // One tile's K and V registers.
   struct Tile {
     kload_t kr[kKSteps][8];
@@ -527,7 +552,121 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     }
   };
 
-  if constexpr (kLdsK) {
+  // Helpers of the LDS-staged loops. The four block ids of a tile are the
+  // same for the whole wave. They (and the per-block scales) are read through
+  // the constant address space, so they become scalar loads even where the
+  // compiler cannot tell that the loop's LDS copies leave that memory alone.
+  typedef __attribute__((address_space(3))) void* lds_ptr_t;
+  typedef __attribute__((address_space(1))) void* gbl_ptr_t;
+  typedef const __attribute__((address_space(4))) int32_t* cint_ptr_t;
+  typedef const __attribute__((address_space(4))) float* cflt_ptr_t;
+  const cint_ptr_t ctable = (cint_ptr_t)table;
+  const int last_blk = nblk_part - 1;
+  auto ids_at = [&](int t, int32_t (&ib)[4]) __attribute__((always_inline)) {
+    const int b0 = min(t / BS, last_blk);
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) ib[blk] = clamp_block(a, ctable[b0 + blk < nblk_part ? b0 + blk : b0]);
+  };
+  // Per-block scales of a tile (the same for the whole wave).
+  constexpr bool bscaled = BSCALE;
+  auto uniform_f = [](float x) __attribute__((always_inline)) {   // keep wave-uniform values in scalar registers
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+  };
+  auto scales_at = [&](const int32_t (&ib)[4], float (&kb)[4], float (&vb)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      const int64_t at = (int64_t)__builtin_amdgcn_readfirstlane(ib[blk]) * a.num_kv_heads + kvh;
+      kb[blk] = bscaled ? uniform_f(((cflt_ptr_t)a.k_bscale)[at]) : 1.f;
+      vb[blk] = bscaled ? uniform_f(((cflt_ptr_t)a.v_bscale)[at]) : 1.f;
+    }
+  };
+  // This lane's two scales of a tile: block (c >> 1) + 2x for x = 0, 1.
+  auto lane_scales = [&](const float (&b)[4], float (&x)[2]) __attribute__((always_inline)) {
+    x[0] = (c >> 1) == 0 ? b[0] : b[1];
+    x[1] = (c >> 1) == 0 ? b[2] : b[3];
+  };
+
+  if constexpr (kShare) {
+    // Tile sharing. A tile's K and V (4 block tiles each) land in one LDS
+    // stage through direct global-to-LDS copies of 1 KiB (16 bytes per lane),
+    // dealt round robin to the NW waves, STAGES - 1 tiles ahead of use. Before
+    // tile i each wave waits for its own copies of it; the workgroup barrier
+    // that follows covers the other waves' copies, and also tells that every
+    // wave is done with the stage of tile i - 1, which then takes tile
+    // i + STAGES - 1. Each wave reads its K pieces and V rows from the stage
+    // and runs the tile for its own query block.
+    constexpr int kCpb = kTileBlk / 1024;     // copies per block tile
+    constexpr int kCopies = 8 * kCpb;         // K and V of 4 blocks
+    constexpr int kPer = kCopies / NW;        // copies per wave per tile
+    static_assert(kCopies % NW == 0, "tile copies must split evenly over the waves");
+    static_assert(STAGES >= 2 && STAGES <= 4, "two to four stages");
+    const int ntiles = (tok1 - tok0 + kTile - 1) / kTile;
+    const bool active = v0 < GV;              // wave-uniform: this wave's query block exists
+    auto issue = [&](int i) __attribute__((always_inline)) {
+      int32_t ib[4];
+      ids_at(tok0 + i * kTile, ib);
+      uint8_t* st = &kv_lds[i % STAGES][0];
+#pragma unroll
+      for (int y = 0; y < kPer; ++y) {
+        const int x = y * NW + wave;          // copy x: cache kv, block blk, KiB pc of the block tile
+        const int kv = x / (4 * kCpb), blk = (x / kCpb) % 4, pc = x % kCpb;
+        const int32_t id = blk == 0 ? ib[0] : blk == 1 ? ib[1] : blk == 2 ? ib[2] : ib[3];
+        const char* src = (kv ? vbase : kbase) + id * blk_bytes + pc * 1024 + lane * 16;
+        __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(st + (4 * kv + blk) * kSlotBlk + pc * 1024),
+                                         16, 0, STREAM ? 2 : 0);   // 2: non-temporal
+      }
+    };
+    // Prologue: tiles 0 .. STAGES - 2. A partition with fewer tiles copies its
+    // last tile again (into the same stage, with the same bytes), so that the
+    // number of copies after the q loads is fixed; the loop's waits then count
+    // the extra copies as later ones and stay on the safe side.
+    if (ntiles > 0) {   // the same for every wave of the item (an empty sequence has none)
+#pragma unroll
+      for (int i = 0; i < STAGES - 1; ++i) issue(min(i, ntiles - 1));
+      for (int i = 0; i < ntiles; ++i) {
+        const int t0 = tok0 + i * kTile;
+        // own copies of tile i: everything but those of the later tiles in flight
+        const int ahead = min(STAGES - 2, ntiles - 1 - i);
+        if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * kPer));
+        else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_wait(kPer));
+        else __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + STAGES - 1 < ntiles) issue(i + STAGES - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (active) {
+          float kb[4], vb[4], ksc[2], vsc[2];
+          if constexpr (BSCALE) {
+            int32_t ib[4];
+            ids_at(t0, ib);
+            scales_at(ib, kb, vb);
+            lane_scales(kb, ksc);
+            lane_scales(vb, vsc);
+          } else {
+            ksc[0] = ksc[1] = vsc[0] = vsc[1] = 1.f;
+          }
+          const uint8_t* st = &kv_lds[i % STAGES][0];
+          const uint8_t* krow = st + kblk * kSlotBlk + c * kRowBytes + ktok * M::kBits / 8;
+          Tile T;
+#pragma unroll
+          for (int ks = 0; ks < kKSteps; ++ks) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+              T.kr[ks][r] = *reinterpret_cast<const kload_t*>(krow + (32 * ks + 4 * r) * kRowBytes);
+          }
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt)
+              T.vr[dt][hh] = *reinterpret_cast<const vload_t*>(st + (4 + (c >> 1) + 2 * hh) * kSlotBlk +
+                                                               (16 * dt + n) * kRowBytes + 8 * (c & 1) * M::kBits / 8);
+          }
+          tile_step(T, t0, []() __attribute__((always_inline)) {}, ksc, vsc);
+        }
+      }
+    }
+  } else if constexpr (kLdsK) {
     // Staged K. A K tile is 4 block tiles of 128 rows x 16 tokens; it lands in
     // this wave's LDS slot through direct global-to-LDS loads of whole rows
     // (16 bytes per lane, each instruction reading 1 KiB contiguous), and QK
@@ -541,16 +680,8 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     // slot is free again) and V of the next tile right after PV (into the V
     // registers PV has released). The four block ids of a tile are the same
     // for the whole wave; they are fetched two tiles ahead.
-    typedef __attribute__((address_space(3))) void* lds_ptr_t;
-    typedef __attribute__((address_space(1))) void* gbl_ptr_t;
     uint8_t* kslot = &k_lds[wave][0];
     const uint8_t* krow = kslot + kblk * kSlotBlk + c * kRowBytes + ktok * M::kBits / 8;   // + row bytes * (32 ks + 4 i)
-    const int last_blk = nblk_part - 1;
-    auto ids_at = [&](int t, int32_t (&ib)[4]) __attribute__((always_inline)) {
-      const int b0 = min(t / BS, last_blk);
-#pragma unroll
-      for (int blk = 0; blk < 4; ++blk) ib[blk] = clamp_block(a, table[b0 + blk < nblk_part ? b0 + blk : b0]);
-    };
     auto load_k_lds = [&](const int32_t (&ib)[4]) __attribute__((always_inline)) {
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk) {
@@ -565,20 +696,6 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     auto load_v_ids = [&](Tile& T, const int32_t (&ib)[4]) __attribute__((always_inline)) {
       load_v(T, (c >> 1) == 0 ? ib[0] : ib[1], (c >> 1) == 0 ? ib[2] : ib[3]);
     };
-    // Per-block scales of a tile (the same for the whole wave), then this
-    // lane's two: block (c >> 1) + 2x for x = 0, 1.
-    constexpr bool bscaled = BSCALE;
-    auto uniform_f = [](float x) __attribute__((always_inline)) {   // keep wave-uniform values in scalar registers
-      return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
-    };
-    auto scales_at = [&](const int32_t (&ib)[4], float (&kb)[4], float (&vb)[4]) __attribute__((always_inline)) {
-#pragma unroll
-      for (int blk = 0; blk < 4; ++blk) {
-        const int64_t at = (int64_t)__builtin_amdgcn_readfirstlane(ib[blk]) * a.num_kv_heads + kvh;
-        kb[blk] = bscaled ? uniform_f(a.k_bscale[at]) : 1.f;
-        vb[blk] = bscaled ? uniform_f(a.v_bscale[at]) : 1.f;
-      }
-    };
     if (first < tok1) {
       Tile T;
       int32_t icur[4], inext[4];
@@ -592,8 +709,9 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
       for (int t0 = first; t0 < tok1; t0 += kStride) {
         const bool more = t0 + kStride < tok1;
         scales_at(inext, kb_next, vb_next);   // the next tile's, a tile ahead of use
-        const float ksc[2] = {(c >> 1) == 0 ? kb_cur[0] : kb_cur[1], (c >> 1) == 0 ? kb_cur[2] : kb_cur[3]};
-        const float vsc[2] = {(c >> 1) == 0 ? vb_cur[0] : vb_cur[1], (c >> 1) == 0 ? vb_cur[2] : vb_cur[3]};
+        float ksc[2], vsc[2];
+        lane_scales(kb_cur, ksc);
+        lane_scales(vb_cur, vsc);
         // The K copy into LDS is a vector-memory operation: wait for every
         // outstanding one (vmcnt 0) before reading the slot. The compiler's own
         // wait insertion does not cover LDS written this way in every
@@ -646,7 +764,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     l_tot[cg] += shfl_xor_f32(l_tot[cg], 16);
     l_tot[cg] += shfl_xor_f32(l_tot[cg], 32);
   }
-  if constexpr (NW > 1) {
+  if constexpr (NW > 1 && !kShare) {
     // Waves 1.. publish their (m, l, o) in LDS; wave 0 rescales them to the
     // common max and adds them in wave order (the merge rule of the partition
     // states, inside the workgroup), then writes the item's result.
@@ -732,32 +850,45 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NCG == 1 ? 2 : 1, 8)))
 
 // Grid schedule: one workgroup per (KV head, sequence, partition) of the dense grid.
-template <int KDT, int NCG, int NW, bool STREAM, bool BSCALE>
+template <int KDT, int NCG, int NW, bool STREAM, bool BSCALE, int STAGES>
 PA_MFMA_KERNEL_ATTRS void mfma_partition_kernel(const Args a, int group) {
   const Item it = work_item(a);
-  partition_item<KDT, NCG, NW, STREAM, BSCALE>(a, group, it.s, it.kvh, it.part, it.qb);
+  partition_item<KDT, NCG, NW, STREAM, BSCALE, STAGES>(a, group, it.s, it.kvh, it.part, it.qb);
 }
 
 // List schedule: workgroup i takes item i of the list the plan kernel built,
 // longest first, and workgroups past its end exit at once. Workgroups are
 // dispatched in index order, so long items start first and short ones fill
 // the end; consecutive (similar) items go to consecutive XCDs.
-template <int KDT, int NCG, int NW, bool STREAM, bool BSCALE>
+template <int KDT, int NCG, int NW, bool STREAM, bool BSCALE, int STAGES>
 PA_MFMA_KERNEL_ATTRS void mfma_partition_list_kernel(const Args a, int group) {
   const int idx = blockIdx.x;
   if (idx >= *a.queue_len) return;
   const int2 w = a.queue_items[idx];            // unit (s * q_blocks + qb) * Hkv + kvh, partition
   const int sq = w.x / a.num_kv_heads;
   const int s = sq / a.q_blocks;
-  partition_item<KDT, NCG, NW, STREAM, BSCALE>(a, group, s, w.x - sq * a.num_kv_heads, w.y, sq - s * a.q_blocks);
+  partition_item<KDT, NCG, NW, STREAM, BSCALE, STAGES>(a, group, s, w.x - sq * a.num_kv_heads, w.y,
+                                                       sq - s * a.q_blocks);
 }
 
 }  // namespace
 
-// Waves per item: 1, 2 or 4 with one column group; 1 or 2 with more (the
-// LDS exchange holds (NW - 1) x NCG x 8 KiB).
-bool mfma_waves_supported(int ncg, int nw) {
-  return nw == 1 || nw == 2 || (nw == 4 && ncg == 1);
+bool mfma_share_tiles(int group, int q_len, int nw) {
+  return nw > 1 && group * q_len > 16 * kMaxColumnGroups;
+}
+
+int mfma_item_blocks(int group, int q_len, int nw) {
+  const int blocks = (group * q_len + 16 * kMaxColumnGroups - 1) / (16 * kMaxColumnGroups);
+  return mfma_share_tiles(group, q_len, nw) ? (blocks + nw - 1) / nw : blocks;
+}
+
+// Waves per item: 1, 2 or 4 with one column group; 1 or 2 with two or four
+// (the LDS exchange holds (NW - 1) x NCG x 8 KiB). With more than one query
+// block the waves share tiles instead: 2 or 4, one block each.
+bool mfma_waves_supported(int group, int q_len, int nw) {
+  const int gv = group * q_len;
+  if (gv > 16 * kMaxColumnGroups) return nw == 1 || nw == 2 || nw == 4;
+  return nw == 1 || nw == 2 || (nw == 4 && gv <= 16);
 }
 
 bool mfma_supported(int q_dtype, int kv_dtype, int head_dim, int group, int block_size, int q_len) {
@@ -768,24 +899,36 @@ bool mfma_supported(int q_dtype, int kv_dtype, int head_dim, int group, int bloc
 
 namespace {
 
-template <int KDT, int NCG, int NW, bool ST, bool BS>
+template <int KDT, int NCG, int NW, bool ST, bool BS, int STG>
 void launch_one(const Args& a, int group, dim3 grid, bool queue, hipStream_t stream) {
-  if (queue) mfma_partition_list_kernel<KDT, NCG, NW, ST, BS><<<grid, 64 * NW, 0, stream>>>(a, group);
-  else mfma_partition_kernel<KDT, NCG, NW, ST, BS><<<grid, 64 * NW, 0, stream>>>(a, group);
+  if (queue) mfma_partition_list_kernel<KDT, NCG, NW, ST, BS, STG><<<grid, 64 * NW, 0, stream>>>(a, group);
+  else mfma_partition_kernel<KDT, NCG, NW, ST, BS, STG><<<grid, 64 * NW, 0, stream>>>(a, group);
 }
 
-template <int KDT, int NCG, int NW, bool ST>
+template <int KDT, int NCG, int NW, bool ST, int STG = 0>
 void launch_scaled(const Args& a, int group, dim3 grid, bool queue, hipStream_t stream) {
-  if constexpr (KDT == kBF16) launch_one<KDT, NCG, NW, ST, false>(a, group, grid, queue, stream);
-  else if constexpr (KDT == kI4) launch_one<KDT, NCG, NW, ST, true>(a, group, grid, queue, stream);
-  else if (a.k_bscale != nullptr) launch_one<KDT, NCG, NW, ST, true>(a, group, grid, queue, stream);
-  else launch_one<KDT, NCG, NW, ST, false>(a, group, grid, queue, stream);
+  if constexpr (KDT == kBF16) launch_one<KDT, NCG, NW, ST, false, STG>(a, group, grid, queue, stream);
+  else if constexpr (KDT == kI4) launch_one<KDT, NCG, NW, ST, true, STG>(a, group, grid, queue, stream);
+  else if (a.k_bscale != nullptr) launch_one<KDT, NCG, NW, ST, true, STG>(a, group, grid, queue, stream);
+  else launch_one<KDT, NCG, NW, ST, false, STG>(a, group, grid, queue, stream);
 }
+
+// LDS stages of the tile-sharing kernels (one wave per SIMD, so a CU holds
+// four waves): four, except for bf16 with two waves, where two stages of
+// 33 KiB let two workgroups share a CU's LDS.
+template <int KDT, int NW>
+constexpr int share_stages() { return (KDT == kBF16 && NW == 2) ? 2 : 4; }
 
 template <int KDT>
-void launch_kdt(const Args& a, int group, int ncg, int nw, dim3 grid, bool queue, hipStream_t stream) {
+void launch_kdt(const Args& a, int group, int ncg, int nw, bool share, dim3 grid, bool queue, hipStream_t stream) {
   const bool st = a.q_blocks == 1;   // several query blocks: share tiles through the caches
-  if (ncg == 1 && nw == 1) launch_scaled<KDT, 1, 1, true>(a, group, grid, queue, stream);
+  if (share) {
+    if (nw == 2 && st) launch_scaled<KDT, 4, 2, true, share_stages<KDT, 2>()>(a, group, grid, queue, stream);
+    else if (nw == 2) launch_scaled<KDT, 4, 2, false, share_stages<KDT, 2>()>(a, group, grid, queue, stream);
+    else if (st) launch_scaled<KDT, 4, 4, true, share_stages<KDT, 4>()>(a, group, grid, queue, stream);
+    else launch_scaled<KDT, 4, 4, false, share_stages<KDT, 4>()>(a, group, grid, queue, stream);
+  }
+  else if (ncg == 1 && nw == 1) launch_scaled<KDT, 1, 1, true>(a, group, grid, queue, stream);
   else if (ncg == 1 && nw == 2) launch_scaled<KDT, 1, 2, true>(a, group, grid, queue, stream);
   else if (ncg == 1) launch_scaled<KDT, 1, 4, true>(a, group, grid, queue, stream);
   else if (ncg == 2 && nw == 1) launch_scaled<KDT, 2, 1, true>(a, group, grid, queue, stream);
@@ -803,18 +946,19 @@ hipError_t launch_mfma(const Args& a, int q_dtype, int kv_dtype, int head_dim, i
   if (!mfma_supported(q_dtype, kv_dtype, head_dim, group, kBlockSize, a.q_len)) return hipErrorInvalidValue;
   const int gv = group * a.q_len;                 // virtual heads per KV head, in blocks of up to 64
   const int ncg = gv <= 16 ? 1 : gv <= 32 ? 2 : 4;
-  if (a.q_blocks != (gv + 16 * kMaxColumnGroups - 1) / (16 * kMaxColumnGroups)) return hipErrorInvalidValue;
+  const int nw = a.waves_per_item;
+  if (!mfma_waves_supported(group, a.q_len, nw)) return hipErrorInvalidValue;
+  const bool share = mfma_share_tiles(group, a.q_len, nw);
+  if (a.q_blocks != mfma_item_blocks(group, a.q_len, nw)) return hipErrorInvalidValue;
   if ((kv_dtype == kI4) != (a.k_bscale != nullptr && a.v_bscale != nullptr) && kv_dtype != kE5M2 &&
       kv_dtype != kE4M3)
     return hipErrorInvalidValue;                  // int4 needs both scale arrays; bf16 takes none
   const bool queue = a.queue_items != nullptr;
   const dim3 grid = queue ? dim3((unsigned)a.queue_workgroups) : partition_grid(a);   // list: one per possible item
-  const int nw = a.waves_per_item;
-  if (!mfma_waves_supported(ncg, nw)) return hipErrorInvalidValue;
-  if (kv_dtype == kBF16) launch_kdt<kBF16>(a, group, ncg, nw, grid, queue, stream);
-  else if (kv_dtype == kE5M2) launch_kdt<kE5M2>(a, group, ncg, nw, grid, queue, stream);
-  else if (kv_dtype == kE4M3) launch_kdt<kE4M3>(a, group, ncg, nw, grid, queue, stream);
-  else launch_kdt<kI4>(a, group, ncg, nw, grid, queue, stream);
+  if (kv_dtype == kBF16) launch_kdt<kBF16>(a, group, ncg, nw, share, grid, queue, stream);
+  else if (kv_dtype == kE5M2) launch_kdt<kE5M2>(a, group, ncg, nw, share, grid, queue, stream);
+  else if (kv_dtype == kE4M3) launch_kdt<kE4M3>(a, group, ncg, nw, share, grid, queue, stream);
+  else launch_kdt<kI4>(a, group, ncg, nw, share, grid, queue, stream);
   return hipGetLastError();
 }
 

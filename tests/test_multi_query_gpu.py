@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import check, log
+from gpu_helpers import check, log, upload
 from oracle import pa_oracle as O
 from paged_kv_cache_220_amd import binding as B
 from paged_kv_cache_220_amd import workloads as W
@@ -177,3 +177,52 @@ def test_multi_query_int4(ql):
                     k_block_scales=sc(w.k_block_scales), v_block_scales=sc(w.v_block_scales))
         torch.cuda.synchronize()
         check(out.float().cpu().numpy().astype(np.float64), ref, w, f"multi-query int4 q_len={ql} P={ptok}")
+
+
+SHARE = [
+    # kv dtype, per-block scales, query positions: 8 heads x q_len pairs in blocks of 64
+    ("bf16", False, 16),    # two blocks: by default one item of two waves
+    ("bf16", False, 24),    # three blocks: four waves, one idle; or two items of two waves
+    ("e5m2", False, 16),
+    ("e4m3", True, 20),
+    ("int4", True, 24),
+]
+
+
+@pytest.mark.parametrize("kv,scaled,ql", SHARE, ids=[f"{c[0]}{'-scaled' if c[1] else ''}-q{c[2]}" for c in SHARE])
+def test_tile_sharing(kv, scaled, ql):
+    """Waves of one work item take one query block each and share every K/V
+    tile through LDS: partitions of 1, 2 and 4 tiles (fewer tiles than LDS
+    stages), lengths shorter than the query window, both schedules. The result
+    of a query block does not depend on how many blocks share its tiles: 1, 2
+    and 4 waves per item give the same bits."""
+    w = W.random_edge_workload(70 + ql, S=4, H=64, Hkv=8, D=128, seq_lens=[1000, 65, 1, 300], kv_dtype=kv)
+    rng = np.random.default_rng([ql, 71])
+    if scaled and kv != "int4":
+        w.k_block_scales = np.exp2(rng.uniform(-2, 2, (w.num_blocks, w.num_kv_heads))).astype(np.float32)
+        w.v_block_scales = np.exp2(rng.uniform(-2, 2, (w.num_blocks, w.num_kv_heads))).astype(np.float32)
+        w.k_scale, w.v_scale = np.float32(0.75), np.float32(1.25)
+    q = W.to_storage(rng.standard_normal((w.num_seqs, ql, w.num_heads, w.head_dim), dtype=np.float32), "bf16")
+    ref = np.concatenate([O.paged_attention_multi(q[s:s + 1], w.k_cache, w.v_cache, w.block_tables[s:s + 1],
+                                                  w.seq_lens[s:s + 1], w.num_kv_heads, w.scale, "bf16", kv,
+                                                  k_scale=float(w.k_scale), v_scale=float(w.v_scale),
+                                                  k_block_scales=w.k_block_scales,
+                                                  v_block_scales=w.v_block_scales)
+                          for s in range(w.num_seqs)])
+    dev = upload(w)
+    qd = _dev(q, "bf16")
+    outs = {}
+    for ptok, sched, nw in ((0, "auto", 0), (64, "grid", 2), (128, "grid", 4), (128, "grid", 2), (128, "grid", 1),
+                            (256, "queue", 4), (64, "grid", 1)):
+        out = torch.full_like(qd, float("nan"))
+        log(f"case tile sharing {kv} scaled={scaled} q_len={ql} P={ptok} {sched} waves={nw}")
+        B.pa_decode(qd, dev["k"], dev["v"], dev["tables"], dev["seq_lens"], w.num_kv_heads, float(w.scale), out,
+                    partition_tokens=ptok, max_seq_len=w.max_seq_len, kernel="mfma", schedule=sched,
+                    waves_per_item=nw, k_scale=float(w.k_scale), v_scale=float(w.v_scale),
+                    k_block_scales=dev["k_block_scales"], v_block_scales=dev["v_block_scales"])
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy().astype(np.float64)
+        check(got, ref, w, f"tile sharing {kv} q_len={ql} P={ptok} {sched} waves={nw}")
+        outs[(ptok, nw)] = out.view(torch.int16).cpu().numpy()
+    for nw in (2, 4):
+        assert np.array_equal(outs[(128, nw)], outs[(128, 1)]), f"{nw} waves sharing tiles differ from one block per item"
