@@ -187,30 +187,35 @@ template <> struct Mfma<kE5M2> {
 
 // int4 KV: two's-complement codes, two tokens per byte (the even token in the
 // low nibble), so a K piece of 4 tokens is 2 bytes and a V piece of 8 tokens
-// 4 bytes. Widening is exact: with u = code ^ 8 (code + 8, 0..15), the
-// binary16 bit pattern 0x6400 | u is 1024 + u, and one packed binary16
-// subtraction of 1032 gives the code, two values per 32-bit word. The
-// per-block scales are applied to the scores (K) and to P (V) instead.
+// 4 bytes. The operands carry u = code ^ 8 = code + 8 (0..15) as a binary16
+// subnormal: the bit pattern u is the value u * 2^-24 exactly, and the pattern
+// 16u (the nibble one place up) is 16u * 2^-24, still subnormal. So widening
+// is one mask per pair of values (and a shift for half of K's); the offset
+// and the power of two are taken out of the fp32 results instead:
+//   score = 2^24 / s_j * (u-product) - 8 * sum_d q[d]   (s_j = 1 or 16: kKShift)
+//   o     = 2^24 * (u-product)       - 8 * sum_t p[t]
+// with the sums over the f16 q values and over the P values fed to the MFMA.
+// The per-block scales are applied to the scores (K) and to P (V).
 template <> struct Mfma<kI4> {
   using op_t = f16x8;
   using kload_t = uint16_t;  // 4 tokens of one row
   using vload_t = uint32_t;  // 8 tokens of one row
   static constexpr int kBits = 4;
-  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-  static __device__ __forceinline__ uint32_t widen2(uint32_t u) {   // nibble values at bits 0..3 and 16..19
-    const f16x2 v = __builtin_bit_cast(f16x2, u | 0x64006400u) - f16x2{(_Float16)1032.0f, (_Float16)1032.0f};
-    return __builtin_bit_cast(uint32_t, v);
-  }
+  static constexpr float kOffset = 8.f;          // u = code + 8
+  static constexpr float kUnit = 16777216.f;     // 2^24: one subnormal binary16 step
+  // QK instruction for token j of a quartet produces s_j times the product
+  static constexpr float kKScale[4] = {1.f, 16.f, 1.f, 16.f};
   static __device__ __forceinline__ f32x4 mma(op_t a, op_t b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
-  // token j of rows 2p (low half) and 2p + 1 (high half)
+  // token j of rows 2p (low half) and 2p + 1 (high half): nibble j of each half
+  // at bits 0..3 (j = 0, 2) or 4..7 (j = 1, 3)
   static __device__ __forceinline__ op_t k_operand(const kload_t (&r)[8], int j) {
     u32x4 x;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const uint32_t w = (uint32_t(r[2 * p]) | (uint32_t(r[2 * p + 1]) << 16)) ^ 0x88888888u;
-      x[p] = widen2((w >> (4 * j)) & 0x000F000Fu);
+      x[p] = (j < 2 ? w : w >> 8) & ((j & 1) ? 0x00F000F0u : 0x000F000Fu);
     }
     return __builtin_bit_cast(op_t, x);
   }
@@ -221,7 +226,7 @@ template <> struct Mfma<kI4> {
     u32x4 y;
 #pragma unroll
     for (int p = 0; p < 4; ++p)
-      y[p] = widen2(__builtin_amdgcn_perm(hi, lo, uint32_t(p) | (0x0Cu << 8) | (uint32_t(4 + p) << 16) | (0x0Cu << 24)));
+      y[p] = __builtin_amdgcn_perm(hi, lo, uint32_t(p) | (0x0Cu << 8) | (uint32_t(4 + p) << 16) | (0x0Cu << 24));
     return __builtin_bit_cast(op_t, y);
   }
   static __device__ __forceinline__ vload_t mask_v(vload_t x, int nvalid) {
@@ -321,6 +326,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   // all loads issue back to back without a branch between them.
   op_t qop[NCG][kKSteps];
   int lim[NCG];                // tokens the column's query may attend: t < lim
+  float qsum[NCG];             // int4: sum_d q[d] of the column
 #pragma unroll
   for (int cg = 0; cg < NCG; ++cg) {
     const int v = v0 + 16 * cg + n;
@@ -342,6 +348,18 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
       for (int i = 0; i < 8; ++i) qb[ks][i] = col_ok ? qb[ks][i] : 0u;
       qop[cg][ks] = M::q_operand(qb[ks]);
     }
+    if constexpr (KDT == kI4) {
+      // sum over head_dim of the binary16 q values the MFMA uses
+      float qs = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qs += static_cast<float>(qop[cg][ks][i]);
+      }
+      qs += shfl_xor_f32(qs, 16);
+      qs += shfl_xor_f32(qs, 32);
+      qsum[cg] = qs;
+    }
   }
 
   // This lane's block (0..3 within a tile) and token offset for the K loads.
@@ -357,11 +375,13 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
 
   float m_run[NCG];          // running max per column (log2 domain), same in all lane groups
   float l_run[NCG];          // this lane group's share of the running sum
+  float pv_run[NCG];         // int4: its share of the running sum of the P values fed to PV
   f32x4 oacc[NCG][8];
 #pragma unroll
   for (int cg = 0; cg < NCG; ++cg) {
     m_run[cg] = -INFINITY;
     l_run[cg] = 0.f;
+    pv_run[cg] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) oacc[cg][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -454,12 +474,26 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     const int nval = min(tok1, lim[cg]) - t0;   // this column's tokens in the tile (may be <= 0)
     float sc[4][4];                             // [r][j]; tokens outside the window: -inf
     float tmax = -INFINITY;
+    float ka[2], kb[2];                         // score = product * ka + kb, per block of the lane
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      if constexpr (KDT == kI4) {
+        ka[x] = a.score_scale * ksc[x] * Mfma<kI4>::kUnit;
+        kb[x] = -(a.score_scale * ksc[x]) * (Mfma<kI4>::kOffset * qsum[cg]);
+      } else {
+        ka[x] = a.score_scale * ksc[x];
+        kb[x] = 0.f;
+      }
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int tt = 16 * ((c >> 1) + 2 * (r >> 1)) + 8 * (c & 1) + 4 * (r & 1);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        sc[r][j] = (tt + j < nval) ? sg[j][r] * (a.score_scale * ksc[r >> 1]) : -INFINITY;
+        float sv;
+        if constexpr (KDT == kI4) sv = fmaf(sg[j][r], ka[r >> 1] * (1.f / Mfma<kI4>::kKScale[j]), kb[r >> 1]);
+        else sv = sg[j][r] * ka[r >> 1];
+        sc[r][j] = (tt + j < nval) ? sv : -INFINITY;
         tmax = fmaxf(tmax, sc[r][j]);
       }
     }
@@ -486,13 +520,26 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) oacc[cg][dt] *= alpha;
     // PV instruction hh takes quartets r = 2hh, 2hh+1
+    float pvsum = 0.f;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       float pv[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pv[i] = p[2 * hh + (i >> 2)][i & 3] * vsc[hh];
+      for (int i = 0; i < 8; ++i) {
+        // int4: the sum adds exactly the rounded values PV receives (the empty
+        // asm keeps the compiler from fusing the product into the sum, which it
+        // would do in some instantiations and not in others)
+        if constexpr (KDT == kI4) {
+          pv[i] = p[2 * hh + (i >> 2)][i & 3] * vsc[hh];
+          asm("" : "+v"(pv[i]));
+          pvsum += pv[i];
+        } else {
+          pv[i] = p[2 * hh + (i >> 2)][i & 3] * vsc[hh];
+        }
+      }
       M::p_operands(pv, phi[hh], plo[hh]);
     }
+    if constexpr (KDT == kI4) pv_run[cg] = fmaf(pv_run[cg], alpha, pvsum);
   };
   // V values of token slots at or past the partition end are zeroed: their
   // weights are 0, but 0 * NaN would poison the sum.
@@ -757,6 +804,21 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   }
 
   // ---- epilogue: lane (c, n) of group cg holds O^T[16*dt + 4*c + r][virtual head 16*cg + n]
+  if constexpr (KDT == kI4) {
+    // o = 2^24 * (offset-code product) - 8 * (sum of the P values fed to PV)
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) {
+      float pv_tot = pv_run[cg];
+      pv_tot += shfl_xor_f32(pv_tot, 16);
+      pv_tot += shfl_xor_f32(pv_tot, 32);
+      const float off = Mfma<kI4>::kOffset * pv_tot;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) oacc[cg][dt][e] = fmaf(oacc[cg][dt][e], Mfma<kI4>::kUnit, -off);
+      }
+    }
+  }
   float l_tot[NCG];
 #pragma unroll
   for (int cg = 0; cg < NCG; ++cg) {
