@@ -267,9 +267,10 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # Two library-recorded events per step bracket the partition kernel (and the
-    # work-list plan kernel when that schedule runs); each event costs the
-    # stream a few microseconds, so none is recorded after the merge kernel.
+    # Two library-recorded events per step bracket the partition kernel: the
+    # matrix-core kernel's dispatch records them itself at the start and end of
+    # its execution (the plan kernel of the list schedule runs before). None is
+    # recorded after the merge kernel.
     K = args.steps
     evs = hip.create(2 * K)
     t_start = torch.cuda.Event(enable_timing=True)

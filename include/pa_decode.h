@@ -167,8 +167,11 @@ int pa_decode_ws(const void* q, const void* k_cache, const void* v_cache,
                  void* stream);
 
 /* pa_decode_ws that also records three caller-created HIP events (hipEvent_t
- * as void*) on `stream`: before the partition kernel, between the partition
- * and reduce kernels, and after the reduce kernel. Any event may be NULL. */
+ * as void*) on `stream`: ev_start and ev_mid at the start and end of the
+ * partition kernel's execution (for the matrix-core kernel they are attached
+ * to its dispatch, so they add no separate stream operations), ev_end after
+ * the reduce kernel. Any event may be NULL. With the list schedule the plan
+ * kernel runs before ev_start. */
 int pa_decode_ws_timed(const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* block_tables, const int32_t* seq_lens,
                        int32_t num_kv_heads, float scale, void* out,

@@ -239,13 +239,17 @@ int run(const void* q, const void* k_cache, const void* v_cache, const int32_t* 
   }
   a.waves_per_item = p.waves_per_item;
 
-  if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return PA_ERR_HIP;
+  // Timing: the matrix-core kernel's dispatch records ev0 / ev1 itself at the
+  // start and end of its execution (no extra stream markers, whose cost would
+  // land in every timed step); around the vector kernel they are recorded on
+  // the stream. The work-list plan kernel, when it runs, precedes ev0.
+  const bool mfma = p.kernel == PA_KERNEL_MFMA;
   if (p.schedule == PA_SCHEDULE_QUEUE && pa::launch_plan(a, stream) != hipSuccess) return PA_ERR_HIP;
-  hipError_t e = p.kernel == PA_KERNEL_MFMA
-                     ? pa::launch_mfma(a, dims->q_dtype, dims->kv_dtype, dims->head_dim, p.group, stream)
-                     : pa::launch_valu(a, dims->q_dtype, dims->kv_dtype, dims->head_dim, p.group, stream);
+  if (!mfma && ev0 && hipEventRecord(ev0, stream) != hipSuccess) return PA_ERR_HIP;
+  hipError_t e = mfma ? pa::launch_mfma(a, dims->q_dtype, dims->kv_dtype, dims->head_dim, p.group, stream, ev0, ev1)
+                      : pa::launch_valu(a, dims->q_dtype, dims->kv_dtype, dims->head_dim, p.group, stream);
   if (e != hipSuccess) return PA_ERR_HIP;
-  if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return PA_ERR_HIP;
+  if (!mfma && ev1 && hipEventRecord(ev1, stream) != hipSuccess) return PA_ERR_HIP;
   if (p.max_parts > 1) {
     e = pa::launch_reduce(a, dims->q_dtype, dims->head_dim, p.group, stream);
     if (e != hipSuccess) return PA_ERR_HIP;

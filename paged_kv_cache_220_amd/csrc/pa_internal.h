@@ -48,8 +48,10 @@ struct Args {
 // Host-side launchers; each returns the hipError_t of the launch.
 hipError_t launch_valu(const Args& a, int q_dtype, int kv_dtype, int head_dim, int group,
                        hipStream_t stream);
+// ev_start / ev_stop (may be null): recorded by the partition kernel's own
+// dispatch at the start and end of its execution.
 hipError_t launch_mfma(const Args& a, int q_dtype, int kv_dtype, int head_dim, int group,
-                       hipStream_t stream);
+                       hipStream_t stream, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 hipError_t launch_reduce(const Args& a, int q_dtype, int head_dim, int group, hipStream_t stream);
 hipError_t launch_plan(const Args& a, hipStream_t stream);
 

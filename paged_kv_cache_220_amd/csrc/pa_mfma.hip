@@ -44,6 +44,8 @@
 // 16-bit operands (the rounded weight and its rounding residual), so the
 // weights carry about twice the operand precision into the fp32 accumulator.
 
+#include <hip/hip_ext.h>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -961,18 +963,28 @@ bool mfma_supported(int q_dtype, int kv_dtype, int head_dim, int group, int bloc
 
 namespace {
 
+// Timing events, when given, are attached to the kernel's own dispatch
+// (start and end of its execution) instead of being separate stream markers.
+struct Timing {
+  hipEvent_t start, stop;
+};
+
 template <int KDT, int NCG, int NW, bool ST, bool BS, int STG>
-void launch_one(const Args& a, int group, dim3 grid, bool queue, hipStream_t stream) {
-  if (queue) mfma_partition_list_kernel<KDT, NCG, NW, ST, BS, STG><<<grid, 64 * NW, 0, stream>>>(a, group);
-  else mfma_partition_kernel<KDT, NCG, NW, ST, BS, STG><<<grid, 64 * NW, 0, stream>>>(a, group);
+void launch_one(const Args& a, int group, dim3 grid, bool queue, hipStream_t stream, Timing tm) {
+  auto kern = queue ? mfma_partition_list_kernel<KDT, NCG, NW, ST, BS, STG>
+                    : mfma_partition_kernel<KDT, NCG, NW, ST, BS, STG>;
+  if (tm.start || tm.stop)
+    hipExtLaunchKernelGGL(kern, grid, dim3(64 * NW), 0, stream, tm.start, tm.stop, 0, a, group);
+  else
+    kern<<<grid, 64 * NW, 0, stream>>>(a, group);
 }
 
 template <int KDT, int NCG, int NW, bool ST, int STG = 0>
-void launch_scaled(const Args& a, int group, dim3 grid, bool queue, hipStream_t stream) {
-  if constexpr (KDT == kBF16) launch_one<KDT, NCG, NW, ST, false, STG>(a, group, grid, queue, stream);
-  else if constexpr (KDT == kI4) launch_one<KDT, NCG, NW, ST, true, STG>(a, group, grid, queue, stream);
-  else if (a.k_bscale != nullptr) launch_one<KDT, NCG, NW, ST, true, STG>(a, group, grid, queue, stream);
-  else launch_one<KDT, NCG, NW, ST, false, STG>(a, group, grid, queue, stream);
+void launch_scaled(const Args& a, int group, dim3 grid, bool queue, hipStream_t stream, Timing tm) {
+  if constexpr (KDT == kBF16) launch_one<KDT, NCG, NW, ST, false, STG>(a, group, grid, queue, stream, tm);
+  else if constexpr (KDT == kI4) launch_one<KDT, NCG, NW, ST, true, STG>(a, group, grid, queue, stream, tm);
+  else if (a.k_bscale != nullptr) launch_one<KDT, NCG, NW, ST, true, STG>(a, group, grid, queue, stream, tm);
+  else launch_one<KDT, NCG, NW, ST, false, STG>(a, group, grid, queue, stream, tm);
 }
 
 // LDS stages of the tile-sharing kernels (one wave per SIMD, so a CU holds
@@ -982,29 +994,31 @@ template <int KDT, int NW>
 constexpr int share_stages() { return (KDT == kBF16 && NW == 2) ? 2 : 4; }
 
 template <int KDT>
-void launch_kdt(const Args& a, int group, int ncg, int nw, bool share, dim3 grid, bool queue, hipStream_t stream) {
+void launch_kdt(const Args& a, int group, int ncg, int nw, bool share, dim3 grid, bool queue, hipStream_t stream,
+                Timing tm) {
   const bool st = a.q_blocks == 1;   // several query blocks: share tiles through the caches
   if (share) {
-    if (nw == 2 && st) launch_scaled<KDT, 4, 2, true, share_stages<KDT, 2>()>(a, group, grid, queue, stream);
-    else if (nw == 2) launch_scaled<KDT, 4, 2, false, share_stages<KDT, 2>()>(a, group, grid, queue, stream);
-    else if (st) launch_scaled<KDT, 4, 4, true, share_stages<KDT, 4>()>(a, group, grid, queue, stream);
-    else launch_scaled<KDT, 4, 4, false, share_stages<KDT, 4>()>(a, group, grid, queue, stream);
+    if (nw == 2 && st) launch_scaled<KDT, 4, 2, true, share_stages<KDT, 2>()>(a, group, grid, queue, stream, tm);
+    else if (nw == 2) launch_scaled<KDT, 4, 2, false, share_stages<KDT, 2>()>(a, group, grid, queue, stream, tm);
+    else if (st) launch_scaled<KDT, 4, 4, true, share_stages<KDT, 4>()>(a, group, grid, queue, stream, tm);
+    else launch_scaled<KDT, 4, 4, false, share_stages<KDT, 4>()>(a, group, grid, queue, stream, tm);
   }
-  else if (ncg == 1 && nw == 1) launch_scaled<KDT, 1, 1, true>(a, group, grid, queue, stream);
-  else if (ncg == 1 && nw == 2) launch_scaled<KDT, 1, 2, true>(a, group, grid, queue, stream);
-  else if (ncg == 1) launch_scaled<KDT, 1, 4, true>(a, group, grid, queue, stream);
-  else if (ncg == 2 && nw == 1) launch_scaled<KDT, 2, 1, true>(a, group, grid, queue, stream);
-  else if (ncg == 2) launch_scaled<KDT, 2, 2, true>(a, group, grid, queue, stream);
-  else if (nw == 1 && st) launch_scaled<KDT, 4, 1, true>(a, group, grid, queue, stream);
-  else if (nw == 1) launch_scaled<KDT, 4, 1, false>(a, group, grid, queue, stream);
-  else if (st) launch_scaled<KDT, 4, 2, true>(a, group, grid, queue, stream);
-  else launch_scaled<KDT, 4, 2, false>(a, group, grid, queue, stream);
+  else if (ncg == 1 && nw == 1) launch_scaled<KDT, 1, 1, true>(a, group, grid, queue, stream, tm);
+  else if (ncg == 1 && nw == 2) launch_scaled<KDT, 1, 2, true>(a, group, grid, queue, stream, tm);
+  else if (ncg == 1) launch_scaled<KDT, 1, 4, true>(a, group, grid, queue, stream, tm);
+  else if (ncg == 2 && nw == 1) launch_scaled<KDT, 2, 1, true>(a, group, grid, queue, stream, tm);
+  else if (ncg == 2) launch_scaled<KDT, 2, 2, true>(a, group, grid, queue, stream, tm);
+  else if (nw == 1 && st) launch_scaled<KDT, 4, 1, true>(a, group, grid, queue, stream, tm);
+  else if (nw == 1) launch_scaled<KDT, 4, 1, false>(a, group, grid, queue, stream, tm);
+  else if (st) launch_scaled<KDT, 4, 2, true>(a, group, grid, queue, stream, tm);
+  else launch_scaled<KDT, 4, 2, false>(a, group, grid, queue, stream, tm);
 }
 
 }  // namespace
 
 hipError_t launch_mfma(const Args& a, int q_dtype, int kv_dtype, int head_dim, int group,
-                       hipStream_t stream) {
+                       hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
+  const Timing tm{ev_start, ev_stop};
   if (!mfma_supported(q_dtype, kv_dtype, head_dim, group, kBlockSize, a.q_len)) return hipErrorInvalidValue;
   const int gv = group * a.q_len;                 // virtual heads per KV head, in blocks of up to 64
   const int ncg = gv <= 16 ? 1 : gv <= 32 ? 2 : 4;
@@ -1017,10 +1031,10 @@ hipError_t launch_mfma(const Args& a, int q_dtype, int kv_dtype, int head_dim, i
     return hipErrorInvalidValue;                  // int4 needs both scale arrays; bf16 takes none
   const bool queue = a.queue_items != nullptr;
   const dim3 grid = queue ? dim3((unsigned)a.queue_workgroups) : partition_grid(a);   // list: one per possible item
-  if (kv_dtype == kBF16) launch_kdt<kBF16>(a, group, ncg, nw, share, grid, queue, stream);
-  else if (kv_dtype == kE5M2) launch_kdt<kE5M2>(a, group, ncg, nw, share, grid, queue, stream);
-  else if (kv_dtype == kE4M3) launch_kdt<kE4M3>(a, group, ncg, nw, share, grid, queue, stream);
-  else launch_kdt<kI4>(a, group, ncg, nw, share, grid, queue, stream);
+  if (kv_dtype == kBF16) launch_kdt<kBF16>(a, group, ncg, nw, share, grid, queue, stream, tm);
+  else if (kv_dtype == kE5M2) launch_kdt<kE5M2>(a, group, ncg, nw, share, grid, queue, stream, tm);
+  else if (kv_dtype == kE4M3) launch_kdt<kE4M3>(a, group, ncg, nw, share, grid, queue, stream, tm);
+  else launch_kdt<kI4>(a, group, ncg, nw, share, grid, queue, stream, tm);
   return hipGetLastError();
 }
 
