@@ -226,3 +226,29 @@ def test_tile_sharing(kv, scaled, ql):
         outs[(ptok, nw)] = out.view(torch.int16).cpu().numpy()
     for nw in (2, 4):
         assert np.array_equal(outs[(128, nw)], outs[(128, 1)]), f"{nw} waves sharing tiles differ from one block per item"
+
+
+@pytest.mark.parametrize("kv", ["bf16", "e5m2", "int4"])
+def test_tile_sharing_poisoned(kv):
+    """Tile sharing over a pool whose unread blocks, tail slots and table padding
+    hold NaN (int4: NaN block scales and code -8): nothing outside the causal
+    window and the sequence may reach the output."""
+    w = W.make_workload("c2", num_seqs=6, poison=True, kv_dtype=kv)
+    ql = 12                                          # 96 pairs: two query blocks
+    rng = np.random.default_rng([ql, 73])
+    q = W.to_storage(rng.standard_normal((w.num_seqs, ql, w.num_heads, w.head_dim), dtype=np.float32), "bf16")
+    ref = np.concatenate([O.paged_attention_multi(q[s:s + 1], w.k_cache, w.v_cache, w.block_tables[s:s + 1],
+                                                  w.seq_lens[s:s + 1], w.num_kv_heads, w.scale, "bf16", kv,
+                                                  k_block_scales=w.k_block_scales,
+                                                  v_block_scales=w.v_block_scales)
+                          for s in range(w.num_seqs)])
+    dev = upload(w)
+    qd = _dev(q, "bf16")
+    for ptok, nw in ((0, 0), (64, 2), (128, 4)):
+        out = torch.full_like(qd, float("nan"))
+        log(f"case tile sharing poisoned {kv} P={ptok} waves={nw}")
+        B.pa_decode(qd, dev["k"], dev["v"], dev["tables"], dev["seq_lens"], w.num_kv_heads, float(w.scale), out,
+                    partition_tokens=ptok, max_seq_len=w.max_seq_len, kernel="mfma", waves_per_item=nw,
+                    k_block_scales=dev["k_block_scales"], v_block_scales=dev["v_block_scales"])
+        torch.cuda.synchronize()
+        check(out.float().cpu().numpy().astype(np.float64), ref, w, f"tile sharing poisoned {kv} P={ptok} waves={nw}")
