@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "PagedAttention decode: achieved HBM GB/s (% of peak) and seq·head/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # MI355X dense matrix / fp32 vector
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -294,6 +295,25 @@ def main():
     achieved = kv_bytes / (part_avg * 1e-3) / 1e9
     kname = "pa_mfma_partition" if plan["kernel"] == "mfma" else "pa_valu_partition"
     traffic = load_traffic(kname, batch, plan)
+    # Attention flops of the launch: QK and PV, 2 * head_dim each per attended
+    # (token, query position, query head); query i of q_len attends L - q_len + 1 + i
+    # tokens. The path is matrix-bound once flops per K/V byte pass the chip's
+    # ratio of the two peaks (bf16 / f16 operands on the matrix cores).
+    L = w.seq_lens.astype(np.float64)[:, None]
+    attended = np.maximum(0.0, L - args.q_len + 1 + np.arange(args.q_len)[None, :]).sum()
+    flops = 4.0 * w.head_dim * w.num_heads * attended
+    op_dtype = "bf16" if w.kv_dtype == "bf16" else ("f32" if w.kv_dtype == "f32" else "f16")
+    if plan["kernel"] != "mfma":
+        op_dtype = "f32"
+    mfma_peak = MFMA_PEAK_TFLOPS[op_dtype]
+    if flops / kv_bytes > mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9):
+        roofline = {"bound": "mfma" if op_dtype != "f32" else "alu", "kernel": kname,
+                    "achieved": round(flops / (part_avg * 1e-3) / 1e12, 2), "peak": mfma_peak,
+                    "unit": "TFLOP/s", "frac": round(flops / (part_avg * 1e-3) / 1e12 / mfma_peak, 4),
+                    "traffic": traffic}
+    else:
+        roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
     result = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -322,9 +342,7 @@ def main():
         "wall_ms_per_step": round(wall * 1e3 / K, 5),
         "partition_kernel_us": round(part_avg * 1e3, 2),
         "rest_of_step_us": round((ms_step - part_avg) * 1e3, 2),
-        "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic},
+        "roofline": roofline,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, args.q_len)
