@@ -122,8 +122,8 @@ typedef struct pa_dims {
                                   with several query rows; a query with no token gets
                                   a zero row). Matrix-core kernel only, q_len <= 4096:
                                   a KV head's group * q_len (position, head) pairs
-                                  are taken in blocks of up to 64. With more than one
-                                  block, the waves of a work item take one block each
+                                  are taken in blocks of up to 64 per work item. With
+                                  more, the waves of a work item take 32 pairs each
                                   and read every K/V tile once, through LDS (see
                                   waves_per_item).                                   */
   int32_t schedule;            /* pa_schedule_t                                        */
@@ -132,10 +132,11 @@ typedef struct pa_dims {
                                   group * q_len <= 64: the waves split the item's
                                   tiles and merge their states in LDS: 1, 2 or 4 (4
                                   only with group * q_len <= 16). group * q_len > 64:
-                                  2 or 4 waves take 2 or 4 query blocks of 64 pairs
-                                  each and share every K/V tile (default: 2 for two
-                                  blocks, else 4); 1 gives one block per item, each
-                                  reading the tiles itself.                          */
+                                  2, 4 or 8 waves take 32 (query position, head)
+                                  pairs each and share every K/V tile through LDS
+                                  (default: 4 for up to 128 pairs, else 8); 1 gives
+                                  one block of 64 pairs per item, each block reading
+                                  the tiles itself.                                  */
   const float* k_block_scales; /* device, [num_blocks][num_kv_heads] float32: the K
                                   values of physical block b, KV head g are multiplied
                                   by k_block_scales[b * num_kv_heads + g]. Required for

@@ -56,7 +56,8 @@ int check_dims(const pa_dims_t* d, int32_t hkv) {
   if (!aligned(d->k_block_scales, 4) || !aligned(d->v_block_scales, 4)) return PA_ERR_ALIGN;
   if (d->kernel < PA_KERNEL_AUTO || d->kernel > PA_KERNEL_MFMA) return PA_ERR_UNSUPPORTED;
   if (d->schedule < PA_SCHEDULE_AUTO || d->schedule > PA_SCHEDULE_QUEUE) return PA_ERR_UNSUPPORTED;
-  if (d->waves_per_item != 0 && d->waves_per_item != 1 && d->waves_per_item != 2 && d->waves_per_item != 4)
+  if (d->waves_per_item != 0 && d->waves_per_item != 1 && d->waves_per_item != 2 && d->waves_per_item != 4 &&
+      d->waves_per_item != 8)
     return PA_ERR_UNSUPPORTED;
   if (d->block_size != pa::kBlockSize) return PA_ERR_UNSUPPORTED;
   const int group = d->num_heads / hkv;
@@ -87,17 +88,18 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
   }
   p->max_len = d->max_seq_len > 0 ? d->max_seq_len : d->max_blocks_per_seq * d->block_size;
   // Query blocks (up to 64 (query position, head) pairs each). With more than
-  // one, the matrix-core kernel by default gives an item 2 or 4 of them, one
-  // per wave, and the waves share every K/V tile; waves_per_item = 1 keeps
-  // one block per item.
+  // one, the matrix-core kernel by default gives an item 4 or 8 waves of 32
+  // pairs each, and the waves share every K/V tile; waves_per_item = 1 keeps
+  // one block of 64 per item.
   const int gv = p->group * p->q_len;   // (query position, head) pairs per KV head
   const int ncg = gv <= 16 ? 1 : gv <= 32 ? 2 : 4;
   const int blocks64 = (gv + 16 * pa::kMaxColumnGroups - 1) / (16 * pa::kMaxColumnGroups);
   const bool mfma = p->kernel == PA_KERNEL_MFMA;
   int share_nw = 0;   // waves per item when they share tiles
   if (mfma && blocks64 > 1 && d->waves_per_item != 1) {
-    share_nw = d->waves_per_item > 0 ? d->waves_per_item : (blocks64 == 2 ? 2 : 4);
-    if (!pa::mfma_share_tiles(p->group, p->q_len, share_nw)) return PA_ERR_UNSUPPORTED;
+    share_nw = d->waves_per_item > 0 ? d->waves_per_item : pa::mfma_share_default_waves(p->group, p->q_len);
+    if (!pa::mfma_share_tiles(p->group, p->q_len, share_nw) || share_nw > pa::kShareMaxWaves)
+      return PA_ERR_UNSUPPORTED;
   }
   p->q_blocks = mfma ? pa::mfma_item_blocks(p->group, p->q_len, share_nw > 0 ? share_nw : 1) : 1;
   // Every wave keeps about one 64-token tile of K and V in flight. Covering
@@ -110,8 +112,7 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
   // are shortened only when even 4 waves per item would not reach the target.
   const long long units = (long long)d->num_seqs * hkv * (p->kernel == PA_KERNEL_MFMA ? p->q_blocks : 1);
   // three waves per SIMD: fp8 without per-block scales and int4 (with them).
-  // The tile-sharing kernels run one wave per SIMD (1024 on the chip); their
-  // target is two rounds of items.
+  // The tile-sharing kernels run two waves per SIMD (2048 on the chip).
   const bool fp8 = d->kv_dtype == PA_DTYPE_FP8_E5M2 || d->kv_dtype == PA_DTYPE_FP8_E4M3;
   const bool three_waves = (fp8 && d->k_block_scales == nullptr) || d->kv_dtype == PA_DTYPE_INT4;
   const long long target_waves = share_nw > 0 ? 2048 : three_waves ? 3072 : 2048;

@@ -63,10 +63,18 @@ bool mfma_waves_supported(int group, int q_len, int nw);
 bool mfma_share_tiles(int group, int q_len, int nw);
 // Work items per (sequence, KV head) of the matrix-core kernel (Args::q_blocks).
 int mfma_item_blocks(int group, int q_len, int nw);
+// Waves per item the planner takes for tile sharing.
+int mfma_share_default_waves(int group, int q_len);
 
 constexpr int kBlockSize = 16;     // tokens per physical block handled by the kernels
 constexpr int kTileTokens = 64;    // partition lengths are multiples of this
 constexpr int kMaxColumnGroups = 4; // matrix-core kernel: up to 64 (query position, head) pairs per work item
+#ifndef PA_SHARE_GROUPS
+#define PA_SHARE_GROUPS 2
+#endif
+// Tile sharing: column groups (16 pairs each) per wave, and the most waves per item.
+constexpr int kShareGroups = PA_SHARE_GROUPS;
+constexpr int kShareMaxWaves = kShareGroups == 2 ? 8 : 4;
 constexpr int kMaxQueryLen = 4096;  // query positions per sequence
 constexpr int kMaxQueueBuckets = 129;  // queue schedule: partitions of at most 128 tiles
 constexpr int kResidentWorkgroups = 2048;  // gfx950: 256 CUs x 8 one-wave workgroups (planning)

@@ -318,7 +318,8 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
 
   // NW waves share the item: without tile sharing wave w takes tiles w, w + NW, ...
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int v0 = 16 * kMaxColumnGroups * (kShare ? qb * NW + wave : qb);   // first virtual head of this query block
+  // first virtual head of this wave's query block
+  const int v0 = kShare ? 16 * NCG * (qb * NW + wave) : 16 * kMaxColumnGroups * qb;
   const int lane = threadIdx.x & 63;
   const int c = lane >> 4;   // lane group: k slots of the operands, rows 4c..4c+3 of results
   const int n = lane & 15;   // MFMA row of A (quartet / head_dim row) and column of B (virtual head)
@@ -601,6 +602,50 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     }
   };
 
+  // One tile of the tile-sharing kernels with at most two column groups per
+  // wave (two waves per SIMD): operands are read from the LDS stage `st` as
+  // they are used (K a k-step at a time, V one 8-token row segment at a time)
+  // and the other wave on the SIMD covers the LDS latency. Per column the
+  // arithmetic and its order are those of tile_step.
+  auto share_tile = [&](const uint8_t* st, const int t0, const float (&ksc)[2], const float (&vsc)[2])
+      __attribute__((always_inline)) {
+    const uint8_t* krow = st + kblk * kSlotBlk + c * kRowBytes + ktok * M::kBits / 8;
+    f32x4 sacc[NCG][4];
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      kload_t kr[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) kr[r] = *reinterpret_cast<const kload_t*>(krow + (32 * ks + 4 * r) * kRowBytes);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const op_t kop = M::k_operand(kr, j);
+#pragma unroll
+        for (int cg = 0; cg < NCG; ++cg)
+          sacc[cg][j] = M::mma(kop, qop[cg][ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[cg][j]);
+      }
+    }
+    op_t phi[NCG][2], plo[NCG][2];
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) softmax(cg, sacc[cg], t0, phi[cg], plo[cg], ksc, vsc);
+    const int nvalid = tok1 - t0;   // tokens of this tile inside the partition (may exceed 64)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const uint8_t* vrow = st + (4 + (c >> 1) + 2 * hh) * kSlotBlk + n * kRowBytes + 8 * (c & 1) * M::kBits / 8;
+      const int nv = min(8, max(0, nvalid - (16 * ((c >> 1) + 2 * hh) + 8 * (c & 1))));
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        vload_t x = *reinterpret_cast<const vload_t*>(vrow + 16 * dt * kRowBytes);
+        if (nvalid < kTile) x = M::mask_v(x, nv);   // 0 * NaN would poison the sum
+        const op_t vop = M::v_operand(x);
+#pragma unroll
+        for (int cg = 0; cg < NCG; ++cg) {
+          oacc[cg][dt] = M::mma(vop, phi[cg][hh], oacc[cg][dt]);
+          oacc[cg][dt] = M::mma(vop, plo[cg][hh], oacc[cg][dt]);
+        }
+      }
+    }
+  };
+
   // Helpers of the LDS-staged loops. The four block ids of a tile are the
   // same for the whole wave. They (and the per-block scales) are read through
   // the constant address space, so they become scalar loads even where the
@@ -696,6 +741,10 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
             ksc[0] = ksc[1] = vsc[0] = vsc[1] = 1.f;
           }
           const uint8_t* st = &kv_lds[i % STAGES][0];
+          if constexpr (NCG <= 2) {
+            share_tile(st, t0, ksc, vsc);
+            continue;
+          }
           const uint8_t* krow = st + kblk * kSlotBlk + c * kRowBytes + ktok * M::kBits / 8;
           Tile T;
 #pragma unroll
@@ -910,8 +959,9 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
 
 // One column group fits two waves per SIMD (<= 256 registers per lane), so
 // one wave's compute overlaps the other's loads; more groups take one wave.
-#define PA_MFMA_KERNEL_ATTRS \
-  __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NCG == 1 ? 2 : 1, 8)))
+#define PA_MFMA_KERNEL_ATTRS                                          \
+  __global__ __launch_bounds__(64 * NW)                               \
+  __attribute__((amdgpu_waves_per_eu((NCG == 1 || (STAGES > 0 && NCG == 2)) ? 2 : 1, 8)))
 
 // Grid schedule: one workgroup per (KV head, sequence, partition) of the dense grid.
 template <int KDT, int NCG, int NW, bool STREAM, bool BSCALE, int STAGES>
@@ -942,8 +992,17 @@ bool mfma_share_tiles(int group, int q_len, int nw) {
 }
 
 int mfma_item_blocks(int group, int q_len, int nw) {
-  const int blocks = (group * q_len + 16 * kMaxColumnGroups - 1) / (16 * kMaxColumnGroups);
-  return mfma_share_tiles(group, q_len, nw) ? (blocks + nw - 1) / nw : blocks;
+  const int gv = group * q_len;
+  if (mfma_share_tiles(group, q_len, nw)) {
+    const int per_wave = 16 * kShareGroups;
+    return ((gv + per_wave - 1) / per_wave + nw - 1) / nw;
+  }
+  return (gv + 16 * kMaxColumnGroups - 1) / (16 * kMaxColumnGroups);
+}
+
+int mfma_share_default_waves(int group, int q_len) {
+  const int blocks = (group * q_len + 16 * kShareGroups - 1) / (16 * kShareGroups);
+  return blocks <= 2 ? 2 : blocks <= 4 || kShareMaxWaves == 4 ? 4 : 8;
 }
 
 // Waves per item: 1, 2 or 4 with one column group; 1 or 2 with two or four
@@ -951,7 +1010,7 @@ int mfma_item_blocks(int group, int q_len, int nw) {
 // block the waves share tiles instead: 2 or 4, one block each.
 bool mfma_waves_supported(int group, int q_len, int nw) {
   const int gv = group * q_len;
-  if (gv > 16 * kMaxColumnGroups) return nw == 1 || nw == 2 || nw == 4;
+  if (gv > 16 * kMaxColumnGroups) return nw == 1 || nw == 2 || nw == 4 || (nw == 8 && kShareMaxWaves == 8);
   return nw == 1 || nw == 2 || (nw == 4 && gv <= 16);
 }
 
@@ -987,21 +1046,31 @@ void launch_scaled(const Args& a, int group, dim3 grid, bool queue, hipStream_t 
   else launch_one<KDT, NCG, NW, ST, false, STG>(a, group, grid, queue, stream, tm);
 }
 
-// LDS stages of the tile-sharing kernels (one wave per SIMD, so a CU holds
-// four waves): four, except for bf16 with two waves, where two stages of
-// 33 KiB let two workgroups share a CU's LDS.
+// LDS stages of the tile-sharing kernels. Four column groups per wave: one
+// wave per SIMD, a CU holds four waves; four stages, except for bf16 with two
+// waves, where two stages of 33 KiB let two workgroups share a CU's LDS. Two
+// groups per wave: two waves per SIMD, eight per CU; a workgroup of fewer than
+// eight waves shares the CU, so bf16 takes two stages there.
 template <int KDT, int NW>
-constexpr int share_stages() { return (KDT == kBF16 && NW == 2) ? 2 : 4; }
+constexpr int share_stages() {
+  if constexpr (kShareGroups == 2) return (KDT == kBF16 && NW < 8) ? 2 : 4;
+  else return (KDT == kBF16 && NW == 2) ? 2 : 4;
+}
 
 template <int KDT>
 void launch_kdt(const Args& a, int group, int ncg, int nw, bool share, dim3 grid, bool queue, hipStream_t stream,
                 Timing tm) {
   const bool st = a.q_blocks == 1;   // several query blocks: share tiles through the caches
   if (share) {
-    if (nw == 2 && st) launch_scaled<KDT, 4, 2, true, share_stages<KDT, 2>()>(a, group, grid, queue, stream, tm);
-    else if (nw == 2) launch_scaled<KDT, 4, 2, false, share_stages<KDT, 2>()>(a, group, grid, queue, stream, tm);
-    else if (st) launch_scaled<KDT, 4, 4, true, share_stages<KDT, 4>()>(a, group, grid, queue, stream, tm);
-    else launch_scaled<KDT, 4, 4, false, share_stages<KDT, 4>()>(a, group, grid, queue, stream, tm);
+    constexpr int G = kShareGroups;
+    if (nw == 2 && st) launch_scaled<KDT, G, 2, true, share_stages<KDT, 2>()>(a, group, grid, queue, stream, tm);
+    else if (nw == 2) launch_scaled<KDT, G, 2, false, share_stages<KDT, 2>()>(a, group, grid, queue, stream, tm);
+    else if (nw == 4 && st) launch_scaled<KDT, G, 4, true, share_stages<KDT, 4>()>(a, group, grid, queue, stream, tm);
+    else if (nw == 4) launch_scaled<KDT, G, 4, false, share_stages<KDT, 4>()>(a, group, grid, queue, stream, tm);
+    else if constexpr (kShareMaxWaves == 8) {
+      if (st) launch_scaled<KDT, G, 8, true, share_stages<KDT, 8>()>(a, group, grid, queue, stream, tm);
+      else launch_scaled<KDT, G, 8, false, share_stages<KDT, 8>()>(a, group, grid, queue, stream, tm);
+    }
   }
   else if (ncg == 1 && nw == 1) launch_scaled<KDT, 1, 1, true>(a, group, grid, queue, stream, tm);
   else if (ncg == 1 && nw == 2) launch_scaled<KDT, 1, 2, true>(a, group, grid, queue, stream, tm);

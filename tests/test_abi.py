@@ -91,7 +91,10 @@ def status_of(d, hkv=8):
     (dict(schedule=2), 8, B.PA_OK),
     (dict(waves_per_item=3), 8, B.PA_ERR_UNSUPPORTED),
     (dict(waves_per_item=4, q_len=4), 8, B.PA_ERR_UNSUPPORTED),  # 4 waves with one column group only
-    (dict(waves_per_item=4, q_len=9), 8, B.PA_OK),               # two query blocks: 4 waves share tiles
+    (dict(waves_per_item=4, q_len=9), 8, B.PA_OK),               # 72 pairs: 4 waves share tiles
+    (dict(waves_per_item=8, q_len=9), 8, B.PA_OK),
+    (dict(waves_per_item=8, q_len=8), 8, B.PA_ERR_UNSUPPORTED),  # 64 pairs: one item, no sharing
+    (dict(waves_per_item=16, q_len=64), 8, B.PA_ERR_UNSUPPORTED),
     (dict(waves_per_item=1, q_len=9), 8, B.PA_OK),
     (dict(waves_per_item=2, kernel=1), 8, B.PA_ERR_UNSUPPORTED),
     (dict(waves_per_item=4), 8, B.PA_OK),
@@ -145,21 +148,21 @@ def test_plan_schedule_choice():
     # 16 x 8 units x 8 partitions = 1024 workgroups: dense grid
     assert B.plan(dims(), 8)["schedule"] == "grid"
     # 256 x 8 units x 8 partitions = 16384 >> 2048 resident workgroups: work queue
-    # query blocks: 8 heads x 16 positions = 128 pairs per KV head -> 2 blocks of
-    # 64, by default one item whose 2 waves share the tiles
+    # query blocks: 8 heads x 16 positions = 128 pairs per KV head; with tile
+    # sharing each wave takes 32 pairs, so by default one item of 4 waves
     pq = B.plan(dims(num_seqs=4, max_seq_len=4096, q_len=16), 8)
-    assert pq["waves_per_item"] == 2 and pq["grid_workgroups"] == 4 * 8 * 1 * pq["max_partitions"]
-    assert pq["partition_tokens"] == 256                                 # 512 items x 2 waves: shortest partitions
+    assert pq["waves_per_item"] == 4 and pq["grid_workgroups"] == 4 * 8 * 1 * pq["max_partitions"]
+    assert pq["partition_tokens"] == 256                                 # 512 items x 4 waves: 2048
     pq1 = B.plan(dims(num_seqs=4, max_seq_len=4096, q_len=16, waves_per_item=1), 8)
     assert pq1["waves_per_item"] == 1 and pq1["grid_workgroups"] == 4 * 8 * 2 * pq1["max_partitions"]
-    # 64 heads, one KV head, 3 positions: 192 pairs -> 3 blocks, one 4-wave item
+    # 64 heads, one KV head, 3 positions: 192 pairs -> 6 wave blocks, one 8-wave item
     pm = B.plan(dims(num_seqs=2, max_seq_len=2048, q_len=3), 1)
-    assert pm["waves_per_item"] == 4 and pm["grid_workgroups"] == 2 * 1 * 1 * pm["max_partitions"]
+    assert pm["waves_per_item"] == 8 and pm["grid_workgroups"] == 2 * 1 * 1 * pm["max_partitions"]
     pm2 = B.plan(dims(num_seqs=2, max_seq_len=2048, q_len=3, waves_per_item=2), 1)
-    assert pm2["waves_per_item"] == 2 and pm2["grid_workgroups"] == 2 * 1 * 2 * pm2["max_partitions"]
-    # prefill chunk: 8 heads x 64 positions = 8 blocks -> 2 items of 4 waves per KV head
+    assert pm2["waves_per_item"] == 2 and pm2["grid_workgroups"] == 2 * 1 * 3 * pm2["max_partitions"]
+    # prefill chunk: 8 heads x 64 positions = 16 wave blocks -> 2 items of 8 waves per KV head
     pp = B.plan(dims(num_seqs=128, max_seq_len=512, max_blocks_per_seq=32, q_len=64), 8)
-    assert pp["waves_per_item"] == 4 and pp["grid_workgroups"] == 128 * 8 * 2 and pp["max_partitions"] == 1
+    assert pp["waves_per_item"] == 8 and pp["grid_workgroups"] == 128 * 8 * 2 and pp["max_partitions"] == 1
     p = B.plan(dims(num_seqs=256, max_seq_len=32657), 8)
     assert p["schedule"] == "queue" and p["partition_tokens"] == 4096 and p["waves_per_item"] == 4
     g = B.plan(dims(num_seqs=256, max_seq_len=32657, schedule=1), 8)

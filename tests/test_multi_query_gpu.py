@@ -194,8 +194,8 @@ def test_tile_sharing(kv, scaled, ql):
     """Waves of one work item take one query block each and share every K/V
     tile through LDS: partitions of 1, 2 and 4 tiles (fewer tiles than LDS
     stages), lengths shorter than the query window, both schedules. The result
-    of a query block does not depend on how many blocks share its tiles: 1, 2
-    and 4 waves per item give the same bits."""
+    of a query does not depend on how many waves share its tiles: 1, 2, 4 and
+    8 waves per item give the same bits."""
     w = W.random_edge_workload(70 + ql, S=4, H=64, Hkv=8, D=128, seq_lens=[1000, 65, 1, 300], kv_dtype=kv)
     rng = np.random.default_rng([ql, 71])
     if scaled and kv != "int4":
@@ -213,7 +213,7 @@ def test_tile_sharing(kv, scaled, ql):
     qd = _dev(q, "bf16")
     outs = {}
     for ptok, sched, nw in ((0, "auto", 0), (64, "grid", 2), (128, "grid", 4), (128, "grid", 2), (128, "grid", 1),
-                            (256, "queue", 4), (64, "grid", 1)):
+                            (128, "grid", 8), (256, "queue", 8), (64, "grid", 1)):
         out = torch.full_like(qd, float("nan"))
         log(f"case tile sharing {kv} scaled={scaled} q_len={ql} P={ptok} {sched} waves={nw}")
         B.pa_decode(qd, dev["k"], dev["v"], dev["tables"], dev["seq_lens"], w.num_kv_heads, float(w.scale), out,
@@ -224,7 +224,7 @@ def test_tile_sharing(kv, scaled, ql):
         got = out.float().cpu().numpy().astype(np.float64)
         check(got, ref, w, f"tile sharing {kv} q_len={ql} P={ptok} {sched} waves={nw}")
         outs[(ptok, nw)] = out.view(torch.int16).cpu().numpy()
-    for nw in (2, 4):
+    for nw in (2, 4, 8):
         assert np.array_equal(outs[(128, nw)], outs[(128, 1)]), f"{nw} waves sharing tiles differ from one block per item"
 
 
