@@ -130,8 +130,9 @@ typedef struct pa_dims {
   int32_t waves_per_item;      /* matrix-core kernel: waves that share one (sequence,
                                   KV head, partition) item; 0 = chosen by the library.
                                   group * q_len <= 64: the waves split the item's
-                                  tiles and merge their states in LDS: 1, 2 or 4 (4
-                                  only with group * q_len <= 16). group * q_len > 64:
+                                  tiles and merge their states in LDS: 1, 2, 3 or 4
+                                  (3 and 4 only with group * q_len <= 16). group *
+                                  q_len > 64:
                                   2, 4 or 8 waves take 32 (query position, head)
                                   pairs each and share every K/V tile through LDS
                                   (default: 4 for up to 128 pairs, else 8); 1 gives

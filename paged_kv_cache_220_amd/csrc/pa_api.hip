@@ -56,8 +56,8 @@ int check_dims(const pa_dims_t* d, int32_t hkv) {
   if (!aligned(d->k_block_scales, 4) || !aligned(d->v_block_scales, 4)) return PA_ERR_ALIGN;
   if (d->kernel < PA_KERNEL_AUTO || d->kernel > PA_KERNEL_MFMA) return PA_ERR_UNSUPPORTED;
   if (d->schedule < PA_SCHEDULE_AUTO || d->schedule > PA_SCHEDULE_QUEUE) return PA_ERR_UNSUPPORTED;
-  if (d->waves_per_item != 0 && d->waves_per_item != 1 && d->waves_per_item != 2 && d->waves_per_item != 4 &&
-      d->waves_per_item != 8)
+  if (d->waves_per_item < 0 || d->waves_per_item > 8 || d->waves_per_item == 5 || d->waves_per_item == 6 ||
+      d->waves_per_item == 7)
     return PA_ERR_UNSUPPORTED;
   if (d->block_size != pa::kBlockSize) return PA_ERR_UNSUPPORTED;
   const int group = d->num_heads / hkv;
@@ -161,10 +161,12 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
     p->waves_per_item = ncg == 1 ? 4 : 2;
   } else {
     const long long tiles = (std::min<long long>(P, p->max_len) + pa::kTileTokens - 1) / pa::kTileTokens;
+    // the most waves (1 to 4) for which the grid fits the target and every
+    // wave keeps at least 4 tiles: 3 fills the three waves per SIMD of the fp8
+    // and int4 kernels when the grid is a third of them
     int nw = 1;
-    while (nw < 4 && p->grid * 2 * nw <= target_waves && tiles >= 4LL * 2 * nw &&
-           pa::mfma_waves_supported(p->group, p->q_len, 2 * nw))
-      nw *= 2;
+    for (int w = 2; w <= 4; ++w)
+      if (p->grid * w <= target_waves && tiles >= 4LL * w && pa::mfma_waves_supported(p->group, p->q_len, w)) nw = w;
     p->waves_per_item = nw;
   }
   size_t off = 0;

@@ -1005,13 +1005,13 @@ int mfma_share_default_waves(int group, int q_len) {
   return blocks <= 2 ? 2 : blocks <= 4 || kShareMaxWaves == 4 ? 4 : 8;
 }
 
-// Waves per item: 1, 2 or 4 with one column group; 1 or 2 with two or four
+// Waves per item: 1 to 4 with one column group; 1 or 2 with two or four
 // (the LDS exchange holds (NW - 1) x NCG x 8 KiB). With more than one query
-// block the waves share tiles instead: 2 or 4, one block each.
+// block the waves share tiles instead: 2, 4 or 8.
 bool mfma_waves_supported(int group, int q_len, int nw) {
   const int gv = group * q_len;
   if (gv > 16 * kMaxColumnGroups) return nw == 1 || nw == 2 || nw == 4 || (nw == 8 && kShareMaxWaves == 8);
-  return nw == 1 || nw == 2 || (nw == 4 && gv <= 16);
+  return nw == 1 || nw == 2 || ((nw == 3 || nw == 4) && gv <= 16);
 }
 
 bool mfma_supported(int q_dtype, int kv_dtype, int head_dim, int group, int block_size, int q_len) {
@@ -1074,6 +1074,7 @@ void launch_kdt(const Args& a, int group, int ncg, int nw, bool share, dim3 grid
   }
   else if (ncg == 1 && nw == 1) launch_scaled<KDT, 1, 1, true>(a, group, grid, queue, stream, tm);
   else if (ncg == 1 && nw == 2) launch_scaled<KDT, 1, 2, true>(a, group, grid, queue, stream, tm);
+  else if (ncg == 1 && nw == 3) launch_scaled<KDT, 1, 3, true>(a, group, grid, queue, stream, tm);
   else if (ncg == 1) launch_scaled<KDT, 1, 4, true>(a, group, grid, queue, stream, tm);
   else if (ncg == 2 && nw == 1) launch_scaled<KDT, 2, 1, true>(a, group, grid, queue, stream, tm);
   else if (ncg == 2) launch_scaled<KDT, 2, 2, true>(a, group, grid, queue, stream, tm);

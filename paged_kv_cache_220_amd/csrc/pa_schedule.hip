@@ -21,6 +21,7 @@ constexpr int kPlanThreads = 1024;
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const Args a) {
   __shared__ int cnt[kMaxQueueBuckets];
   __shared__ int cur[kMaxQueueBuckets];
+  __shared__ int scan[kMaxQueueBuckets];
   const int tid = threadIdx.x;
   const int P = a.partition_tokens;
   const int full = P / kTileTokens;             // bucket of a full partition
@@ -38,14 +39,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const Args a) {
     if (rem > 0 || L == 0) atomicAdd(&cnt[(rem + kTileTokens - 1) / kTileTokens], units_per_seq);
   }
   __syncthreads();
-  if (tid == 0) {
-    int off = 0;
-    for (int b = full; b >= 0; --b) {
-      cur[b] = off;
-      off += cnt[b];
-    }
-    *const_cast<int*>(a.queue_len) = off;
+  // Bucket offsets, longest first: an exclusive prefix sum over ranks
+  // r = full - b (Hillis-Steele in LDS; a serial loop over up to 129 buckets
+  // in one thread cost several microseconds of dependent LDS round trips).
+  const int v = tid <= full ? cnt[full - tid] : 0;
+  if (tid <= full) scan[tid] = v;
+  __syncthreads();
+  for (int d = 1; d <= full; d <<= 1) {
+    const int add = (tid <= full && tid >= d) ? scan[tid - d] : 0;
+    __syncthreads();
+    if (tid <= full) scan[tid] += add;
+    __syncthreads();
   }
+  if (tid <= full) cur[full - tid] = scan[tid] - v;
+  if (tid == full) *const_cast<int*>(a.queue_len) = scan[tid];
   __syncthreads();
   // Each sequence reserves its items of a bucket as one run (one LDS atomic
   // per bucket it touches, not one per item) and fills the run in order.

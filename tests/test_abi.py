@@ -89,7 +89,9 @@ def status_of(d, hkv=8):
     (dict(schedule=2, kernel=1), 8, B.PA_ERR_UNSUPPORTED),       # queue: matrix-core kernel only
     (dict(schedule=2, partition_tokens=16384), 8, B.PA_ERR_UNSUPPORTED),   # > 128 tiles per item
     (dict(schedule=2), 8, B.PA_OK),
-    (dict(waves_per_item=3), 8, B.PA_ERR_UNSUPPORTED),
+    (dict(waves_per_item=3), 8, B.PA_OK),
+    (dict(waves_per_item=3, q_len=4), 8, B.PA_ERR_UNSUPPORTED),  # 3 waves with one column group only
+    (dict(waves_per_item=5), 8, B.PA_ERR_UNSUPPORTED),
     (dict(waves_per_item=4, q_len=4), 8, B.PA_ERR_UNSUPPORTED),  # 4 waves with one column group only
     (dict(waves_per_item=4, q_len=9), 8, B.PA_OK),               # 72 pairs: 4 waves share tiles
     (dict(waves_per_item=8, q_len=9), 8, B.PA_OK),
@@ -130,9 +132,9 @@ def test_plan_long_context():
     items = 16 * 8 * 8 * 8
     assert p["workspace_bytes"] >= items * (128 + 2) * 4
     assert p["waves_per_item"] == 2                                      # 1024 items x 2 = 2048 waves
-    # fp8 runs 3 waves per SIMD (3072 resident): 1024 items x 2 waves; 4 would not fit at once
+    # fp8 runs 3 waves per SIMD (3072 resident): 1024 items x 3 waves fill them; 4 would not fit at once
     pf = B.plan(dims(num_seqs=128, max_blocks_per_seq=256, kv_dtype=B.PA_DTYPE_FP8_E5M2), 8)
-    assert pf["partition_tokens"] == 4096 and pf["grid_workgroups"] == 8 * 128 and pf["waves_per_item"] == 2
+    assert pf["partition_tokens"] == 4096 and pf["grid_workgroups"] == 8 * 128 and pf["waves_per_item"] == 3
     # one sequence: partitions shrink until 4 waves per item would reach 2048 waves
     p1 = B.plan(dims(num_seqs=1), 8)
     assert p1["partition_tokens"] == 512 and p1["grid_workgroups"] == 512 and p1["waves_per_item"] == 2

@@ -200,19 +200,19 @@ WAVES = [("c2", dict(num_seqs=12), 512), ("c3", dict(num_seqs=2, seq_len=4100), 
 
 @pytest.mark.parametrize("name,kw,ptok", WAVES, ids=[f"{c[0]}{c[1].get('kv_dtype', '')}-P{c[2]}" for c in WAVES])
 def test_waves_per_item(name, kw, ptok):
-    """Items split over 1, 2 or 4 waves (tiles strided over the waves, states
+    """Items split over 1 to 4 waves (tiles strided over the waves, states
     merged in LDS) all match the oracle, on both schedules."""
     w = W.make_workload(name, **kw)
     dev = upload(w)
     ref = oracle_full(w)
-    for nw in (1, 2, 4):
+    for nw in (1, 2, 3, 4):
         for sched in ("grid", "queue"):
             log(f"case waves {name}{kw} P={ptok} waves={nw} {sched}")
             got = run_gpu(w, dev, kernel="mfma", partition_tokens=ptok, schedule=sched, waves_per_item=nw)
             check(got, ref, w, f"waves {name} P={ptok} waves={nw} {sched}")
 
 
-@pytest.mark.parametrize("kv_dtype", ["bf16", "e5m2", "e4m3"])
+@pytest.mark.parametrize("kv_dtype", ["bf16", "e5m2", "e4m3", "int4"])
 def test_waves_per_item_edge_lengths(kv_dtype):
     """Waves past the end of a short item contribute an empty state; partial
     last tiles and blocks past the partition end are masked (fp8 K through LDS too)."""
@@ -220,7 +220,7 @@ def test_waves_per_item_edge_lengths(kv_dtype):
                                seq_lens=[0, 1, 15, 16, 17, 63, 64, 65, 129, 300])
     ref = oracle_full(w)
     dev = upload(w)
-    for nw in (1, 2, 4):
+    for nw in (1, 2, 3, 4):
         for ptok in (64, 128, 256):
             got = run_gpu(w, dev, kernel="mfma", partition_tokens=ptok, waves_per_item=nw)
             check(got, ref, w, f"waves edge P={ptok} waves={nw}")
