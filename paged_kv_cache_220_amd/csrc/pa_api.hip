@@ -108,7 +108,7 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
   // with fp8 and int4 tiles (16 / 8 KiB; those kernels stage K in LDS and run
   // three waves per SIMD, fp8 with per-block scales two). Partitions are made as long as
   // possible (up to 4096 tokens: start-up and merge traffic are amortised) and
-  // the waves come from splitting each item over 1, 2 or 4 waves; partitions
+  // the waves come from splitting each item over 1 to 4 waves; partitions
   // are shortened only when even 4 waves per item would not reach the target.
   const long long units = (long long)d->num_seqs * hkv * (p->kernel == PA_KERNEL_MFMA ? p->q_blocks : 1);
   // three waves per SIMD: fp8 without per-block scales and int4 (with them).
