@@ -221,14 +221,20 @@ template <> struct Mfma<kI4> {
     }
     return __builtin_bit_cast(op_t, x);
   }
+  // V: the 8 tokens of a row segment enter the MFMA in the order kVTok, half
+  // of them (kVHigh) at scale 16 (nibble left at bits 4..7); P is fed in the
+  // same order with those weights divided by 16, so each product is
+  // p * u * 2^-24. Two masks and a shift per 8 values, no byte permutes.
+  static constexpr int kVTok[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+  static constexpr bool kVHigh[8] = {false, false, true, true, false, false, true, true};
   static __device__ __forceinline__ op_t v_operand(vload_t x) {
     const uint32_t w = x ^ 0x88888888u;
-    const uint32_t lo = w & 0x0F0F0F0Fu;          // even tokens, one per byte
-    const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;   // odd tokens
+    const uint32_t s = w >> 8;
     u32x4 y;
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-      y[p] = __builtin_amdgcn_perm(hi, lo, uint32_t(p) | (0x0Cu << 8) | (uint32_t(4 + p) << 16) | (0x0Cu << 24));
+    y[0] = w & 0x000F000Fu;   // tokens 0, 4
+    y[1] = w & 0x00F000F0u;   // tokens 1, 5 (x16)
+    y[2] = s & 0x000F000Fu;   // tokens 2, 6
+    y[3] = s & 0x00F000F0u;   // tokens 3, 7 (x16)
     return __builtin_bit_cast(op_t, y);
   }
   static __device__ __forceinline__ vload_t mask_v(vload_t x, int nvalid) {
@@ -522,27 +528,33 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     l_run[cg] = l_run[cg] * alpha + psum;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) oacc[cg][dt] *= alpha;
-    // PV instruction hh takes quartets r = 2hh, 2hh+1
-    float pvsum = 0.f;
+    // PV instruction hh takes quartets r = 2hh, 2hh+1 (token i of the lane's
+    // 8-token segment is p[2hh + i / 4][i % 4])
+    float pv_lo = 0.f, pv_hi = 0.f;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       float pv[8];
+      if constexpr (KDT == kI4) {
+        // int4: tokens in the V operand's order, the scale-16 ones divided by 16
+        // (exactly); the sums add exactly the rounded values PV receives (the
+        // empty asm keeps the compiler from fusing the product into the sum,
+        // which it would do in some instantiations and not in others)
+        const float vs16 = vsc[hh] * 0.0625f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        // int4: the sum adds exactly the rounded values PV receives (the empty
-        // asm keeps the compiler from fusing the product into the sum, which it
-        // would do in some instantiations and not in others)
-        if constexpr (KDT == kI4) {
-          pv[i] = p[2 * hh + (i >> 2)][i & 3] * vsc[hh];
-          asm("" : "+v"(pv[i]));
-          pvsum += pv[i];
-        } else {
-          pv[i] = p[2 * hh + (i >> 2)][i & 3] * vsc[hh];
+        for (int k = 0; k < 8; ++k) {
+          const int i = Mfma<kI4>::kVTok[k];
+          pv[k] = p[2 * hh + (i >> 2)][i & 3] * (Mfma<kI4>::kVHigh[k] ? vs16 : vsc[hh]);
+          asm("" : "+v"(pv[k]));
+          if (Mfma<kI4>::kVHigh[k]) pv_hi += pv[k];
+          else pv_lo += pv[k];
         }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pv[i] = p[2 * hh + (i >> 2)][i & 3] * vsc[hh];
       }
       M::p_operands(pv, phi[hh], plo[hh]);
     }
-    if constexpr (KDT == kI4) pv_run[cg] = fmaf(pv_run[cg], alpha, pvsum);
+    if constexpr (KDT == kI4) pv_run[cg] = fmaf(pv_run[cg], alpha, fmaf(pv_hi, 16.f, pv_lo));
   };
   // V values of token slots at or past the partition end are zeroed: their
   // weights are 0, but 0 * NaN would poison the sum.
