@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--schedule", default="auto", choices=["auto", "grid", "queue"])
-    ap.add_argument("--waves-per-item", type=int, default=0, choices=[0, 1, 2, 4])
+    ap.add_argument("--waves-per-item", type=int, default=0, choices=[0, 1, 2, 3, 4, 8])
     ap.add_argument("--replicas", type=int, default=0,
                     help="copies of the batch cycled through (0: enough for 2 GiB of cache, beating the 256 MB MALL)")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for cpu_baseline")
