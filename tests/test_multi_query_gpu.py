@@ -252,3 +252,32 @@ def test_tile_sharing_poisoned(kv):
                     k_block_scales=dev["k_block_scales"], v_block_scales=dev["v_block_scales"])
         torch.cuda.synchronize()
         check(out.float().cpu().numpy().astype(np.float64), ref, w, f"tile sharing poisoned {kv} P={ptok} waves={nw}")
+
+
+SHARE_SHAPES = [
+    # (H, Hkv, q_len, seq_lens): pair counts that are not multiples of 32, MHA, one KV head
+    (40, 8, 13, [700, 130, 13, 12]),     # G 5: 65 pairs -> 3 waves of 32, the last with 1 pair
+    (8, 8, 100, [100, 257, 64]),         # MHA, 100 pairs, windows as long as the sequences
+    (32, 1, 3, [900, 2, 0]),             # one KV head, 96 pairs; an empty sequence
+]
+
+
+@pytest.mark.parametrize("H,Hkv,ql,lens", SHARE_SHAPES, ids=[f"H{c[0]}-Hkv{c[1]}-q{c[2]}" for c in SHARE_SHAPES])
+def test_tile_sharing_shapes(H, Hkv, ql, lens):
+    w = W.random_edge_workload(80 + ql, S=len(lens), H=H, Hkv=Hkv, D=128, seq_lens=lens)
+    rng = np.random.default_rng([ql, 81])
+    q = W.to_storage(rng.standard_normal((w.num_seqs, ql, w.num_heads, w.head_dim), dtype=np.float32), "bf16")
+    ref = _multi_ref(w, q)
+    qd = _dev(q, "bf16")
+    kd, vd = _dev(w.k_cache, "bf16"), _dev(w.v_cache, "bf16")
+    td, ld = torch.from_numpy(w.block_tables).cuda(), torch.from_numpy(w.seq_lens).cuda()
+    for ptok, nw in ((0, 0), (64, 2), (128, 4), (256, 8), (128, 1)):
+        out = torch.full_like(qd, float("nan"))
+        log(f"case tile sharing shape H={H} Hkv={Hkv} q_len={ql} P={ptok} waves={nw}")
+        B.pa_decode(qd, kd, vd, td, ld, w.num_kv_heads, float(w.scale), out, partition_tokens=ptok,
+                    max_seq_len=w.max_seq_len, kernel="mfma", waves_per_item=nw)
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy().astype(np.float64)
+        check(got, ref, w, f"tile sharing H={H} Hkv={Hkv} q_len={ql} P={ptok} waves={nw}")
+        if 0 in lens:
+            assert np.all(got[lens.index(0)] == 0)
