@@ -98,26 +98,87 @@ struct AppendArgs {
   const float* v_bscale;
 };
 
-// One wavefront per (token, KV head); lane d writes rows d and d + 64.
+// Code bits of one value for a whole-row store.
+template <int KV> __device__ __forceinline__ uint32_t encode(float x, float scale);
+template <> __device__ __forceinline__ uint32_t encode<kF32>(float x, float) { return __float_as_uint(x); }
+template <> __device__ __forceinline__ uint32_t encode<kBF16>(float x, float) { return f32_to_bf16_bits(x); }
+template <> __device__ __forceinline__ uint32_t encode<kE5M2>(float x, float scale) { return f32_to_e5m2(x / scale); }
+template <> __device__ __forceinline__ uint32_t encode<kE4M3>(float x, float scale) { return f32_to_e4m3(x / scale); }
+template <> __device__ __forceinline__ uint32_t encode<kI4>(float x, float scale) {
+  return f32_to_int4_nibble(x / scale);
+}
+
+// One head_dim row of a block tile (16 tokens) from 16 encoded values, written
+// with 128-bit stores (64-bit for int4). `row` is the row's first element.
+template <int KV> __device__ __forceinline__ void store_row(void* cache, int64_t row, const uint32_t (&c)[16]) {
+  constexpr int kBits = KV == kF32 ? 32 : KV == kBF16 ? 16 : KV == kI4 ? 4 : 8;
+  uint32_t w[16 * kBits / 32];
+#pragma unroll
+  for (int k = 0; k < 16 * kBits / 32; ++k) {
+    w[k] = 0;
+#pragma unroll
+    for (int e = 0; e < 32 / kBits; ++e) w[k] |= c[k * (32 / kBits) + e] << (e * kBits);
+  }
+  char* dst = static_cast<char*>(cache) + row * kBits / 8;
+  if constexpr (kBits == 4) {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 16 * kBits / 32; k += 4)
+      *reinterpret_cast<uint4*>(dst + 4 * k) = make_uint4(w[k], w[k + 1], w[k + 2], w[k + 3]);
+  }
+}
+
+// One wavefront per (list entry, KV head). If the entry's block is written
+// whole by this call (the 16 entries from the one at the block's first
+// position are that block's positions, in order, in the same sequence: a bulk
+// append), the wavefront of that first entry writes the block, lane d rows d
+// and d + 64, 16 tokens each, with wide stores, and the other 15 return.
+// Otherwise lane d writes element (d, slot) of rows d and d + 64 (int4: one
+// nibble, by atomics on its word).
 template <int IN, int KV>
 __global__ __launch_bounds__(64) void append_kernel(const AppendArgs a) {
   const int i = blockIdx.x;
   const int g = blockIdx.y;
+  const int lane = threadIdx.x;
   const int s = a.token_seq[i];
   const int pos = a.token_pos[i];
-  if (pos < 0 || s < 0 || s >= a.num_seqs || pos >= a.max_blocks * kBlockSize) return;
+  const int max_pos = a.max_blocks * kBlockSize;
+  if (pos < 0 || s < 0 || s >= a.num_seqs || pos >= max_pos) return;
+  const int slot = pos % kBlockSize;
+  const int first = i - slot;                       // list index of the block's first position, if bulk
+  bool whole = false;
+  if (first >= 0 && first + kBlockSize <= a.num_tokens && pos - slot + kBlockSize <= max_pos) {
+    bool ok = true;
+    if (lane < kBlockSize) ok = a.token_seq[first + lane] == s && a.token_pos[first + lane] == pos - slot + lane;
+    whole = __builtin_amdgcn_ballot_w64(!ok) == 0;
+  }
+  if (whole && slot != 0) return;                   // written by the block's first entry
   int32_t id = a.tables[(int64_t)s * a.max_blocks + pos / kBlockSize];
   id = min(max(id, 0), a.num_blocks - 1);
-  const int slot = pos % kBlockSize;
-  const int64_t src = ((int64_t)i * a.num_kv_heads + g) * a.head_dim;
-  const int64_t dst = (((int64_t)id * a.num_kv_heads + g) * a.head_dim) * kBlockSize + slot;   // in elements
   // code of value / scale, the scale being k_scale times the block's own
   // (rounded to float32 first) when the cache has per-block scales
   const float ks = a.k_bscale ? a.k_scale * a.k_bscale[(int64_t)id * a.num_kv_heads + g] : a.k_scale;
   const float vs = a.v_bscale ? a.v_scale * a.v_bscale[(int64_t)id * a.num_kv_heads + g] : a.v_scale;
-  for (int d = threadIdx.x; d < a.head_dim; d += 64) {
-    store_kv<KV>(a.k_cache, dst + (int64_t)d * kBlockSize, load_in<IN>(a.k_new, src + d), ks);
-    store_kv<KV>(a.v_cache, dst + (int64_t)d * kBlockSize, load_in<IN>(a.v_new, src + d), vs);
+  const int64_t head_stride = (int64_t)a.num_kv_heads * a.head_dim;   // elements per list entry
+  const int64_t src = (int64_t)i * head_stride + (int64_t)g * a.head_dim;
+  const int64_t tile = ((int64_t)id * a.num_kv_heads + g) * a.head_dim * kBlockSize;   // in elements
+  if (whole) {
+    for (int d = lane; d < a.head_dim; d += 64) {
+      uint32_t ck[kBlockSize], cv[kBlockSize];
+#pragma unroll
+      for (int t = 0; t < kBlockSize; ++t) {
+        ck[t] = encode<KV>(load_in<IN>(a.k_new, src + t * head_stride + d), ks);
+        cv[t] = encode<KV>(load_in<IN>(a.v_new, src + t * head_stride + d), vs);
+      }
+      store_row<KV>(a.k_cache, tile + (int64_t)d * kBlockSize, ck);
+      store_row<KV>(a.v_cache, tile + (int64_t)d * kBlockSize, cv);
+    }
+    return;
+  }
+  for (int d = lane; d < a.head_dim; d += 64) {
+    store_kv<KV>(a.k_cache, tile + (int64_t)d * kBlockSize + slot, load_in<IN>(a.k_new, src + d), ks);
+    store_kv<KV>(a.v_cache, tile + (int64_t)d * kBlockSize + slot, load_in<IN>(a.v_new, src + d), vs);
   }
 }
 

@@ -258,3 +258,55 @@ def test_int4_append_then_decode():
     wk = W.workload_from_arrays("appended", w.q, k2, v2, tables, new_lens, Hkv, "bf16", "int4",
                                 k_block_scales=w.k_block_scales, v_block_scales=w.v_block_scales)
     check(got, ref, wk, "append+decode int4")
+
+
+BULK = [("bf16", "bf16", 1.0, 128), ("f32", "f32", 1.0, 64), ("bf16", "e5m2", 0.37, 128), ("f32", "e4m3", 1.0, 128),
+        ("bf16", "int4", 0.25, 128), ("f32", "bf16", 1.0, 64)]
+
+
+@pytest.mark.parametrize("in_dtype,kv_dtype,scale,D", BULK)
+def test_append_bulk_byte_exact(in_dtype, kv_dtype, scale, D):
+    """Prefill-style appends: runs of consecutive positions that fill whole
+    blocks (written as whole rows), runs that start or end inside a block,
+    one run split across list groups, padding entries and a decode-style
+    tail, all byte-exact against the oracle."""
+    rng = np.random.default_rng([12, D, len(kv_dtype)])
+    S, Hkv = 6, 2
+    lens = [0, 16, 40, 7, 64, 33]                     # tokens already in each sequence
+    new = [48, 21, 24, 9, 32, 1]                      # tokens appended now
+    nblk = [(L + m + 15) // 16 for L, m in zip(lens, new)]
+    pool = sum(nblk) + 4
+    perm = rng.permutation(pool).astype(np.int32)
+    tables = np.zeros((S, max(nblk)), np.int32)
+    off = 0
+    for s_, nb in enumerate(nblk):
+        tables[s_, :nb] = perm[off:off + nb]
+        off += nb
+    w = W.random_edge_workload(90 + D, S=S, H=2 * Hkv, Hkv=Hkv, D=D, seq_lens=lens, kv_dtype=kv_dtype,
+                               extra_pool=pool)
+    k_cache, v_cache = w.k_cache[:pool].copy(), w.v_cache[:pool].copy()
+    token_seq, token_pos = [], []
+    for s_ in range(S):
+        token_seq += [s_] * new[s_]
+        token_pos += list(range(lens[s_], lens[s_] + new[s_]))
+    token_seq += [3, 0]
+    token_pos += [-1, -7]                             # padding entries
+    token_seq, token_pos = np.array(token_seq, np.int32), np.array(token_pos, np.int32)
+    n = len(token_seq)
+    kn = _special_rows((n, Hkv, D), in_dtype, kv_dtype, rng)
+    vn = _special_rows((n, Hkv, D), in_dtype, kv_dtype, rng)
+    ks = vs = None
+    if kv_dtype == "int4":
+        ks = np.exp2(rng.uniform(-3, -1, (pool, Hkv))).astype(np.float32)
+        vs = np.exp2(rng.uniform(-3, -1, (pool, Hkv))).astype(np.float32)
+    k_ref, v_ref = O.paged_append(kn, vn, k_cache, v_cache, tables, token_seq, token_pos, in_dtype, kv_dtype,
+                                  k_scale=scale, v_scale=scale, k_block_scales=ks, v_block_scales=vs)
+    kd, vd = _to_dev(k_cache, kv_dtype), _to_dev(v_cache, kv_dtype)
+    sc = lambda x: None if x is None else torch.from_numpy(x).cuda()
+    log(f"case bulk append {in_dtype}->{kv_dtype} scale={scale} D={D} n={n}")
+    B.pa_cache_append(_to_dev(kn, in_dtype), _to_dev(vn, in_dtype), kd, vd, torch.from_numpy(tables).cuda(),
+                      torch.from_numpy(token_seq).cuda(), torch.from_numpy(token_pos).cuda(),
+                      k_scale=scale, v_scale=scale, k_block_scales=sc(ks), v_block_scales=sc(vs))
+    torch.cuda.synchronize()
+    assert _same(_from_dev(kd, kv_dtype), k_ref, kv_dtype)
+    assert _same(_from_dev(vd, kv_dtype), v_ref, kv_dtype)
