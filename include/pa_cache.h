@@ -17,12 +17,19 @@
  *   E4M3 (no infinities), where values that round beyond 448 become NaN.
  *   For an fp8 cache the division is one correctly rounded fp32 division;
  *   for other caches the scales must be 1.
+ *   INT4 cache (the inference page's exercise names INT4 KV; the format is
+ *   the one of pa_decode.h): the code is the nearest integer to
+ *   value / (k_scale * k_block_scales[b][g]) (the product rounded to fp32
+ *   first, one fp32 division), ties to even, held to -8..7, NaN -> 0, stored
+ *   as a two's-complement nibble (two tokens per byte, the even token in the
+ *   low nibble). The same per-block scales may divide an fp8 cache's values.
  *   A negative token_pos marks a padding entry that writes nothing.
  *
  * Copy on write ("Optimização da inferência" page, "PagedAttention": pages
  * of a shared prefix are stored once; a request that diverges gets its own):
  *   for every pair i, physical block dst_blocks[i] of both caches (all KV
- *   heads, all slots) becomes a copy of block src_blocks[i].
+ *   heads, all slots) becomes a copy of block src_blocks[i], and so do its
+ *   per-block scales when dims carries them.
  *
  * Layouts are those of pa_decode.h: caches [num_blocks][num_kv_heads]
  * [head_dim][block_size]; k_new / v_new [num_tokens][num_kv_heads][head_dim]
@@ -54,15 +61,21 @@ extern "C" {
 #endif
 
 /* dims: num_seqs, head_dim, num_blocks, block_size, max_blocks_per_seq,
- * kv_dtype (cache element type), k_scale, v_scale are read; the rest ignored.
- * Supported (in_dtype -> kv_dtype): F32->F32, F32->BF16, BF16->BF16,
- * F32 or BF16 -> FP8_E5M2 or FP8_E4M3; head_dim 64 or 128; block_size 16. */
+ * kv_dtype (cache element type), k_scale, v_scale, k_block_scales,
+ * v_block_scales are read; the rest ignored. Supported (in_dtype -> kv_dtype):
+ * F32->F32, F32->BF16, BF16->BF16, F32 or BF16 -> FP8_E5M2, FP8_E4M3 or INT4
+ * (INT4 requires both block-scale arrays; fp8 takes both or neither; the
+ * scales themselves are read, never written); head_dim 64 or 128; block_size
+ * 16. A run of list entries that covers a whole block in order is written
+ * row by row with wide stores; the result is the same as token by token. */
 int pa_cache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                     const int32_t* block_tables, const int32_t* token_seq,
                     const int32_t* token_pos, int32_t num_tokens, int32_t num_kv_heads,
                     int32_t in_dtype, const pa_dims_t* dims, void* stream);
 
-/* dims: head_dim, num_blocks, block_size, kv_dtype are read. num_pairs may be 0. */
+/* dims: head_dim, num_blocks, block_size, kv_dtype, k_block_scales,
+ * v_block_scales are read (the scale arrays, when given, are copied with
+ * their blocks). num_pairs may be 0. */
 int pa_cache_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_blocks,
                          const int32_t* dst_blocks, int32_t num_pairs, int32_t num_kv_heads,
                          const pa_dims_t* dims, void* stream);
