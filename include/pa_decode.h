@@ -95,7 +95,8 @@ typedef enum pa_kernel {
 /* Sizes and types of one call. Supported: block_size 16; head_dim 64 or 128;
  * group = num_heads / num_kv_heads in {1, 2, 4, 8, 16} (any group for the
  * matrix-core kernel); (q_dtype, kv_dtype) in {(F32, F32), (BF16, BF16),
- * (BF16, FP8_E5M2), (BF16, FP8_E4M3)}.
+ * (BF16, FP8_E5M2), (BF16, FP8_E4M3), (BF16, INT4)} (INT4 and per-block scales:
+ * matrix-core kernel, head_dim 128).
  * Non-finite K/V values in attended slots give non-finite outputs (the
  * matrix-core kernel may return NaN where exact arithmetic gives +-inf). */
 typedef struct pa_dims {
