@@ -332,10 +332,15 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
 
   // Q^T operands: lane (c, n) of group cg holds q[query qi][head h][32*ks + 4*i + c],
   // i = 0..7. Columns past the last virtual head read a valid row and zero it, so
-  // all loads issue back to back without a branch between them.
+  // all loads issue back to back without a branch between them. The loads and
+  // the conversion to operands are apart: the plain loop issues its first K/V
+  // tile in between, so that q's latency and the tile's overlap.
+  constexpr bool kLdsK = !kShare && (M::kBits < 16 || NCG == 2);
+  constexpr bool kPlain = !kShare && !kLdsK;
   op_t qop[NCG][kKSteps];
   int lim[NCG];                // tokens the column's query may attend: t < lim
   float qsum[NCG];             // int4: sum_d q[d] of the column
+  uint32_t qraw[NCG][kKSteps][8];
 #pragma unroll
   for (int cg = 0; cg < NCG; ++cg) {
     const int v = v0 + 16 * cg + n;
@@ -345,31 +350,37 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     lim[cg] = col_ok ? L - QL + 1 + qi : 0;
     const uint16_t* qh = static_cast<const uint16_t*>(a.q) +
                          (((int64_t)s * QL + qi) * a.num_heads + (int64_t)kvh * group + h) * kD;
-    uint32_t qb[kKSteps][8];
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) qb[ks][i] = qh[32 * ks + 4 * i + c];
+      for (int i = 0; i < 8; ++i) qraw[cg][ks][i] = qh[32 * ks + 4 * i + c];
     }
+  }
+  auto make_q = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) qb[ks][i] = col_ok ? qb[ks][i] : 0u;
-      qop[cg][ks] = M::q_operand(qb[ks]);
-    }
-    if constexpr (KDT == kI4) {
-      // sum over head_dim of the binary16 q values the MFMA uses
-      float qs = 0.f;
+    for (int cg = 0; cg < NCG; ++cg) {
+      const bool col_ok = v0 + 16 * cg + n < GV;
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) qs += static_cast<float>(qop[cg][ks][i]);
+        for (int i = 0; i < 8; ++i) qraw[cg][ks][i] = col_ok ? qraw[cg][ks][i] : 0u;
+        qop[cg][ks] = M::q_operand(qraw[cg][ks]);
       }
-      qs += shfl_xor_f32(qs, 16);
-      qs += shfl_xor_f32(qs, 32);
-      qsum[cg] = qs;
+      if constexpr (KDT == kI4) {
+        // sum over head_dim of the binary16 q values the MFMA uses
+        float qs = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < kKSteps; ++ks) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) qs += static_cast<float>(qop[cg][ks][i]);
+        }
+        qs += shfl_xor_f32(qs, 16);
+        qs += shfl_xor_f32(qs, 32);
+        qsum[cg] = qs;
+      }
     }
-  }
+  };
+  if constexpr (!kPlain) make_q();
 
   // This lane's block (0..3 within a tile) and token offset for the K loads.
   const int kblk = (n >> 3) + 2 * ((n >> 1) & 1);
@@ -395,26 +406,14 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     for (int dt = 0; dt < 8; ++dt) oacc[cg][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Physical ids this lane needs for a tile starting at logical block b0: the
-  // K-load block and the two V-load blocks. Blocks past the partition end are
-  // not looked up; the tile's first block stands in (its tokens are masked).
-  auto tile_ids = [&](int b0, int32_t& idk, int32_t& idv0, int32_t& idv1) {
-    const int bk = b0 + kblk, bv0 = b0 + (c >> 1), bv1 = b0 + (c >> 1) + 2;
-    idk = table[bk < nblk_part ? bk : b0];
-    idv0 = table[bv0 < nblk_part ? bv0 : b0];
-    idv1 = table[bv1 < nblk_part ? bv1 : b0];
-  };
-  int32_t idk = 0, idv0 = 0, idv1 = 0;
   const int first = tok0 + (kShare ? 0 : wave) * kTile;
   constexpr int kStride = (kShare ? 1 : NW) * kTile;
-  if (first < tok1) tile_ids(first / BS, idk, idv0, idv1);
 
   // K slots in LDS (one per wave) for the kernels that stage K tiles there:
   // fp8 (whole-row copies instead of 4-byte pieces) and two column groups
   // (one wave per SIMD: the next tile's K copy then overlaps this tile's
   // compute at no register cost). Four bf16 groups have no registers left
   // for the staged loop and load K directly.
-  constexpr bool kLdsK = !kShare && (M::kBits < 16 || NCG == 2);
   constexpr int kTileBlk = kD * kRowBytes;   // one block tile of one KV head
   constexpr int kSlotBlk = kTileBlk + 64;
   __shared__ __attribute__((aligned(16))) uint8_t k_lds[kLdsK ? NW : 1][kLdsK ? 4 * kSlotBlk : 16];
@@ -854,15 +853,33 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
       }
     }
   } else {
-    for (int t0 = first; t0 < tok1; t0 += kStride) {
-      Tile T;
-      load_tile(T, idk, idv0, idv1);
-      // Next tile's block ids behind this tile's loads; all 48 K/V loads of the
-      // tile are in flight before any compute is scheduled.
-      if (t0 + kStride < tok1) tile_ids((t0 + kStride) / BS, idk, idv0, idv1);
+    // Plain loop: K and V straight into registers, one tile in flight per
+    // wave. This lane's K-load block is kblk of the tile and its V-load blocks
+    // (c >> 1) and (c >> 1) + 2; the ids of the next tile are fetched (scalar)
+    // behind this tile's loads.
+    auto pick = [&](const int32_t (&ib)[4], int j) __attribute__((always_inline)) {
+      const int32_t x = (j & 1) ? ib[1] : ib[0];
+      const int32_t y = (j & 1) ? ib[3] : ib[2];
+      return (j & 2) ? y : x;
+    };
+    int32_t ib[4] = {0, 0, 0, 0};
+    Tile T;
+    auto issue = [&](int t) __attribute__((always_inline)) {
+      load_tile(T, pick(ib, kblk), pick(ib, c >> 1), pick(ib, (c >> 1) + 2));
+      if (t + kStride < tok1) ids_at(t + kStride, ib);
+    };
+    if (first < tok1) {   // a wave without tiles needs no q operands
+      ids_at(first, ib);
+      issue(first);
+      make_q();
       __builtin_amdgcn_sched_barrier(0);
-      constexpr float kOnes[2] = {1.f, 1.f};
-      tile_step(T, t0, []() __attribute__((always_inline)) {}, kOnes, kOnes);
+      for (int t0 = first; t0 < tok1; t0 += kStride) {
+        constexpr float kOnes[2] = {1.f, 1.f};
+        tile_step(T, t0, []() __attribute__((always_inline)) {}, kOnes, kOnes);
+        __builtin_amdgcn_sched_barrier(0);
+        if (t0 + kStride < tok1) issue(t0 + kStride);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 
