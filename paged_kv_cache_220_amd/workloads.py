@@ -250,6 +250,29 @@ def _seq_lens_for(name: str, rng, num_seqs: Optional[int], seq_len: Optional[int
     raise ValueError(name)
 
 
+def batch_heads(name: str, kv_dtype: Optional[str] = None):
+    """(num_heads, num_kv_heads, head_dim, q dtype, KV dtype) of batch `name`."""
+    if name == "c1":
+        H, Hkv, D, qd, kvd = 4, 4, 64, F32, F32
+    elif name == "c5":
+        H, Hkv, D, qd, kvd = 64, 8, 128, BF16, E5M2
+    else:
+        H, Hkv, D, qd, kvd = 64, 8, 128, BF16, BF16
+    if kv_dtype:
+        if qd != BF16 or kv_dtype not in (BF16, E5M2, E4M3, INT4):
+            raise ValueError(f"{name} cannot take a {kv_dtype} cache")
+        kvd = kv_dtype
+    return H, Hkv, D, qd, kvd
+
+
+def batch_seq_lens(name: str) -> np.ndarray:
+    """The sequence lengths of full-size batch `name`, without drawing its tensors."""
+    if name not in CONFIG_NAMES:
+        raise ValueError(f"unknown workload {name}")
+    rng = np.random.default_rng([220, CONFIG_NAMES.index(name) + 1])
+    return _seq_lens_for(name, rng, None, None)
+
+
 def make_workload(name: str, *, num_seqs: Optional[int] = None, seq_len: Optional[int] = None,
                   poison: bool = False, seed_extra: int = 0, kv_dtype: Optional[str] = None) -> Workload:
     """Build decode batch `name` (c1..c5).
@@ -268,16 +291,7 @@ def make_workload(name: str, *, num_seqs: Optional[int] = None, seq_len: Optiona
     seed_root = (220, idx) if seed_extra == 0 else (220, idx, 1000 + seed_extra)
     rng = np.random.default_rng(list(seed_root))
     bs = BLOCK_SIZE_DEFAULT
-    if name == "c1":
-        H, Hkv, D, qd, kvd = 4, 4, 64, F32, F32
-    elif name == "c5":
-        H, Hkv, D, qd, kvd = 64, 8, 128, BF16, E5M2
-    else:
-        H, Hkv, D, qd, kvd = 64, 8, 128, BF16, BF16
-    if kv_dtype is not None:
-        if qd != BF16 or kv_dtype not in (BF16, E5M2, E4M3, INT4):
-            raise ValueError(f"{name} cannot take a {kv_dtype} cache")
-        kvd = kv_dtype
+    H, Hkv, D, qd, kvd = batch_heads(name, kv_dtype)
 
     seq_lens = _seq_lens_for(name, rng, num_seqs, seq_len)
     S = len(seq_lens)
