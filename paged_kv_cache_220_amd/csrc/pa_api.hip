@@ -133,7 +133,12 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
   if (p->max_parts < 1) p->max_parts = 1;
   if (p->max_parts > kMaxParts) return PA_ERR_UNSUPPORTED;
   p->grid = (long long)p->max_parts * hkv * p->q_blocks * d->num_seqs;
-  p->reduce_grid = p->max_parts > 1 ? (long long)d->num_heads * p->q_len * d->num_seqs : 0;
+  // merge: one workgroup per (sequence, KV head, 8 virtual heads) up to 8
+  // partitions, else one per (sequence, virtual head)
+  const long long gv_all = (long long)p->group * p->q_len;
+  p->reduce_grid = p->max_parts <= 1 ? 0
+                   : p->max_parts <= pa::kMergeHeadsMaxParts ? (long long)hkv * ((gv_all + 7) / 8) * d->num_seqs
+                                                             : (long long)d->num_heads * p->q_len * d->num_seqs;
   // List schedule: for the matrix-core kernel when asked, or when the dense
   // grid is far larger than the resident workgroups (a skewed or sparse
   // length mix leaves most of it empty and its long partitions in the tail).

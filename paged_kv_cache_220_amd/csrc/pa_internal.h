@@ -68,6 +68,7 @@ int mfma_share_default_waves(int group, int q_len);
 
 constexpr int kBlockSize = 16;     // tokens per physical block handled by the kernels
 constexpr int kTileTokens = 64;    // partition lengths are multiples of this
+constexpr int kMergeHeadsMaxParts = 8;  // merge by KV head (all its query heads per workgroup) up to this many partitions
 constexpr int kMaxColumnGroups = 4; // matrix-core kernel: up to 64 (query position, head) pairs per work item
 #ifndef PA_SHARE_GROUPS
 #define PA_SHARE_GROUPS 2

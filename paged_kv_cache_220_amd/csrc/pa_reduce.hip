@@ -13,12 +13,23 @@
 // merged alike; a query whose window holds no token in any partition gets a
 // zero row.
 //
-// One workgroup of 256 threads per (sequence, query head): 8 partition
-// groups x 32 column groups of 4 output elements. Each thread walks every
-// 8th partition with 128-bit loads of o_p (a wave reads 512 contiguous bytes
-// per partition), folding them into a running (m, l, o) by the same rule, so
-// all loads go out in one round trip; the 8 group states then meet in LDS in
-// a fixed order, so the result does not depend on timing.
+// Up to 8 partitions per sequence (the usual case: partitions are made as
+// long as the grid allows): one workgroup of 256 threads per (sequence, KV
+// head, 8 of its query heads), 8 heads x 32 column groups of 4 output
+// elements. Each thread issues the 128-bit loads of o_p for all partitions
+// at once (a wave reads 512 contiguous bytes per partition and head) and
+// combines them in partition order. One workgroup per KV head instead of one
+// per query head means 8x fewer workgroups at G = 8, most of them empty when
+// most sequences fit one partition.
+//
+// More partitions: one workgroup per (sequence, query head), 8 partition
+// groups x 32 column groups. Each thread walks every 8th partition, folding
+// them into a running (m, l, o) by the same rule, so all loads go out in one
+// round trip; the 8 group states then meet in LDS in a fixed order.
+//
+// Both orders give the same result for up to 8 partitions (a group that
+// holds one partition keeps its state unchanged), and neither depends on
+// timing.
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -106,10 +117,80 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(const Args a, int head
   }
 }
 
+// Up to kGroups partitions: partition p's state is loaded for every p <
+// kGroups (index clamped to the last partition, so every load is in bounds
+// and issues without a branch) and the states past nparts are given weight 0.
+template <int QDT>
+__global__ __launch_bounds__(kThreads) void reduce_heads_kernel(const Args a, int head_dim, int group) {
+  const int GV = group * a.q_len;                     // virtual heads (query position, head) per KV head
+  const int chunks = (GV + kGroups - 1) / kGroups;
+  const int kvh = blockIdx.x / chunks;
+  const int g = (blockIdx.x - kvh * chunks) * kGroups + threadIdx.x / kCols;
+  const int s = blockIdx.y;
+  const int L = clamp_len(a, s);
+  const int P = a.partition_tokens;
+  const int nparts = (L + P - 1) / P;
+  if (nparts <= 1) return;
+  const int col = (threadIdx.x % kCols) * 4;
+  if (g >= GV || col >= head_dim) return;
+  const int qi = g / group;
+  const int h = kvh * group + (g - qi * group);
+  const int64_t item0 = ((int64_t)s * a.num_kv_heads + kvh) * a.max_parts;
+  const int64_t orow = (((int64_t)s * a.q_len + qi) * a.num_heads + h) * head_dim;
+
+  float mp[kGroups], lp[kGroups];
+  float4 op[kGroups];
+#pragma unroll
+  for (int p = 0; p < kGroups; ++p) {
+    const int64_t it = (item0 + min(p, nparts - 1)) * GV + g;
+    mp[p] = a.part_m[it];
+    lp[p] = a.part_l[it];
+    op[p] = *reinterpret_cast<const float4*>(a.part_o + it * head_dim + col);
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int p = 0; p < kGroups; ++p)
+    if (p < nparts) M = fmaxf(M, mp[p]);
+  if (M == -INFINITY) {
+    // no partition saw a token this query may attend (query window longer than the sequence)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) store_out<QDT>(a.out, orow + col + j, 0.f);
+    return;
+  }
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float den = 0.f;
+#pragma unroll
+  for (int p = 0; p < kGroups; ++p) {
+    const float w = p < nparts ? exp2f(mp[p] - M) : 0.f;
+    acc.x += op[p].x * w;
+    acc.y += op[p].y * w;
+    acc.z += op[p].z * w;
+    acc.w += op[p].w * w;
+    den += lp[p] * w;
+  }
+  store_out<QDT>(a.out, orow + col + 0, acc.x / den);
+  store_out<QDT>(a.out, orow + col + 1, acc.y / den);
+  store_out<QDT>(a.out, orow + col + 2, acc.z / den);
+  store_out<QDT>(a.out, orow + col + 3, acc.w / den);
+}
+
 }  // namespace
 
 hipError_t launch_reduce(const Args& a, int q_dtype, int head_dim, int group, hipStream_t stream) {
   if (head_dim > kCols * 4 || head_dim % 4 != 0) return hipErrorInvalidValue;
+  static_assert(kMergeHeadsMaxParts == kGroups, "the head-wise merge loads one state per partition group");
+  if (a.max_parts <= kMergeHeadsMaxParts) {
+    const int gv = group * a.q_len;
+    const dim3 grid(a.num_kv_heads * ((gv + kGroups - 1) / kGroups), a.num_seqs);
+    if (q_dtype == kF32) {
+      reduce_heads_kernel<kF32><<<grid, kThreads, 0, stream>>>(a, head_dim, group);
+    } else if (q_dtype == kBF16) {
+      reduce_heads_kernel<kBF16><<<grid, kThreads, 0, stream>>>(a, head_dim, group);
+    } else {
+      return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   const dim3 grid(a.num_heads * a.q_len, a.num_seqs);
   if (q_dtype == kF32) {
     reduce_kernel<kF32><<<grid, kThreads, 0, stream>>>(a, head_dim, group);

@@ -128,7 +128,7 @@ def test_plan_long_context():
     # 1024 items of one 32 KiB tile in flight each, the 32 MiB the planner wants
     p = B.plan(dims(), 8)
     assert p["partition_tokens"] == 4096 and p["max_partitions"] == 8
-    assert p["grid_workgroups"] == 8 * 8 * 16 and p["reduce_workgroups"] == 64 * 16
+    assert p["grid_workgroups"] == 8 * 8 * 16 and p["reduce_workgroups"] == 8 * 16   # one merge workgroup per (sequence, KV head)
     items = 16 * 8 * 8 * 8
     assert p["workspace_bytes"] >= items * (128 + 2) * 4
     assert p["waves_per_item"] == 2                                      # 1024 items x 2 = 2048 waves
