@@ -33,6 +33,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 EVENT_EVERY = 4                # partition-kernel timing events on every 4th timed step
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # MI355X dense matrix / fp32 vector
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+READ_PROBE_BYTES = 4 << 30   # streaming-read probe buffer: 16x the 256 MiB Infinity Cache
 
 
 def parse():
@@ -55,6 +56,8 @@ def parse():
                     help="copies of the batch cycled through (0: enough for 2 GiB of cache, beating the 256 MB MALL)")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-read-probe", action="store_true",
+                    help="skip the streaming-read probe that measures the chip's practical read ceiling")
     ap.add_argument("--sweep", default="", help="comma list of partition_tokens to time (printed to stderr)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="dispatch a device copy of this many MiB first (calibrates HBM byte counters)")
@@ -353,9 +356,39 @@ def main():
         "rest_of_step_us": round((ms_step - part_avg) * 1e3, 2),
         "roofline": roofline,
     }
+    if not args.no_read_probe:
+        result["read_ceiling"] = read_ceiling(stream, dev, achieved if roofline["unit"] == "GB/s" else None)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, args.q_len)
     print(json.dumps(result), flush=True)
+
+
+def read_ceiling(stream, dev, kernel_gbs, nbytes=READ_PROBE_BYTES, reps=10):
+    """Rate of the library's streaming-read probe (every byte read once, nothing else) on this GPU.
+
+    The buffer is 16x the 256 MiB Infinity Cache, so repeats stream from HBM.
+    """
+    import torch
+    from paged_kv_cache_220_amd import binding as B
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(B.PROBE_SINK_WORDS, dtype=torch.int32, device=dev)
+    sid = stream.cuda_stream
+    for _ in range(3):
+        B.pa_read_probe(buf, sink, stream=sid)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        B.pa_read_probe(buf, sink, stream=sid)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    gbs = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf
+    out = {"kernel": "pa_read_probe", "value": round(gbs, 2), "unit": "GB/s", "bytes": nbytes,
+           "launches": reps, "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    if kernel_gbs is not None:
+        out["partition_kernel_frac"] = round(kernel_gbs / gbs, 4)
+    return out
 
 
 def _timed(fn, steps, warmup, stream):

@@ -26,7 +26,7 @@ SCHEDULE_NAMES = {v: k for k, v in SCHEDULES.items()}
 
 # Symbols declared in include/pa_decode.h and include/pa_cache.h.
 EXPORTED = ("pa_decode", "pa_decode_ws", "pa_decode_ws_timed", "pa_decode_workspace_bytes",
-            "pa_decode_plan", "pa_status_str", "pa_version", "pa_cache_append", "pa_cache_copy_blocks")
+            "pa_decode_plan", "pa_status_str", "pa_version", "pa_cache_append", "pa_cache_copy_blocks", "pa_read_probe")
 
 
 class PaDims(ctypes.Structure):
@@ -88,6 +88,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.pa_cache_append.restype = ctypes.c_int
     lib.pa_cache_copy_blocks.argtypes = [vp, vp, vp, vp, i32, i32, dims_p, vp]
     lib.pa_cache_copy_blocks.restype = ctypes.c_int
+    lib.pa_read_probe.argtypes = [vp, sz, vp, vp]
+    lib.pa_read_probe.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -337,3 +339,29 @@ def pa_cache_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, src_block
         ctypes.c_void_p(src_blocks.data_ptr()), ctypes.c_void_p(dst_blocks.data_ptr()), src_blocks.numel(),
         k_cache.shape[1], ctypes.byref(dims), stream)
     _check(rc)
+
+
+PROBE_SINK_WORDS = 4096      # PA_PROBE_SINK_WORDS
+PROBE_CHUNK_BYTES = 32768    # PA_PROBE_CHUNK_BYTES
+
+
+def pa_read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> int:
+    """Stream every byte of `buf` once (128-bit non-temporal loads), nothing else.
+
+    Measurement only: its rate is the read ceiling the decode kernels are compared with.
+    `buf` is any contiguous device tensor whose byte size is a multiple of 16; `sink` a
+    device tensor of PROBE_SINK_WORDS 32-bit words. Workgroup w stores the XOR of the words it
+    read in sink[w]; returns the number of workgroups n, so the XOR of sink[:n] is the XOR of
+    all of buf's 32-bit words.
+    """
+    if not buf.is_contiguous() or not sink.is_contiguous() or sink.numel() < PROBE_SINK_WORDS \
+            or sink.element_size() != 4:
+        raise ValueError(f"pa_read_probe: contiguous buf and a {PROBE_SINK_WORDS}-word 32-bit sink expected")
+    if buf.device != sink.device:
+        raise ValueError("pa_read_probe: buf and sink must be on the same device")
+    if stream is None:
+        stream = torch.cuda.current_stream(buf.device).cuda_stream
+    nbytes = buf.numel() * buf.element_size()
+    _check(load_library().pa_read_probe(ctypes.c_void_p(buf.data_ptr()), nbytes,
+                                        ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream)))
+    return min(-(-nbytes // PROBE_CHUNK_BYTES), PROBE_SINK_WORDS)

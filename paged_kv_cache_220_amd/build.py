@@ -17,7 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libpadecode.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["pa_api.hip", "pa_valu.hip", "pa_mfma.hip", "pa_reduce.hip", "pa_cache.hip", "pa_schedule.hip"]
+SOURCES = ["pa_api.hip", "pa_valu.hip", "pa_mfma.hip", "pa_reduce.hip", "pa_cache.hip", "pa_schedule.hip",
+           "pa_probe.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are kept out of the generated code on purpose.

@@ -70,11 +70,10 @@ constexpr int kBlockSize = 16;     // tokens per physical block handled by the k
 constexpr int kTileTokens = 64;    // partition lengths are multiples of this
 constexpr int kMergeHeadsMaxParts = 8;  // merge by KV head (all its query heads per workgroup) up to this many partitions
 constexpr int kMaxColumnGroups = 4; // matrix-core kernel: up to 64 (query position, head) pairs per work item
-#ifndef PA_SHARE_GROUPS
-#define PA_SHARE_GROUPS 2
-#endif
-// Tile sharing: column groups (16 pairs each) per wave, and the most waves per item.
-constexpr int kShareGroups = PA_SHARE_GROUPS;
+// Tile sharing: column groups (16 pairs each) per wave, and the most waves per
+// item. Two groups per wave run two waves per SIMD; four groups per wave (one
+// wave per SIMD, up to 4 waves per item) measured 4-8 % slower.
+constexpr int kShareGroups = 2;
 constexpr int kShareMaxWaves = kShareGroups == 2 ? 8 : 4;
 constexpr int kMaxQueryLen = 4096;  // query positions per sequence
 constexpr int kMaxQueueBuckets = 129;  // queue schedule: partitions of at most 128 tiles
