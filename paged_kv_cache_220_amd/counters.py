@@ -34,7 +34,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["pa_internal.h", "pa_device.h", "pa_api.hip", "pa_mfma.hip"]
 COPY_KERNEL = "copyBuffer"
 PARTITION_KERNEL = "mfma_partition_kernel"
-REDUCE_KERNEL = "reduce_kernel"
+REDUCE_KERNEL = "reduce_"   # the merge kernel in either form
 
 
 def source_digest(files):
