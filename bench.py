@@ -352,6 +352,7 @@ def main():
         "seq_head_per_s": round(seq_heads / (ms_step * 1e-3), 1),
         "wall_ms_per_step": round(wall * 1e3 / K, 5),
         "partition_kernel_us": round(part_avg * 1e3, 2),
+        "partition_kernel_us_p10_p50_p90": [round(float(x) * 1e3, 2) for x in np.percentile(part_ms, [10, 50, 90])],
         "partition_kernel_timed_launches": len(part_ms),
         "rest_of_step_us": round((ms_step - part_avg) * 1e3, 2),
         "roofline": roofline,
