@@ -33,7 +33,7 @@ ROOT = os.path.dirname(PKG)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["pa_internal.h", "pa_device.h", "pa_api.hip", "pa_mfma.hip"]
 COPY_KERNEL = "copyBuffer"
-PARTITION_KERNEL = "mfma_partition_kernel"
+PARTITION_KERNEL = "mfma_partition"   # the grid or the work-list form
 REDUCE_KERNEL = "reduce_"   # the merge kernel in either form
 
 
