@@ -136,21 +136,31 @@ template <int KV> __device__ __forceinline__ void store_row(void* cache, int64_t
 // and d + 64, 16 tokens each, with wide stores, and the other 15 return.
 // Otherwise lane d writes element (d, slot) of rows d and d + 64 (int4: one
 // nibble, by atomics on its word).
+//
+// The (sequence, position) pairs of the entry and of the 15 on either side,
+// which the check needs, arrive in one round of loads, one entry per lane:
+// most wavefronts of a bulk append only find that another writes their
+// block, and their time is that round.
 template <int IN, int KV>
 __global__ __launch_bounds__(64) void append_kernel(const AppendArgs a) {
+  constexpr int kHalo = kBlockSize - 1;
   const int i = blockIdx.x;
   const int g = blockIdx.y;
   const int lane = threadIdx.x;
-  const int s = a.token_seq[i];
-  const int pos = a.token_pos[i];
+  const int we = i - kHalo + lane;                  // entry of this lane's window slot
+  const bool in_win = lane < 2 * kHalo + 1 && we >= 0 && we < a.num_tokens;
+  const int wseq = in_win ? a.token_seq[we] : -1;
+  const int wpos = in_win ? a.token_pos[we] : -1;
+  const int s = __builtin_amdgcn_readlane(wseq, kHalo);
+  const int pos = __builtin_amdgcn_readlane(wpos, kHalo);
   const int max_pos = a.max_blocks * kBlockSize;
   if (pos < 0 || s < 0 || s >= a.num_seqs || pos >= max_pos) return;
   const int slot = pos % kBlockSize;
   const int first = i - slot;                       // list index of the block's first position, if bulk
   bool whole = false;
   if (first >= 0 && first + kBlockSize <= a.num_tokens && pos - slot + kBlockSize <= max_pos) {
-    bool ok = true;
-    if (lane < kBlockSize) ok = a.token_seq[first + lane] == s && a.token_pos[first + lane] == pos - slot + lane;
+    const int k = lane - (kHalo - slot);            // this lane's entry is first + k
+    const bool ok = k < 0 || k >= kBlockSize || (wseq == s && wpos == pos - slot + k);
     whole = __builtin_amdgcn_ballot_w64(!ok) == 0;
   }
   if (whole && slot != 0) return;                   // written by the block's first entry
