@@ -169,6 +169,26 @@ def test_full_size_sampled(name, sample):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("kv_dtype", ["bf16", "e5m2"])
+def test_one_sequence_of_128k_tokens(kv_dtype):
+    """A context longer than the batches: one sequence of 131,072 tokens (the
+    page's 128K-context example). The default plan shortens partitions to put
+    enough waves on the chip (hundreds of partitions, so the merge takes its
+    many-partition form); every head is checked against the oracle."""
+    w = W.make_workload("c3", num_seqs=1, seq_len=131072, kv_dtype=None if kv_dtype == "bf16" else kv_dtype)
+    dev = upload(w)
+    d = B.make_dims(dev["q"], dev["k"], dev["tables"], max_seq_len=w.max_seq_len)
+    plan = B.plan(d, w.num_kv_heads)
+    log(f"case 128k {kv_dtype}: plan {plan}")
+    assert plan["max_partitions"] > 8
+    ref = oracle_full(w)
+    for kern in kernels_for(w):
+        got = run_gpu(w, dev, kernel=kern)
+        check(got, ref, w, f"128k {kv_dtype} {kern}")
+    del dev
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------ queue schedule --
 
 QUEUE = [("c4", dict(num_seqs=40, seq_len=6000), 0), ("c4", dict(num_seqs=40, seq_len=6000), 512),
