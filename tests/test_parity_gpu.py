@@ -141,6 +141,22 @@ def test_special_values_single_token_and_zero_query():
         check(run_gpu(w2, kernel=kern), ref, w2, f"q=0 {kern}")
 
 
+@pytest.mark.parametrize("kv_dtype", ["bf16", "e5m2", "int4"])
+@pytest.mark.parametrize("boost", [32.0, 1024.0])
+def test_peaked_softmax(kv_dtype, boost):
+    """Large scores: the scale times 32 (scores of tens) or 1024 (scores of
+    thousands, where every weight but the largest underflows to 0 and the
+    output is one token's V row). The running max keeps every exponent <= 0."""
+    w = W.make_workload("c2", num_seqs=6, kv_dtype=None if kv_dtype == "bf16" else kv_dtype)
+    w.scale = np.float32(w.scale * np.float32(boost))      # a power of two: exact
+    ref = oracle_full(w)
+    dev = upload(w)
+    for kern in kernels_for(w):
+        for ptok in (0, 64):
+            got = run_gpu(w, dev, kernel=kern, partition_tokens=ptok)
+            check(got, ref, w, f"peaked x{boost:g} {kv_dtype} {kern} P={ptok}")
+
+
 # ---------------------------------------------------------------- full size --
 
 FULL = [("c2", None), ("c3", [0, 7, 15]), ("c4", "longest"), ("c5", [0, 63, 127])]
