@@ -401,3 +401,64 @@ def test_multi_query_rows_are_prefix_decodes():
     short = O.paged_attention_multi(q, w.k_cache, w.v_cache, w.block_tables, np.array([2, 300], np.int32), 8,
                                     w.scale, "bf16", "e5m2")
     assert np.all(short[0, :2] == 0) and np.any(short[0, 2:] != 0)
+
+
+# ------------------------------- planted mistakes: query window, block scales --
+
+def _pinned_multi_query_holds(attend_fn):
+    """The masked dense form of the inference page against `attend_fn` (the oracle or a mutant)."""
+    w = W.make_workload("c2", num_seqs=2)
+    rng = np.random.default_rng(31)
+    ql = 3
+    q = W.to_storage(rng.standard_normal((2, ql, 64, 128), dtype=np.float32), "bf16")
+    got = attend_fn(q, w)
+    for s in range(2):
+        L = int(w.seq_lens[s])
+        for g in (0, 5):
+            K = O.logical_kv(w.k_cache, w.block_tables, s, L, g, "bf16")
+            V = O.logical_kv(w.v_cache, w.block_tables, s, L, g, "bf16")
+            for h in (g * 8, g * 8 + 7):
+                ref = _masked_sdpa_pages_form(O.decode_bits(q[s, :, h], "bf16"), K, V, float(np.float32(w.scale)))
+                if not np.allclose(got[s, :, h], ref, rtol=1e-12, atol=1e-13):
+                    return False
+    return True
+
+
+def test_multi_query_pin_catches_window_mistakes():
+    multi = lambda q, w, lens=None: O.paged_attention_multi(
+        q, w.k_cache, w.v_cache, w.block_tables, w.seq_lens if lens is None else lens, 8, w.scale, "bf16", "bf16")
+    assert _pinned_multi_query_holds(multi)
+    # window one token short (query i attends t < L - q_len + i)
+    assert not _pinned_multi_query_holds(lambda q, w: multi(q, w, (w.seq_lens - 1).astype(np.int32)))
+    # queries taken in reverse order (the last query position gets the first window)
+    assert not _pinned_multi_query_holds(lambda q, w: multi(np.ascontiguousarray(q[:, ::-1]), w)[:, ::-1])
+
+
+def test_block_scale_pin_catches_swapped_or_shifted_scales():
+    """The explicit dense reassembly with per-block scales must reject an oracle that applies V's
+    scales to K, or takes each block's scale from its neighbour in the pool."""
+    w = W.random_edge_workload(6, S=2, H=16, Hkv=2, D=128, seq_lens=[70, 33], kv_dtype="int4")
+    sc = float(np.float32(w.scale))
+
+    def dense(ks, vs, s, h):
+        L, g = int(w.seq_lens[s]), h // 8
+        blk = [int(w.block_tables[s, t // 16]) for t in range(L)]
+        K = np.array([[O.int4_unpack(w.k_cache[blk[t], g, d])[t % 16] * float(ks[blk[t], g]) for d in range(128)]
+                      for t in range(L)])
+        V = np.array([[O.int4_unpack(w.v_cache[blk[t], g, d])[t % 16] * float(vs[blk[t], g]) for d in range(128)]
+                      for t in range(L)])
+        z = sc * (K @ O.decode_bits(w.q[s, h], "bf16"))
+        p = np.exp(z - z.max())
+        return (p @ V) / p.sum()
+
+    ref = [dense(w.k_block_scales, w.v_block_scales, s, h) for s in range(2) for h in (0, 9)]
+
+    def matches(ks, vs):
+        out = O.paged_decode(w.q, w.k_cache, w.v_cache, w.block_tables, w.seq_lens, 2, w.scale, "bf16", "int4",
+                             k_block_scales=ks, v_block_scales=vs)
+        got = [out[s, h] for s in range(2) for h in (0, 9)]
+        return all(np.allclose(a, b, rtol=1e-12, atol=1e-13) for a, b in zip(got, ref))
+
+    assert matches(w.k_block_scales, w.v_block_scales)
+    assert not matches(w.v_block_scales, w.k_block_scales)
+    assert not matches(np.roll(w.k_block_scales, 1, axis=0), np.roll(w.v_block_scales, 1, axis=0))
