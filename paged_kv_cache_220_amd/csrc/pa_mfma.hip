@@ -321,6 +321,11 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   if (part >= nparts) return;
   const int tok0 = part * P;
   const int tok1 = min(L, tok0 + P);
+  // Tokens below this bound are inside the partition and inside every query's
+  // causal window (query 0 of the last QL positions attends t < L - QL + 1);
+  // columns past the last (position, head) pair carry zero queries and are
+  // never written, so they need no selection either.
+  const int full_lim = min(tok1, L - QL + 1);
 
   // NW waves share the item: without tile sharing wave w takes tiles w, w + NW, ...
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -495,15 +500,26 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int tt = 16 * ((c >> 1) + 2 * (r >> 1)) + 8 * (c & 1) + 4 * (r & 1);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float sv;
-        if constexpr (KDT == kI4) sv = fmaf(sg[j][r], ka[r >> 1] * (1.f / Mfma<kI4>::kKScale[j]), kb[r >> 1]);
-        else sv = sg[j][r] * ka[r >> 1];
-        sc[r][j] = (tt + j < nval) ? sv : -INFINITY;
-        tmax = fmaxf(tmax, sc[r][j]);
+        if constexpr (KDT == kI4) sc[r][j] = fmaf(sg[j][r], ka[r >> 1] * (1.f / Mfma<kI4>::kKScale[j]), kb[r >> 1]);
+        else sc[r][j] = sg[j][r] * ka[r >> 1];
       }
+    }
+    // Only a tile that reaches past the partition end or a query's window
+    // has tokens to select out; the test is the same for the whole wave.
+    if (t0 + kTile > full_lim) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tt = 16 * ((c >> 1) + 2 * (r >> 1)) + 8 * (c & 1) + 4 * (r & 1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sc[r][j] = (tt + j < nval) ? sc[r][j] : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) tmax = fmaxf(tmax, sc[r][j]);
     }
     tmax = fmaxf(tmax, shfl_xor_f32(tmax, 16));
     tmax = fmaxf(tmax, shfl_xor_f32(tmax, 32));
