@@ -274,6 +274,22 @@ def test_queue_schedule_edge_lengths():
 
 
 
+def test_queue_schedule_many_sequences():
+    """More sequences than the plan kernel has threads, several times over
+    (5,000: each thread counts and places 4 or 5 of them), lengths 0 to 300
+    with many zeros; the work list must still cover every item exactly once."""
+    rng = np.random.default_rng(5000)
+    lens = rng.integers(0, 301, 5000)
+    lens[rng.random(5000) < 0.1] = 0
+    w = W.random_edge_workload(32, S=5000, H=8, Hkv=1, D=128, seq_lens=lens.tolist())
+    ref = oracle_full(w)
+    dev = upload(w)
+    for ptok in (64, 128):
+        got = run_gpu(w, dev, kernel="mfma", partition_tokens=ptok, schedule="queue")
+        check(got, ref, w, f"queue 5000 seqs P={ptok}")
+        assert np.all(got[lens == 0] == 0)
+
+
 @pytest.mark.parametrize("kv_dtype", ["e5m2", "e4m3"])
 def test_every_fp8_code_decodes_exactly(kv_dtype):
     """One-token sequences return their V row; two sequences cover all 256 codes.
