@@ -40,6 +40,15 @@
  * enqueued on `stream` (hipStream_t as void*) without synchronising, host-side
  * validation before any HIP call, a pa_status_t result.
  *
+ * Caller's obligations on the buffers (sizes only cross this interface): the
+ * caches hold num_blocks * num_kv_heads * head_dim * block_size elements of
+ * kv_dtype (int4: two tokens per byte); k_new and v_new hold num_tokens rows of
+ * [num_kv_heads][head_dim] with the caches' num_kv_heads and head_dim;
+ * token_seq and token_pos hold num_tokens entries; block_tables num_seqs rows
+ * of max_blocks_per_seq; src_blocks and dst_blocks num_pairs entries each. The
+ * Python binding checks these against the tensors' shapes and raises
+ * PA_ERR_SHAPE before calling the library.
+ *
  * Device-side preconditions (not checked; violations are clamped or skipped
  * so every access stays in bounds, and the result is then unspecified):
  *   append: 0 <= token_seq[i] < num_seqs; token_pos[i] < max_blocks_per_seq *

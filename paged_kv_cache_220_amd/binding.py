@@ -123,7 +123,15 @@ def _kv_dtype_code(t: torch.Tensor, kv_dtype: Optional[str]) -> int:
     raise TypeError(f"unsupported KV cache dtype {t.dtype}; pass kv_dtype for raw byte views")
 
 
+_KV_ELEM_BYTES = {PA_DTYPE_F32: 4, PA_DTYPE_BF16: 2, PA_DTYPE_FP8_E5M2: 1, PA_DTYPE_FP8_E4M3: 1, PA_DTYPE_INT4: 1}
+
+
 def _tokens_per_row(k_cache: torch.Tensor, kv_code: int) -> int:
+    """Tokens per block from the cache's last axis; the tensor's element size
+    must be that of the cache type (one byte holds two int4 tokens), so the
+    library's byte arithmetic matches the tensor's extent."""
+    if k_cache.element_size() != _KV_ELEM_BYTES[kv_code]:
+        _shape_error(f"a {k_cache.element_size()}-byte cache element does not hold the KV dtype {kv_code}")
     return k_cache.shape[3] * (2 if kv_code == PA_DTYPE_INT4 else 1)
 
 
@@ -179,8 +187,36 @@ def workspace_bytes(dims: PaDims, num_kv_heads: int) -> int:
     return int(n)
 
 
-def _validate_tensors(q, k_cache, v_cache, block_tables, seq_lens, out):
+def _shape_error(msg: str):
+    """PA_ERR_SHAPE raised by the binding: the C ABI sees sizes, not tensors, so
+    the agreement between the tensors and the sizes passed on is checked here."""
+    raise PagedAttentionError(PA_ERR_SHAPE, f"PA_ERR_SHAPE: {msg}")
+
+
+def _check_decode_shapes(q, k_cache, block_tables, seq_lens, num_kv_heads):
+    """The tensor shapes pa_decode relies on (they size every device access):
+    k_cache [num_blocks, num_kv_heads, head_dim, block_size (int4: block_size / 2 bytes)],
+    q [S, H, head_dim] or [S, q_len, H, head_dim], block_tables [S, max_blocks], seq_lens [S]."""
+    if q.dim() not in (3, 4) or k_cache.dim() != 4 or block_tables.dim() != 2:
+        _shape_error("q [S,H,D] or [S,q_len,H,D], k_cache [NB,Hkv,D,bs], block_tables [S,max_blocks] expected")
+    S, D = q.shape[0], q.shape[-1]
+    if int(num_kv_heads) != k_cache.shape[1]:
+        _shape_error(f"num_kv_heads {num_kv_heads} differs from the cache's KV-head axis {k_cache.shape[1]}")
+    if k_cache.shape[2] != D:
+        _shape_error(f"the cache's head_dim {k_cache.shape[2]} differs from q's {D}")
+    if block_tables.shape[0] != S:
+        _shape_error(f"block_tables has {block_tables.shape[0]} rows for {S} sequences")
+    if seq_lens.dim() != 1 or seq_lens.numel() != S:
+        _shape_error(f"seq_lens has shape {tuple(seq_lens.shape)} for {S} sequences")
+
+
+def _validate_tensors(q, k_cache, v_cache, block_tables, seq_lens, out, num_kv_heads):
     dev = q.device
+    _check_decode_shapes(q, k_cache, block_tables, seq_lens, num_kv_heads)
+    if out.shape != q.shape:
+        _shape_error(f"out has shape {tuple(out.shape)}, q {tuple(q.shape)}")
+    if v_cache.shape != k_cache.shape:
+        _shape_error(f"v_cache has shape {tuple(v_cache.shape)}, k_cache {tuple(k_cache.shape)}")
     if dev.type != "cuda":
         raise ValueError("pa_decode runs on the GPU: q must be a cuda tensor")
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("block_tables", block_tables),
@@ -215,7 +251,7 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, blo
     """
     if out is None:
         out = torch.empty_like(q)
-    _validate_tensors(q, k_cache, v_cache, block_tables, seq_lens, out)
+    _validate_tensors(q, k_cache, v_cache, block_tables, seq_lens, out, num_kv_heads)
     dims = make_dims(q, k_cache, block_tables, kv_dtype=kv_dtype, max_seq_len=max_seq_len,
                      partition_tokens=partition_tokens, kernel=kernel, k_scale=k_scale, v_scale=v_scale,
                      schedule=schedule, waves_per_item=waves_per_item, k_block_scales=k_block_scales,
@@ -252,7 +288,7 @@ class DecodeCall:
                  workspace=None, kv_dtype=None, max_seq_len=0, partition_tokens=0, kernel="auto",
                  k_scale=1.0, v_scale=1.0, schedule="auto", waves_per_item=0, k_block_scales=None,
                  v_block_scales=None):
-        _validate_tensors(q, k_cache, v_cache, block_tables, seq_lens, out)
+        _validate_tensors(q, k_cache, v_cache, block_tables, seq_lens, out, num_kv_heads)
         self.dims = make_dims(q, k_cache, block_tables, kv_dtype=kv_dtype, max_seq_len=max_seq_len,
                               partition_tokens=partition_tokens, kernel=kernel, k_scale=k_scale, v_scale=v_scale,
                               schedule=schedule, waves_per_item=waves_per_item,
@@ -310,7 +346,20 @@ def pa_cache_append(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Ten
         raise TypeError("k_new / v_new: same shape, float32 or bfloat16")
     if token_seq.dtype != torch.int32 or token_pos.dtype != torch.int32 or block_tables.dtype != torch.int32:
         raise TypeError("block_tables, token_seq and token_pos must be int32")
-    n, hkv, _ = k_new.shape
+    if k_new.dim() != 3 or k_cache.dim() != 4 or block_tables.dim() != 2:
+        _shape_error("k_new [num_tokens, num_kv_heads, head_dim], k_cache [NB, Hkv, D, bs], "
+                     "block_tables [S, max_blocks] expected")
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        _shape_error("v_cache must match k_cache")
+    n, hkv, d = k_new.shape
+    if (hkv, d) != (k_cache.shape[1], k_cache.shape[2]):
+        _shape_error(f"k_new rows are [{hkv}, {d}], the cache holds [{k_cache.shape[1]}, {k_cache.shape[2]}] "
+                     f"(num_kv_heads, head_dim)")
+    if token_seq.dim() != 1 or token_pos.dim() != 1 or token_seq.numel() != n or token_pos.numel() != n:
+        _shape_error(f"token_seq {tuple(token_seq.shape)} and token_pos {tuple(token_pos.shape)} must both "
+                     f"have num_tokens = {n} entries")
+    if k_cache.device.type != "cuda":
+        raise ValueError("pa_cache_append runs on the GPU: the caches must be cuda tensors")
     dims = _cache_dims(k_cache, block_tables, kv_dtype, k_scale, v_scale, k_block_scales, v_block_scales)
     stream = ctypes.c_void_p(torch.cuda.current_stream(k_cache.device).cuda_stream)
     rc = load_library().pa_cache_append(
@@ -330,8 +379,15 @@ def pa_cache_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, src_block
     for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("src_blocks", src_blocks), ("dst_blocks", dst_blocks)):
         if t.device != k_cache.device or not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous on the caches' device")
-    if src_blocks.dtype != torch.int32 or dst_blocks.dtype != torch.int32 or src_blocks.shape != dst_blocks.shape:
-        raise TypeError("src_blocks / dst_blocks: int32 of the same length")
+    if src_blocks.dtype != torch.int32 or dst_blocks.dtype != torch.int32:
+        raise TypeError("src_blocks / dst_blocks must be int32")
+    if src_blocks.dim() != 1 or src_blocks.shape != dst_blocks.shape:
+        _shape_error(f"src_blocks {tuple(src_blocks.shape)} and dst_blocks {tuple(dst_blocks.shape)} must be "
+                     f"1-D of the same length")
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        _shape_error("k_cache [NB, Hkv, D, bs] and a v_cache of the same shape and dtype expected")
+    if k_cache.device.type != "cuda":
+        raise ValueError("pa_cache_copy_blocks runs on the GPU: the caches must be cuda tensors")
     dims = _cache_dims(k_cache, None, kv_dtype, 1.0, 1.0, k_block_scales, v_block_scales)
     stream = ctypes.c_void_p(torch.cuda.current_stream(k_cache.device).cuda_stream)
     rc = load_library().pa_cache_copy_blocks(

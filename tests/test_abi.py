@@ -304,3 +304,112 @@ def test_probe_constants_match_the_header():
     defs = dict(re.findall(r"#define\s+(PA_PROBE_\w+)\s+(\d+)", text))
     assert int(defs["PA_PROBE_SINK_WORDS"]) == B.PROBE_SINK_WORDS
     assert int(defs["PA_PROBE_CHUNK_BYTES"]) == B.PROBE_CHUNK_BYTES
+
+
+# ------------------------------------------------------ binding shape checks --
+# The C ABI receives sizes, not allocations, so the binding compares the
+# tensors' shapes with the sizes it passes on and raises PA_ERR_SHAPE first.
+# CPU tensors suffice: every case below fails before the device check and
+# before any library call.
+
+import torch  # noqa: E402
+
+
+def _decode_tensors(S=4, H=16, Hkv=2, D=128, NB=40, MB=5, kv=torch.bfloat16):
+    q = torch.zeros(S, H, D, dtype=torch.bfloat16)
+    k = torch.zeros(NB, Hkv, D, 16, dtype=kv)
+    return dict(q=q, k_cache=k, v_cache=k.clone(), block_tables=torch.zeros(S, MB, dtype=torch.int32),
+                seq_lens=torch.zeros(S, dtype=torch.int32), out=torch.empty_like(q))
+
+
+def _decode(t, hkv=2, **kw):
+    return B.pa_decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["seq_lens"], hkv, 0.125,
+                       t["out"], **kw)
+
+
+@pytest.mark.parametrize("change,hkv", [
+    (dict(), 4),                                                           # num_kv_heads != cache dim 1
+    (dict(), 1),
+    (dict(k_cache=torch.zeros(40, 2, 64, 16, dtype=torch.bfloat16)), 2),  # cache head_dim != q's
+    (dict(block_tables=torch.zeros(3, 5, dtype=torch.int32)), 2),        # table rows != sequences
+    (dict(seq_lens=torch.zeros(5, dtype=torch.int32)), 2),               # seq_lens entries != sequences
+    (dict(seq_lens=torch.zeros(4, 1, dtype=torch.int32)), 2),
+    (dict(out=torch.zeros(4, 16, 64, dtype=torch.bfloat16)), 2),          # out != q
+    (dict(v_cache=torch.zeros(41, 2, 128, 16, dtype=torch.bfloat16)), 2),  # v != k
+    (dict(k_cache=torch.zeros(40, 2, 128, dtype=torch.bfloat16)), 2),     # not 4-D
+])
+def test_decode_shape_mismatch_raises_shape_error(change, hkv):
+    t = _decode_tensors()
+    t.update(change)
+    if "k_cache" in change and "v_cache" not in change:
+        t["v_cache"] = t["k_cache"].clone()
+    with pytest.raises(B.PagedAttentionError) as e:
+        _decode(t, hkv)
+    assert e.value.status == B.PA_ERR_SHAPE
+
+
+def test_decode_shape_mismatch_in_the_prebuilt_call():
+    t = _decode_tensors()
+    with pytest.raises(B.PagedAttentionError) as e:
+        B.DecodeCall(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["seq_lens"], 8, 0.125, t["out"])
+    assert e.value.status == B.PA_ERR_SHAPE
+
+
+def test_cache_element_size_must_match_the_kv_dtype():
+    t = _decode_tensors()
+    with pytest.raises(B.PagedAttentionError) as e:       # a bf16 tensor read as an fp8 cache
+        B.make_dims(t["q"], t["k_cache"], t["block_tables"], kv_dtype="e5m2")
+    assert e.value.status == B.PA_ERR_SHAPE
+    u8 = torch.zeros(40, 2, 128, 16, dtype=torch.uint8)
+    with pytest.raises(B.PagedAttentionError):            # bytes read as a bf16 cache
+        B.make_dims(t["q"], u8, t["block_tables"], kv_dtype="bf16")
+    assert B.make_dims(t["q"], u8, t["block_tables"], kv_dtype="e5m2").block_size == 16
+    assert B.make_dims(t["q"], u8[..., :8].contiguous(), t["block_tables"], kv_dtype="int4").block_size == 16
+
+
+def _append_tensors(n=6, Hkv=2, D=128):
+    k = torch.zeros(40, Hkv, D, 16, dtype=torch.bfloat16)
+    return dict(k_new=torch.zeros(n, Hkv, D), v_new=torch.zeros(n, Hkv, D), k_cache=k, v_cache=k.clone(),
+                block_tables=torch.zeros(3, 5, dtype=torch.int32), token_seq=torch.zeros(n, dtype=torch.int32),
+                token_pos=torch.zeros(n, dtype=torch.int32))
+
+
+@pytest.mark.parametrize("change", [
+    dict(k_new=torch.zeros(6, 4, 128), v_new=torch.zeros(6, 4, 128)),     # more KV heads than the cache
+    dict(k_new=torch.zeros(6, 1, 128), v_new=torch.zeros(6, 1, 128)),
+    dict(k_new=torch.zeros(6, 2, 64), v_new=torch.zeros(6, 2, 64)),       # head_dim differs
+    dict(token_seq=torch.zeros(5, dtype=torch.int32)),                    # list lengths != num_tokens
+    dict(token_pos=torch.zeros(7, dtype=torch.int32)),
+    dict(token_seq=torch.zeros(6, 1, dtype=torch.int32)),
+    dict(k_new=torch.zeros(6, 256), v_new=torch.zeros(6, 256)),           # not 3-D
+    dict(v_cache=torch.zeros(40, 2, 128, 8, dtype=torch.bfloat16)),       # v != k
+])
+def test_append_shape_mismatch_raises_shape_error(change):
+    t = _append_tensors()
+    t.update(change)
+    with pytest.raises(B.PagedAttentionError) as e:
+        B.pa_cache_append(**t)
+    assert e.value.status == B.PA_ERR_SHAPE
+
+
+def test_copy_blocks_shape_mismatch_raises_shape_error():
+    k = torch.zeros(40, 2, 128, 16, dtype=torch.bfloat16)
+    for src, dst in ((torch.zeros(3, dtype=torch.int32), torch.zeros(4, dtype=torch.int32)),
+                     (torch.zeros(2, 2, dtype=torch.int32), torch.zeros(2, 2, dtype=torch.int32))):
+        with pytest.raises(B.PagedAttentionError) as e:
+            B.pa_cache_copy_blocks(k, k.clone(), src, dst)
+        assert e.value.status == B.PA_ERR_SHAPE
+    with pytest.raises(B.PagedAttentionError):
+        B.pa_cache_copy_blocks(k, torch.zeros(40, 2, 128, 8, dtype=torch.bfloat16),
+                               torch.zeros(3, dtype=torch.int32), torch.zeros(3, dtype=torch.int32))
+
+
+def test_well_shaped_cpu_tensors_fail_on_the_device_check_only():
+    t = _decode_tensors()
+    with pytest.raises(ValueError, match="GPU"):
+        _decode(t, 2)
+    with pytest.raises(ValueError, match="GPU"):
+        B.pa_cache_append(**_append_tensors())
+    k = torch.zeros(40, 2, 128, 16, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        B.pa_cache_copy_blocks(k, k.clone(), torch.zeros(3, dtype=torch.int32), torch.zeros(3, dtype=torch.int32))
