@@ -35,12 +35,40 @@
  * the host before any HIP call, so a rejected call enqueues nothing. There is
  * no global error state; pa_status_str() names a status.
  *
+ * Caller's obligations on the buffers (this interface receives sizes, not
+ * allocations, so it cannot check them; a mismatch is an out-of-bounds access):
+ * each cache holds num_blocks * num_kv_heads * head_dim * block_size elements
+ * in the layout above, i.e. its KV-head axis has exactly num_kv_heads entries
+ * and its head_dim axis is q's; q and out hold num_seqs * q_len * num_heads *
+ * head_dim elements; block_tables num_seqs rows of max_blocks_per_seq; seq_lens
+ * num_seqs entries; per-block scale arrays num_blocks * num_kv_heads floats.
+ * The Python binding compares these with the tensors' shapes (and the element
+ * size with kv_dtype) and raises PA_ERR_SHAPE before calling the library.
+ *
  * Device-side preconditions (not checked, the data lives on the device):
  *   0 <= seq_lens[s] <= min(max_seq_len, max_blocks_per_seq * block_size)
  *   0 <= block_tables[s][j] < num_blocks for j < ceil(seq_lens[s] / block_size)
  * Table entries past ceil(seq_lens[s] / block_size), and cache slots past
  * seq_lens[s] in the last block, are never read. Several sequences may map
  * to the same physical block (shared prefixes).
+ *
+ * Numeric range. Every kernel accumulates in float32 and needs the scores
+ * scale * k_scale * (block scale) * q . K to be finite in float32. The
+ * matrix-core kernel's fp8 and int4 paths multiply binary16 operands; they
+ * take any finite bf16 q and any per-block scale in [2^-100, 2^100] without
+ * loss of range:
+ *   - each (query position, head) row of q is multiplied by the power of two
+ *     that puts its largest magnitude in [2^14, 2^15) before rounding to
+ *     binary16 (exact for every element down to 2^-28 of that maximum), and
+ *     its scores are multiplied back in float32; this requires
+ *     |scale * k_scale * k_block_scale| * max|q| < 2^100;
+ *   - a per-block V scale is split into a mantissa in [1, 2), which multiplies
+ *     the softmax weights fed to the matrix cores (kept in [0, 2)), and a power
+ *     of two, added to the score in the log2 domain, so the running maximum
+ *     follows weight x scale and no fed weight overflows or loses precision.
+ * The softmax weights enter the P.V product as a rounded 16-bit value plus its
+ * rounding residual: about 16 significant bits with bf16 operands, 22 with
+ * binary16 ones.
  */
 #ifndef PA_DECODE_H
 #define PA_DECODE_H

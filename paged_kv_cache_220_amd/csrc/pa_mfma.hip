@@ -39,7 +39,12 @@
 //
 // fp8 KV (E5M2 here, E4M3 below): an E5M2 byte is the top byte of the binary16 of the same
 // value, so v_perm_b32 widens K and V to fp16 exactly and the f16 MFMA runs
-// with q rounded to fp16 (exact for bf16 q in [2^-14, 65504]).
+// with q in binary16. Each query column is first scaled by a power of two that
+// puts its largest |q| in [2^14, 2^15) (the scores are scaled back in fp32), so
+// every bf16 q converts exactly down to 2^-28 of the column's maximum, and no
+// finite q overflows. Per-block V scales are split into mantissa and exponent:
+// the mantissa multiplies P, the exponent joins the score (see softmax), so P
+// stays in [0, 2) whatever the scales.
 // bf16 KV: bf16 MFMA with q exact. In both, P enters the PV product as two
 // 16-bit operands (the rounded weight and its rounding residual), so the
 // weights carry about twice the operand precision into the fp32 accumulator.
@@ -105,8 +110,10 @@ template <> struct Mfma<kBF16> {
     }
     return x;
   }
-  // q is bf16 already: the operand is its bits, packed two per register.
-  static __device__ __forceinline__ op_t q_operand(const uint32_t (&qb)[8]) {
+  // q is bf16 already: the operand is its bits, packed two per register
+  // (bf16 has float32's exponent range, so q needs no rescaling).
+  static constexpr bool kRescaleQ = false;
+  static __device__ __forceinline__ op_t q_operand(const uint32_t (&qb)[8], int) {
     u32x4 x;
 #pragma unroll
     for (int w = 0; w < 4; ++w) x[w] = qb[2 * w] | (qb[2 * w + 1] << 16);
@@ -167,10 +174,16 @@ template <> struct Mfma<kE5M2> {
     }
     return x;
   }
-  static __device__ __forceinline__ op_t q_operand(const uint32_t (&qb)[8]) {
+  // q (bf16) times 2^shift, rounded to binary16. The caller picks the shift
+  // per query column so that its largest |q| lands in [2^14, 2^15): every
+  // element within 2^-28 of that maximum is then a normal binary16, exact
+  // (bf16 carries 8 significant bits, binary16 11), and nothing overflows.
+  // The scores are scaled back by 2^-shift in float32.
+  static constexpr bool kRescaleQ = true;
+  static __device__ __forceinline__ op_t q_operand(const uint32_t (&qb)[8], int shift) {
     op_t o;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = static_cast<_Float16>(bf16_bits_to_f32(qb[i]));
+    for (int i = 0; i < 8; ++i) o[i] = static_cast<_Float16>(__builtin_amdgcn_ldexpf(bf16_bits_to_f32(qb[i]), shift));
     return o;
   }
   static __device__ __forceinline__ void p_operands(const float (&p)[8], op_t& hi, op_t& lo) {
@@ -240,7 +253,10 @@ template <> struct Mfma<kI4> {
   static __device__ __forceinline__ vload_t mask_v(vload_t x, int nvalid) {
     return nvalid >= 8 ? x : (nvalid <= 0 ? 0u : x & ((1u << (4 * nvalid)) - 1u));   // code 0 = value 0
   }
-  static __device__ __forceinline__ op_t q_operand(const uint32_t (&qb)[8]) { return Mfma<kE5M2>::q_operand(qb); }
+  static constexpr bool kRescaleQ = true;
+  static __device__ __forceinline__ op_t q_operand(const uint32_t (&qb)[8], int shift) {
+    return Mfma<kE5M2>::q_operand(qb, shift);
+  }
   static __device__ __forceinline__ void p_operands(const float (&p)[8], op_t& hi, op_t& lo) {
     Mfma<kE5M2>::p_operands(p, hi, lo);
   }
@@ -286,7 +302,10 @@ template <> struct Mfma<kE4M3> {
     return __builtin_bit_cast(op_t, y);
   }
   static __device__ __forceinline__ vload_t mask_v(vload_t x, int nvalid) { return Mfma<kE5M2>::mask_v(x, nvalid); }
-  static __device__ __forceinline__ op_t q_operand(const uint32_t (&qb)[8]) { return Mfma<kE5M2>::q_operand(qb); }
+  static constexpr bool kRescaleQ = true;
+  static __device__ __forceinline__ op_t q_operand(const uint32_t (&qb)[8], int shift) {
+    return Mfma<kE5M2>::q_operand(qb, shift);
+  }
   static __device__ __forceinline__ void p_operands(const float (&p)[8], op_t& hi, op_t& lo) {
     Mfma<kE5M2>::p_operands(p, hi, lo);
   }
@@ -345,6 +364,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   op_t qop[NCG][kKSteps];
   int lim[NCG];                // tokens the column's query may attend: t < lim
   float qsum[NCG];             // int4: sum_d q[d] of the column
+  float qss[NCG];              // score scale of the column: scale * k_scale * log2(e) * 2^-(q shift)
   uint32_t qraw[NCG][kKSteps][8];
 #pragma unroll
   for (int cg = 0; cg < NCG; ++cg) {
@@ -365,12 +385,27 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
 #pragma unroll
     for (int cg = 0; cg < NCG; ++cg) {
       const bool col_ok = v0 + 16 * cg + n < GV;
+      // binary16 operands: the column's largest |q| (bf16 magnitudes order as
+      // integers; the column spans the four lane groups) sets a power of two
+      // that brings it into [2^14, 2^15); the score scale undoes it in float32.
+      int shift = 0;
+      uint32_t qmax = 0;
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) qraw[cg][ks][i] = col_ok ? qraw[cg][ks][i] : 0u;
-        qop[cg][ks] = M::q_operand(qraw[cg][ks]);
+        for (int i = 0; i < 8; ++i) {
+          qraw[cg][ks][i] = col_ok ? qraw[cg][ks][i] : 0u;
+          qmax = max(qmax, qraw[cg][ks][i] & 0x7FFFu);
+        }
       }
+      if constexpr (M::kRescaleQ) {
+        qmax = max(qmax, (uint32_t)__shfl_xor((int)qmax, 16, 64));
+        qmax = max(qmax, (uint32_t)__shfl_xor((int)qmax, 32, 64));
+        shift = 15 - __builtin_amdgcn_frexp_expf(bf16_bits_to_f32(qmax));   // max in [2^(e-1), 2^e)
+      }
+      qss[cg] = M::kRescaleQ ? __builtin_amdgcn_ldexpf(a.score_scale, -shift) : a.score_scale;
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks) qop[cg][ks] = M::q_operand(qraw[cg][ks], shift);
       if constexpr (KDT == kI4) {
         // sum over head_dim of the binary16 q values the MFMA uses
         float qs = 0.f;
@@ -481,6 +516,16 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   // ksc[x] / vsc[x]: per-block K / V scale of the tile's block (c >> 1) + 2x
   // (1 without per-block scales); quartets r = 2x, 2x + 1 and PV instruction x
   // of this lane lie in that block.
+  //
+  // With per-block V scales, the weight fed to PV for a token of block x is
+  // p * vsc[x], which a 16-bit operand cannot hold for every scale (it
+  // overflows above about 2^15 and loses bits below 2^-14). So vsc[x] is split
+  // into vm[x] * 2^ve[x] with vm in [1, 2): the power of two joins the score
+  // (s' = s + ve, exact in the log2 domain) and the running max follows s',
+  // so the largest fed weight of the state is 2^0 * vm, whatever the scales.
+  // PV receives 2^(s' - m) * vm = 2^(s - m) * vsc, and the running sum adds
+  // 2^(s' - m) * 2^-ve = 2^(s - m): the state (m, l, o) keeps its meaning with
+  // m the reference of both sums, and o / l is unchanged.
   auto softmax = [&](const int cg, const f32x4 (&sg)[4], const int t0, op_t (&phi)[2], op_t (&plo)[2],
                      const float (&ksc)[2], const float (&vsc)[2])
       __attribute__((always_inline)) {
@@ -488,14 +533,23 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     float sc[4][4];                             // [r][j]; tokens outside the window: -inf
     float tmax = -INFINITY;
     float ka[2], kb[2];                         // score = product * ka + kb, per block of the lane
+    float vm[2];                                // V scale's mantissa (1 without per-block scales)
+    int ve[2];                                  // and its exponent
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
-      if constexpr (KDT == kI4) {
-        ka[x] = a.score_scale * ksc[x] * Mfma<kI4>::kUnit;
-        kb[x] = -(a.score_scale * ksc[x]) * (Mfma<kI4>::kOffset * qsum[cg]);
+      if constexpr (BSCALE) {
+        ve[x] = __builtin_amdgcn_frexp_expf(vsc[x]) - 1;
+        vm[x] = 2.f * __builtin_amdgcn_frexp_mantf(vsc[x]);
       } else {
-        ka[x] = a.score_scale * ksc[x];
-        kb[x] = 0.f;
+        ve[x] = 0;
+        vm[x] = 1.f;
+      }
+      if constexpr (KDT == kI4) {
+        ka[x] = qss[cg] * ksc[x] * Mfma<kI4>::kUnit;
+        kb[x] = -(qss[cg] * ksc[x]) * (Mfma<kI4>::kOffset * qsum[cg]) + (float)ve[x];
+      } else {
+        ka[x] = qss[cg] * ksc[x];
+        kb[x] = (float)ve[x];
       }
     }
 #pragma unroll
@@ -503,6 +557,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if constexpr (KDT == kI4) sc[r][j] = fmaf(sg[j][r], ka[r >> 1] * (1.f / Mfma<kI4>::kKScale[j]), kb[r >> 1]);
+        else if constexpr (BSCALE) sc[r][j] = fmaf(sg[j][r], ka[r >> 1], kb[r >> 1]);
         else sc[r][j] = sg[j][r] * ka[r >> 1];
       }
     }
@@ -530,17 +585,20 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run[cg] - m_use);
     m_run[cg] = m_new;
-    float psum = 0.f;
+    float psum[2] = {0.f, 0.f};                 // per block of the lane
     float p[4][4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         p[r][j] = __builtin_amdgcn_exp2f(sc[r][j] - m_use);
-        psum += p[r][j];
+        psum[r >> 1] += p[r][j];
       }
     }
-    l_run[cg] = l_run[cg] * alpha + psum;
+    if constexpr (BSCALE)
+      l_run[cg] = l_run[cg] * alpha + (__builtin_amdgcn_ldexpf(psum[0], -ve[0]) + __builtin_amdgcn_ldexpf(psum[1], -ve[1]));
+    else
+      l_run[cg] = l_run[cg] * alpha + (psum[0] + psum[1]);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) oacc[cg][dt] *= alpha;
     // PV instruction hh takes quartets r = 2hh, 2hh+1 (token i of the lane's
@@ -554,18 +612,18 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
         // (exactly); the sums add exactly the rounded values PV receives (the
         // empty asm keeps the compiler from fusing the product into the sum,
         // which it would do in some instantiations and not in others)
-        const float vs16 = vsc[hh] * 0.0625f;
+        const float vs16 = vm[hh] * 0.0625f;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           const int i = Mfma<kI4>::kVTok[k];
-          pv[k] = p[2 * hh + (i >> 2)][i & 3] * (Mfma<kI4>::kVHigh[k] ? vs16 : vsc[hh]);
+          pv[k] = p[2 * hh + (i >> 2)][i & 3] * (Mfma<kI4>::kVHigh[k] ? vs16 : vm[hh]);
           asm("" : "+v"(pv[k]));
           if (Mfma<kI4>::kVHigh[k]) pv_hi += pv[k];
           else pv_lo += pv[k];
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pv[i] = p[2 * hh + (i >> 2)][i & 3] * vsc[hh];
+        for (int i = 0; i < 8; ++i) pv[i] = p[2 * hh + (i >> 2)][i & 3] * vm[hh];
       }
       M::p_operands(pv, phi[hh], plo[hh]);
     }
