@@ -65,12 +65,6 @@ def oracle_full(w):
                           k_block_scales=w.k_block_scales, v_block_scales=w.v_block_scales)
 
 
-def oracle_rows(w, rows):
-    return O.paged_decode_rows(w.q, w.k_cache, w.v_cache, w.block_tables, w.seq_lens, w.num_kv_heads, w.scale,
-                               w.q_dtype, w.kv_dtype, rows, k_scale=float(w.k_scale), v_scale=float(w.v_scale),
-                               k_block_scales=w.k_block_scales, v_block_scales=w.v_block_scales)
-
-
 def check(got, ref, w, label=""):
     """The task's absolute bar, plus a relative gate for bf16 outputs.
 
