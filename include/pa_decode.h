@@ -197,6 +197,25 @@ int pa_decode_ws(const void* q, const void* k_cache, const void* v_cache,
                  const pa_dims_t* dims, void* workspace, size_t workspace_bytes,
                  void* stream);
 
+/* Decode for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): pa_decode
+ * with the workspace taken from a fixed device array inside the library, one
+ * per GPU, of PA_NOALLOC_SCRATCH_BYTES, held until the process ends. It calls
+ * no allocator. A call whose plan needs more (pa_decode_workspace_bytes)
+ * returns PA_ERR_WORKSPACE before any HIP call. 128 MiB holds the partition
+ * states of 256 sequences x 8 KV heads x 8 query heads at 32K tokens (65 MiB),
+ * or 16 query positions of 16 such sequences (65 MiB). Every call on
+ * one GPU uses that GPU's same array: calls that may overlap on a GPU (other
+ * streams, other host threads) race and must be ordered by the caller; calls
+ * on one stream are ordered by it. Results are those of pa_decode_ws with the
+ * same arguments (same kernels, same plan). The array's device address is
+ * looked up on the first call on each GPU (the stream's device). */
+#define PA_NOALLOC_SCRATCH_BYTES (128u << 20)
+int pa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* seq_lens,
+                      int32_t num_kv_heads, float scale, void* out,
+                      const pa_dims_t* dims, void* stream);
+
 /* pa_decode_ws that also records three caller-created HIP events (hipEvent_t
  * as void*) on `stream`: ev_start and ev_mid at the start and end of the
  * partition kernel's execution (for the matrix-core kernel they are attached

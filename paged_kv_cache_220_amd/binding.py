@@ -25,8 +25,9 @@ SCHEDULES = {"auto": 0, "grid": 1, "queue": 2}
 SCHEDULE_NAMES = {v: k for k, v in SCHEDULES.items()}
 
 # Symbols declared in include/pa_decode.h and include/pa_cache.h.
-EXPORTED = ("pa_decode", "pa_decode_ws", "pa_decode_ws_timed", "pa_decode_workspace_bytes",
+EXPORTED = ("pa_decode", "pa_decode_ws", "pa_decode_ws_timed", "pa_decode_noalloc", "pa_decode_workspace_bytes",
             "pa_decode_plan", "pa_status_str", "pa_version", "pa_cache_append", "pa_cache_copy_blocks", "pa_read_probe")
+NOALLOC_SCRATCH_BYTES = 128 << 20   # PA_NOALLOC_SCRATCH_BYTES
 
 
 class PaDims(ctypes.Structure):
@@ -76,6 +77,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.pa_decode_ws.restype = ctypes.c_int
     lib.pa_decode_ws_timed.argtypes = common + [vp, sz, vp, vp, vp, vp]
     lib.pa_decode_ws_timed.restype = ctypes.c_int
+    lib.pa_decode_noalloc.argtypes = common + [vp]
+    lib.pa_decode_noalloc.restype = ctypes.c_int
     lib.pa_decode_workspace_bytes.argtypes = [dims_p, i32, ctypes.POINTER(ctypes.c_int)]
     lib.pa_decode_workspace_bytes.restype = sz
     lib.pa_decode_plan.argtypes = [dims_p, i32, ctypes.POINTER(PaPlan)]
@@ -276,6 +279,28 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, blo
             ev = [ctypes.c_void_p(e) if e else None for e in events]
             rc = lib.pa_decode_ws_timed(*args, *ws, stream, *ev)
     _check(rc)
+    return out
+
+
+def pa_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+                      seq_lens: torch.Tensor, num_kv_heads: int, scale: float, out: torch.Tensor, *,
+                      kv_dtype: Optional[str] = None, max_seq_len: int = 0, partition_tokens: int = 0,
+                      kernel: str = "auto", k_scale: float = 1.0, v_scale: float = 1.0, schedule: str = "auto",
+                      waves_per_item: int = 0, k_block_scales: Optional[torch.Tensor] = None,
+                      v_block_scales: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``pa_decode_noalloc``: decode without any allocation, the workspace taken
+    from the library's fixed per-GPU scratch array (NOALLOC_SCRATCH_BYTES). The
+    caller passes `out`; calls that may overlap on one GPU must be ordered."""
+    _validate_tensors(q, k_cache, v_cache, block_tables, seq_lens, out, num_kv_heads)
+    dims = make_dims(q, k_cache, block_tables, kv_dtype=kv_dtype, max_seq_len=max_seq_len,
+                     partition_tokens=partition_tokens, kernel=kernel, k_scale=k_scale, v_scale=v_scale,
+                     schedule=schedule, waves_per_item=waves_per_item, k_block_scales=k_block_scales,
+                     v_block_scales=v_block_scales)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(q.device).cuda_stream)
+    _check(load_library().pa_decode_noalloc(
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_cache.data_ptr()), ctypes.c_void_p(v_cache.data_ptr()),
+        ctypes.c_void_p(block_tables.data_ptr()), ctypes.c_void_p(seq_lens.data_ptr()), ctypes.c_int32(num_kv_heads),
+        ctypes.c_float(scale), ctypes.c_void_p(out.data_ptr()), ctypes.byref(dims), stream))
     return out
 
 

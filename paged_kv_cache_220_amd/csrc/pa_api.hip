@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "pa_internal.h"
 
@@ -266,6 +267,45 @@ int run(const void* q, const void* k_cache, const void* v_cache, const int32_t* 
   return PA_OK;
 }
 
+// Scratch of pa_decode_noalloc: a device array of fixed size in this
+// library's code object, one copy per GPU (each device that loads the code
+// object holds its own), kept until the process ends. In host code the name
+// `scratch` is only a stand-in: its device address on a GPU comes from
+// hipGetSymbolAddress with that GPU current, looked up once per device and
+// kept in scratch_ptr. Nothing in it has to start at zero: the partition
+// kernel writes every state the merge kernel reads, and the plan kernel of the
+// list schedule writes the list and its length.
+static __device__ __align__(256) uint8_t scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the GPU that runs `stream` (the current
+// device for the null stream).
+int scratch_for(hipStream_t stream, void** out) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return PA_ERR_HIP;
+  int dev = cur;
+  if (stream != nullptr) {
+    hipDevice_t d = 0;
+    if (hipStreamGetDevice(stream, &d) != hipSuccess) return PA_ERR_HIP;
+    dev = d;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return PA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return PA_ERR_HIP;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return PA_ERR_HIP;
+    if (e != hipSuccess || ptr == nullptr) return PA_ERR_HIP;
+    scratch_ptr[dev] = ptr;
+  }
+  *out = scratch_ptr[dev];
+  return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -325,6 +365,22 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
                      p.ws_bytes, s, nullptr, nullptr, nullptr);
   if (ws != nullptr && hipFreeAsync(ws, s) != hipSuccess && rc == PA_OK) return PA_ERR_HIP;
   return rc;
+}
+
+int pa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                      const int32_t* seq_lens, int32_t num_kv_heads, float scale, void* out,
+                      const pa_dims_t* dims, void* stream) {
+  if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !out) return PA_ERR_NULL;
+  Plan p;
+  const int st = make_plan(dims, num_kv_heads, &p);
+  if (st != PA_OK) return st;
+  if (p.ws_bytes > (size_t)PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_WORKSPACE;   // before any HIP call
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  const int sst = scratch_for(s, &ws);
+  if (sst != PA_OK) return sst;
+  return run(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale, out, dims, ws,
+             (size_t)PA_NOALLOC_SCRATCH_BYTES, s, nullptr, nullptr, nullptr);
 }
 
 const char* pa_status_str(int status) {

@@ -413,3 +413,24 @@ def test_well_shaped_cpu_tensors_fail_on_the_device_check_only():
     k = torch.zeros(40, 2, 128, 16, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         B.pa_cache_copy_blocks(k, k.clone(), torch.zeros(3, dtype=torch.int32), torch.zeros(3, dtype=torch.int32))
+
+
+def test_noalloc_rejects_before_any_hip_call(lib):
+    """pa_decode_noalloc: NULL pointers and a plan whose workspace exceeds the
+    fixed scratch are refused before the library touches the GPU."""
+    fake = ctypes.c_void_p(1 << 20)
+    big = dims(num_seqs=600, max_seq_len=32768)          # 600 x 8 KV heads x 8 partitions of states
+    assert B.plan(big, 8)["workspace_bytes"] > B.NOALLOC_SCRATCH_BYTES
+    args = [fake] * 5 + [8, ctypes.c_float(0.1), fake, ctypes.byref(big), None]
+    assert lib.pa_decode_noalloc(*args) == B.PA_ERR_WORKSPACE
+    args[0] = None
+    assert lib.pa_decode_noalloc(*args) == B.PA_ERR_NULL
+    bad = dims(num_heads=60)
+    assert lib.pa_decode_noalloc(*([fake] * 5 + [8, ctypes.c_float(0.1), fake, ctypes.byref(bad), None])) == \
+        B.PA_ERR_SHAPE
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    text = open(os.path.join(ROOT, "include", "pa_decode.h")).read()
+    m = re.search(r"#define PA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.NOALLOC_SCRATCH_BYTES
