@@ -66,7 +66,7 @@ import numpy as np
 
 __all__ = [
     "decode_bits", "e5m2_value", "logical_kv", "paged_decode", "paged_decode_rows",
-    "online_decode", "merge_partials", "dense_attention",
+    "online_decode", "merge_partials", "softmax_state", "combine_states", "dense_attention",
     "e5m2_encode", "bf16_encode", "encode_bits", "paged_append", "copy_blocks",
     "paged_attention_multi", "e4m3_value", "e4m3_encode",
     "int4_pack", "int4_unpack", "int4_encode", "block_values",
@@ -260,78 +260,84 @@ def paged_decode(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scal
 
 
 # ----------------------------------------------------------------------------
-# second implementation: the pages' block-by-block online softmax
+# second implementation: streaming softmax states folded chunk by chunk
 # ----------------------------------------------------------------------------
+# The decode kernel on "vLLM e PagedAttention" (its kernel pseudocode) keeps a
+# running maximum, a running sum and a rescaled output while it walks the
+# sequence's blocks. The same quantity is written here as a fold over softmax
+# states. A state (m, l, o) summarises a stretch of tokens: m is its largest
+# score, l the sum of exp(score - m) and o the same weights times the V rows.
+# Two states of disjoint stretches combine by rescaling both to the larger m;
+# the attention output of a stretch is o / l. Because combining is exact up to
+# rounding, stretches of any length, in any grouping, give the two-pass result.
 
-def _online_partition(qv, k_cache, v_cache, table_row, L, g, first_block, last_block, bs,
-                      kv_dtype, scale, k_scale, v_scale, k_block_scales=None, v_block_scales=None):
-    """Online softmax over logical blocks [first_block, last_block) of one sequence.
+_EMPTY_STATE = (-math.inf, 0.0, None)
 
-    Per block: scores = scale * q . K_block; m_new = max(m, max scores);
-    l = e^(m - m_new) l + sum e^(scores - m_new); o = e^(m - m_new) o + V_block e^(scores - m_new).
-    Tokens past L in the last block are left out. Returns (m, l, o) unnormalised.
-    """
-    D = qv.shape[0]
-    m, l, o = -math.inf, 0.0, np.zeros(D, dtype=np.float64)
-    for j in range(first_block, last_block):
-        b = int(table_row[j])
-        n_valid = min(bs, L - j * bs)
-        if n_valid <= 0:
-            break
-        Kb = block_values(k_cache, b, g, kv_dtype, k_scale, k_block_scales)[:, :n_valid]    # [D, n]
-        Vb = block_values(v_cache, b, g, kv_dtype, v_scale, v_block_scales)[:, :n_valid]
-        scores = scale * (qv @ Kb)
-        m_new = max(m, float(scores.max()))
-        alpha = math.exp(m - m_new) if m != -math.inf else 0.0
-        p = np.exp(scores - m_new)
-        l = alpha * l + float(p.sum())
-        o = alpha * o + Vb @ p
-        m = m_new
-    return m, l, o
+
+def softmax_state(scores: np.ndarray, V: np.ndarray):
+    """State (m, l, o) of one stretch of tokens: scores [n], V rows [n, D]."""
+    if scores.size == 0:
+        return _EMPTY_STATE
+    m = float(scores.max())
+    w = np.exp(scores - m)
+    return m, float(w.sum()), w @ V
+
+
+def combine_states(a, b):
+    """State of the union of two disjoint stretches (log-sum-exp rule)."""
+    if a[0] == -math.inf:
+        return b
+    if b[0] == -math.inf:
+        return a
+    top = max(a[0], b[0])
+    fa, fb = math.exp(a[0] - top), math.exp(b[0] - top)
+    return top, fa * a[1] + fb * b[1], fa * a[2] + fb * b[2]
 
 
 def merge_partials(parts: List[Tuple[float, float, np.ndarray]]) -> np.ndarray:
-    """Combine per-partition (m, l, o) states into o_total / l_total.
-
-    The same rescaling the per-block update applies, taken across partitions:
-    M = max m_p, l = sum e^(m_p - M) l_p, o = sum e^(m_p - M) o_p.
-    """
-    live = [(m, l, o) for (m, l, o) in parts if m != -math.inf]
-    if not live:
-        return np.zeros_like(parts[0][2]) if parts else np.zeros(0)
-    M = max(m for m, _, _ in live)
-    lt = sum(math.exp(m - M) * l for m, l, _ in live)
-    ot = sum(math.exp(m - M) * o for m, _, o in live)
-    return ot / lt
+    """Output o / l of the union of several partition states (the merge the
+    partition-split decode applies); an all-empty list gives zeros."""
+    acc = _EMPTY_STATE
+    for st in parts:
+        acc = combine_states(acc, st)
+    if acc[0] == -math.inf:
+        return np.zeros_like(parts[0][2]) if parts and parts[0][2] is not None else np.zeros(0)
+    return acc[2] / acc[1]
 
 
 def online_decode(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale,
                   q_dtype: str, kv_dtype: str, partition_blocks: Optional[int] = None,
                   k_scale: float = 1.0, v_scale: float = 1.0, k_block_scales=None,
-                  v_block_scales=None) -> np.ndarray:
-    """Block-by-block online softmax, optionally split into partitions of
-    `partition_blocks` logical blocks whose states are merged at the end."""
+                  v_block_scales=None, chunk_tokens: int = 16) -> np.ndarray:
+    """Streaming form: each (sequence, head) folds the states of consecutive
+    chunks of `chunk_tokens` tokens; with `partition_blocks` the sequence is
+    first cut into partitions of that many blocks, each folded on its own, and
+    the partition states are merged at the end."""
     S, H, D, G = _check_shapes(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads)
     bs = _tokens_per_row(k_cache, kv_dtype)
     sc64 = float(np.float32(scale))
     out = np.zeros((S, H, D), dtype=np.float64)
     for s in range(S):
         L = int(seq_lens[s])
-        nblk = (L + bs - 1) // bs
-        step = partition_blocks or max(nblk, 1)
-        for h in range(H):
-            g = h // G
-            qv = decode_bits(q[s, h], q_dtype)
-            parts = [_online_partition(qv, k_cache, v_cache, block_tables[s], L, g, b0,
-                                       min(nblk, b0 + step), bs, kv_dtype, sc64, k_scale, v_scale,
-                                       k_block_scales, v_block_scales)
-                     for b0 in range(0, nblk, step)]
-            out[s, h] = merge_partials(parts) if parts else 0.0
+        if L == 0:
+            continue
+        span = partition_blocks * bs if partition_blocks else L
+        for g in range(num_kv_heads):
+            K = logical_kv(k_cache, block_tables, s, L, g, kv_dtype, k_scale, k_block_scales)
+            V = logical_kv(v_cache, block_tables, s, L, g, kv_dtype, v_scale, v_block_scales)
+            for h in range(g * G, (g + 1) * G):
+                qv = decode_bits(q[s, h], q_dtype)
+                parts = []
+                for p0 in range(0, L, span):
+                    st = _EMPTY_STATE
+                    for c0 in range(p0, min(L, p0 + span), chunk_tokens):
+                        c1 = min(L, p0 + span, c0 + chunk_tokens)
+                        st = combine_states(st, softmax_state(sc64 * (K[c0:c1] @ qv), V[c0:c1]))
+                    parts.append(st)
+                out[s, h] = merge_partials(parts)
     return out
 
 
-# ----------------------------------------------------------------------------
-# writing the cache: encoders, the paged append and the block copy
 # ----------------------------------------------------------------------------
 #
 # "Optimização da inferência", "Caches de KV": when token N is generated, only

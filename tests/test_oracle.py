@@ -263,14 +263,42 @@ def test_poisoned_unread_memory_changes_nothing(name, kw):
 
 @pytest.mark.parametrize("name,kw", [("c1", {}), ("c2", dict(num_seqs=2)),
                                      ("c5", dict(num_seqs=2, seq_len=700))])
-@pytest.mark.parametrize("pblocks", [None, 1, 3, 8])
-def test_online_softmax_matches_two_pass(name, kw, pblocks):
+@pytest.mark.parametrize("pblocks,chunk", [(None, 16), (1, 16), (3, 7), (8, 1), (None, 100), (2, 5)])
+def test_online_softmax_matches_two_pass(name, kw, pblocks, chunk):
+    """Folding softmax states over chunks (of any length, not tied to the
+    blocks) and partitions reaches the two-pass result."""
     w = W.make_workload(name, **kw)
     ref = run_oracle(w)
     got = O.online_decode(w.q, w.k_cache, w.v_cache, w.block_tables, w.seq_lens, w.num_kv_heads,
-                          w.scale, w.q_dtype, w.kv_dtype, partition_blocks=pblocks)
+                          w.scale, w.q_dtype, w.kv_dtype, partition_blocks=pblocks, chunk_tokens=chunk)
     err = np.abs(got - ref).max() / np.abs(ref).max()
     assert err <= 1e-12
+
+
+def test_online_state_rule_mistakes_are_caught(monkeypatch):
+    """A combine that forgets to rescale to the common maximum, or rescales the
+    newer state with the older one's factor, no longer reaches two-pass."""
+    w = W.make_workload("c2", num_seqs=2)
+    ref = run_oracle(w)
+    good = O.combine_states
+
+    def no_rescale(a, b):
+        if a[0] == -math.inf or b[0] == -math.inf:
+            return good(a, b)
+        return max(a[0], b[0]), a[1] + b[1], a[2] + b[2]
+
+    def one_factor(a, b):
+        if a[0] == -math.inf or b[0] == -math.inf:
+            return good(a, b)
+        top = max(a[0], b[0])
+        f = math.exp(a[0] - top)
+        return top, f * (a[1] + b[1]), f * (a[2] + b[2])
+
+    for bad in (no_rescale, one_factor):
+        monkeypatch.setattr(O, "combine_states", bad)
+        got = O.online_decode(w.q, w.k_cache, w.v_cache, w.block_tables, w.seq_lens, w.num_kv_heads,
+                              w.scale, w.q_dtype, w.kv_dtype)
+        assert np.abs(got - ref).max() > 1e-3, bad.__name__
 
 
 def test_merge_of_random_splits():
@@ -360,14 +388,16 @@ def test_kv_size_formula_matches_page_example():
 
 # ------------------------------------------------- several query positions --
 
-def _masked_sdpa_pages_form(qrows, K, V, scale):
-    """The inference page's attention with seq_len_q > 1: additive -1e9 upper-triangular mask."""
+def _causal_attention(qrows, K, V, scale):
+    """Attention of the last Lq positions over Lk cached tokens with the causal
+    rule of "Optimização da inferência", step 2 (attention with the KV cache,
+    several query rows): row i may see key j only when j <= i + (Lk - Lq).
+    Hidden keys get a score of -inf, so they take no weight at all."""
     Lq, Lk = qrows.shape[0], K.shape[0]
-    scores = (qrows @ K.T) * scale
-    mask = np.triu(np.ones((Lq, Lk)), k=Lk - Lq + 1)
-    scores = scores + mask * (-1e9)
-    e = np.exp(scores - scores.max(axis=-1, keepdims=True))
-    return (e / e.sum(axis=-1, keepdims=True)) @ V
+    visible = np.arange(Lk)[None, :] <= np.arange(Lq)[:, None] + (Lk - Lq)
+    scores = np.where(visible, scale * (qrows @ K.T), -np.inf)
+    weights = np.exp(scores - scores.max(axis=1, keepdims=True))
+    return (weights @ V) / weights.sum(axis=1, keepdims=True)
 
 
 @pytest.mark.parametrize("ql", [1, 2, 5])
@@ -382,7 +412,7 @@ def test_multi_query_matches_masked_dense_form(ql):
             K = O.logical_kv(w.k_cache, w.block_tables, s, L, g, "bf16")
             V = O.logical_kv(w.v_cache, w.block_tables, s, L, g, "bf16")
             for h in range(g * 8, g * 8 + 8):
-                ref = _masked_sdpa_pages_form(O.decode_bits(q[s, :, h], "bf16"), K, V, float(np.float32(w.scale)))
+                ref = _causal_attention(O.decode_bits(q[s, :, h], "bf16"), K, V, float(np.float32(w.scale)))
                 assert np.allclose(got[s, :, h], ref, rtol=1e-12, atol=1e-13)
 
 
@@ -418,7 +448,7 @@ def _pinned_multi_query_holds(attend_fn):
             K = O.logical_kv(w.k_cache, w.block_tables, s, L, g, "bf16")
             V = O.logical_kv(w.v_cache, w.block_tables, s, L, g, "bf16")
             for h in (g * 8, g * 8 + 7):
-                ref = _masked_sdpa_pages_form(O.decode_bits(q[s, :, h], "bf16"), K, V, float(np.float32(w.scale)))
+                ref = _causal_attention(O.decode_bits(q[s, :, h], "bf16"), K, V, float(np.float32(w.scale)))
                 if not np.allclose(got[s, :, h], ref, rtol=1e-12, atol=1e-13):
                     return False
     return True
