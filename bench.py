@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--no-read-probe", action="store_true",
                     help="skip the streaming-read probe that measures the chip's practical read ceiling")
     ap.add_argument("--sweep", default="", help="comma list of partition_tokens to time (printed to stderr)")
+    ap.add_argument("--configs", default="auto",
+                    help="comma list of other batches (c1..c5) to time at full size in their default plans and "
+                         "report under `configs`; auto: all five on the default run, none otherwise")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="dispatch a device copy of this many MiB first (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -167,6 +170,147 @@ def _cpu_model():
     return "unknown"
 
 
+def decode_batch(args_config, kv_dtype, q_len):
+    """The seeded batch (and its name) of one decode measurement."""
+    from paged_kv_cache_220_amd import workloads as W
+    w = W.make_workload(args_config, kv_dtype=kv_dtype or None)
+    batch = args_config + (f"-{kv_dtype}" if kv_dtype else "") + (f"-q{q_len}" if q_len > 1 else "")
+    q_seed = None
+    if q_len > 1:
+        # q_len query rows per sequence (the last q_len tokens of each sequence), seeded apart from the batch
+        q_seed = list(w.seed) + [7, q_len]
+        rng = np.random.default_rng(q_seed)
+        w.q = W.to_storage(rng.standard_normal((w.num_seqs, q_len, w.num_heads, w.head_dim), dtype=np.float32),
+                           w.q_dtype)
+    return w, batch, q_seed
+
+
+def time_decode(w, batch, q_len, dev, hip, steps, warmup, opts, replicas=0):
+    """Time `steps` decode calls (after `warmup`) on resident inputs.
+
+    Returns the plan, the per-step time, the partition kernel's mean time from
+    the library-recorded events of every EVENT_EVERY-th step (the first
+    included), and the figures derived from them. Two events bracket the
+    partition kernel of a sampled step: the matrix-core kernel's dispatch
+    records them itself at the start and end of its execution. Each pair
+    still costs the stream about 5 us, which would otherwise land in every
+    step. None is recorded after the merge kernel.
+    """
+    import torch
+    from paged_kv_cache_220_amd import accounting as A
+    from paged_kv_cache_220_amd import binding as B
+
+    def upload(x, dtype):
+        if dtype == "f32":
+            return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+        if dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+        if dtype == "e4m3":
+            return torch.from_numpy(np.ascontiguousarray(x)).view(torch.float8_e4m3fn).to(dev)
+        if dtype == "int4":
+            return torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).to(dev)     # packed codes
+        return torch.from_numpy(np.ascontiguousarray(x)).view(torch.float8_e5m2).to(dev)
+
+    kv_bytes = A.algorithmic_kv_bytes(w.seq_lens, w.num_kv_heads, w.head_dim, w.kv_dtype)
+    pool_bytes = 2 * w.k_cache.nbytes
+    R = replicas or max(1, int(np.ceil(2 * 2 ** 30 / pool_bytes)))
+    q = upload(w.q, w.q_dtype)
+    tables = torch.from_numpy(w.block_tables).to(dev)
+    seq_lens = torch.from_numpy(w.seq_lens).to(dev)
+    caches = [(upload(w.k_cache, w.kv_dtype), upload(w.v_cache, w.kv_dtype)) for _ in range(R)]
+    out = torch.empty_like(q)
+    scales = {}
+    if w.k_block_scales is not None:   # int4: per-(block, KV head) scales, shared by the replicas
+        scales = dict(k_block_scales=torch.from_numpy(w.k_block_scales).to(dev),
+                      v_block_scales=torch.from_numpy(w.v_block_scales).to(dev))
+    kw = dict(opts, max_seq_len=w.max_seq_len, k_scale=float(w.k_scale), v_scale=float(w.v_scale), **scales)
+    dims = B.make_dims(q, caches[0][0], tables, **kw)
+    plan = B.plan(dims, w.num_kv_heads)
+    ws = B.alloc_workspace(dims, w.num_kv_heads, dev)
+    stream = torch.cuda.current_stream(dev)
+    # arguments marshalled once per replica: a step costs the host one library call
+    calls = [B.DecodeCall(q, k, v, tables, seq_lens, w.num_kv_heads, float(w.scale), out, workspace=ws, **kw)
+             for (k, v) in caches]
+
+    for i in range(warmup):
+        calls[i % R]()
+    torch.cuda.synchronize()
+    timed_steps = list(range(0, steps, EVENT_EVERY))
+    evs = hip.create(2 * len(timed_steps))
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(steps):
+        if i % EVENT_EVERY == 0:
+            j = i // EVENT_EVERY
+            calls[i % R](events=(evs[2 * j], evs[2 * j + 1], None))
+        else:
+            calls[i % R]()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    part_ms = [hip.elapsed_ms(evs[2 * j], evs[2 * j + 1]) for j in range(len(timed_steps))]
+    hip.destroy(evs)
+    del calls, caches, ws, q, out
+    torch.cuda.empty_cache()
+
+    ms_step = total_ms / steps
+    part_avg = float(np.mean(part_ms))
+    kname = "pa_mfma_partition" if plan["kernel"] == "mfma" else "pa_valu_partition"
+    # Attention flops of the launch: QK and PV, 2 * head_dim each per attended
+    # (token, query position, query head); query i of q_len attends L - q_len + 1 + i
+    # tokens. The path is matrix-bound once flops per K/V byte pass the chip's
+    # ratio of the two peaks (bf16 / f16 operands on the matrix cores).
+    L = w.seq_lens.astype(np.float64)[:, None]
+    attended = np.maximum(0.0, L - q_len + 1 + np.arange(q_len)[None, :]).sum()
+    flops = 4.0 * w.head_dim * w.num_heads * attended
+    op_dtype = "bf16" if w.kv_dtype == "bf16" else ("f32" if w.kv_dtype == "f32" else "f16")
+    if plan["kernel"] != "mfma":
+        op_dtype = "f32"
+    mfma_peak = MFMA_PEAK_TFLOPS[op_dtype]
+    traffic = load_traffic(kname, batch, plan)
+    achieved = kv_bytes / (part_avg * 1e-3) / 1e9
+    if flops / kv_bytes > mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9):
+        tf = flops / (part_avg * 1e-3) / 1e12
+        roofline = {"bound": "mfma" if op_dtype != "f32" else "alu", "kernel": kname, "achieved": round(tf, 2),
+                    "peak": mfma_peak, "unit": "TFLOP/s", "frac": round(tf / mfma_peak, 4), "traffic": traffic}
+    else:
+        roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
+    return dict(plan=plan, kv_bytes=kv_bytes, replicas=R, ms_step=ms_step, wall_ms=wall * 1e3 / steps,
+                part_ms=part_ms, part_avg=part_avg, achieved_gbs=achieved, roofline=roofline, flops=flops)
+
+
+def config_row(name, w, q_len, r):
+    """One measured batch in the units of the metric."""
+    gbs = r["kv_bytes"] / (r["ms_step"] * 1e-3) / 1e9
+    traffic = r["roofline"]["traffic"]
+    return {"workload": _title(name, w),
+            "us_per_step": round(r["ms_step"] * 1e3, 2),
+            "kv_bytes_per_step": r["kv_bytes"],
+            "GB_per_s": round(gbs, 2),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "seq_head_per_s": round(w.num_seqs * w.num_heads * q_len / (r["ms_step"] * 1e-3), 1),
+            "partition_kernel_us": round(r["part_avg"] * 1e3, 2),
+            "roofline_frac": r["roofline"]["frac"],
+            "roofline_bound": r["roofline"]["bound"],
+            "traffic_ratio": None if traffic is None else round(traffic / r["kv_bytes"], 4),
+            "kernel": r["plan"]["kernel"], "schedule": r["plan"]["schedule"],
+            "partition_tokens": r["plan"]["partition_tokens"], "waves_per_item": r["plan"]["waves_per_item"],
+            "replicas": r["replicas"]}
+
+
+def _title(name, w):
+    from paged_kv_cache_220_amd import workloads as W
+    base = name.split("-")[0]
+    own_kv = W.batch_heads(base)[4]
+    title = W.CONFIG_TITLES[base] + (f", {w.kv_dtype} KV" if w.kv_dtype != own_kv else "")
+    return title + (f", {name.split('-q')[1]} query positions" if "-q" in name else "")
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -176,9 +320,7 @@ def main():
         sys.exit(2)
 
     import torch
-    from paged_kv_cache_220_amd import accounting as A
     from paged_kv_cache_220_amd import binding as B
-    from paged_kv_cache_220_amd import workloads as W
 
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
@@ -196,135 +338,23 @@ def main():
         torch.cuda.synchronize()
         print(f"copy probe: {n} bytes read and written per dispatch", file=sys.stderr, flush=True)
         del src, dst
-    w = W.make_workload(args.config, kv_dtype=args.kv_dtype or None)
-    batch = args.config + (f"-{args.kv_dtype}" if args.kv_dtype else "") + (f"-q{args.q_len}" if args.q_len > 1 else "")
-    q_seed = None
-    if args.q_len > 1:
-        # q_len query rows per sequence (the last q_len tokens of each sequence), seeded apart from the batch
-        q_seed = list(w.seed) + [7, args.q_len]
-        rng = np.random.default_rng(q_seed)
-        w.q = W.to_storage(rng.standard_normal((w.num_seqs, args.q_len, w.num_heads, w.head_dim), dtype=np.float32),
-                           w.q_dtype)
-
-    def upload(x, dtype):
-        if dtype == "f32":
-            return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
-        if dtype == "bf16":
-            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
-        if dtype == "e4m3":
-            return torch.from_numpy(np.ascontiguousarray(x)).view(torch.float8_e4m3fn).to(dev)
-        if dtype == "int4":
-            return torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).to(dev)     # packed codes
-        return torch.from_numpy(np.ascontiguousarray(x)).view(torch.float8_e5m2).to(dev)
-
-    kv_bytes = A.algorithmic_kv_bytes(w.seq_lens, w.num_kv_heads, w.head_dim, w.kv_dtype)
-    pool_bytes = 2 * w.k_cache.nbytes
-    R = args.replicas or max(1, int(np.ceil(2 * 2 ** 30 / pool_bytes)))
-    q = upload(w.q, w.q_dtype)
-    tables = torch.from_numpy(w.block_tables).to(dev)
-    seq_lens = torch.from_numpy(w.seq_lens).to(dev)
-    caches = [(upload(w.k_cache, w.kv_dtype), upload(w.v_cache, w.kv_dtype)) for _ in range(R)]
-    out = torch.empty_like(q)
-    scales = {}
-    if w.k_block_scales is not None:   # int4: per-(block, KV head) scales, shared by the replicas
-        scales = dict(k_block_scales=torch.from_numpy(w.k_block_scales).to(dev),
-                      v_block_scales=torch.from_numpy(w.v_block_scales).to(dev))
-    kw = dict(kernel=args.kernel, partition_tokens=args.partition_tokens, max_seq_len=w.max_seq_len,
-              k_scale=float(w.k_scale), v_scale=float(w.v_scale), schedule=args.schedule,
-              waves_per_item=args.waves_per_item, **scales)
-    dims = B.make_dims(q, caches[0][0], tables, **kw)
-    plan = B.plan(dims, w.num_kv_heads)
-    ws = B.alloc_workspace(dims, w.num_kv_heads, dev)
     hip = HipEvents()
-    stream = torch.cuda.current_stream(dev)
-    # arguments marshalled once per replica: a step costs the host one library call
-    calls = [B.DecodeCall(q, k, v, tables, seq_lens, w.num_kv_heads, float(w.scale), out, workspace=ws, **kw)
-             for (k, v) in caches]
-
-    def step(i, events=None):
-        calls[i % R](events)
+    opts = dict(kernel=args.kernel, partition_tokens=args.partition_tokens, schedule=args.schedule,
+                waves_per_item=args.waves_per_item)
+    w, batch, q_seed = decode_batch(args.config, args.kv_dtype, args.q_len)
 
     if args.sweep:
         for ptok in [int(x) for x in args.sweep.split(",")]:
-            kw2 = dict(kw, partition_tokens=ptok)
-            d2 = B.make_dims(q, caches[0][0], tables, **kw2)
-            ws2 = B.alloc_workspace(d2, w.num_kv_heads, dev)
-            for i in range(3):
-                B.pa_decode(q, caches[i % R][0], caches[i % R][1], tables, seq_lens, w.num_kv_heads,
-                            float(w.scale), out, workspace=ws2, **kw2)
-            ev = hip.create(2)
-            torch.cuda.synchronize()
-            stream_ev0 = torch.cuda.Event(enable_timing=True)
-            stream_ev1 = torch.cuda.Event(enable_timing=True)
-            stream_ev0.record(stream)
-            for i in range(20):
-                B.pa_decode(q, caches[i % R][0], caches[i % R][1], tables, seq_lens, w.num_kv_heads,
-                            float(w.scale), out, workspace=ws2, **kw2)
-            stream_ev1.record(stream)
-            torch.cuda.synchronize()
-            ms = stream_ev0.elapsed_time(stream_ev1) / 20
-            print(f"sweep P={ptok}: {ms * 1e3:.1f} us/step {kv_bytes / ms / 1e6:.1f} GB/s", file=sys.stderr,
-                  flush=True)
-            hip.destroy(ev)
-            del ws2
+            r = time_decode(w, batch, args.q_len, dev, hip, 20, 3, dict(opts, partition_tokens=ptok), args.replicas)
+            print(f"sweep P={ptok}: {r['ms_step'] * 1e3:.1f} us/step {r['kv_bytes'] / r['ms_step'] / 1e6:.1f} GB/s",
+                  file=sys.stderr, flush=True)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # Two library-recorded events bracket the partition kernel of every
-    # EVENT_EVERY-th timed step (the first included): the matrix-core kernel's
-    # dispatch records them itself at the start and end of its execution (the
-    # plan kernel of the list schedule runs before). Each such pair still costs
-    # the stream about 5 us, which would otherwise land in every step. None is
-    # recorded after the merge kernel.
     K = args.steps
-    timed_steps = list(range(0, K, EVENT_EVERY))
-    evs = hip.create(2 * len(timed_steps))
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record(stream)
-    for i in range(K):
-        if i % EVENT_EVERY == 0:
-            j = i // EVENT_EVERY
-            step(i, events=(evs[2 * j], evs[2 * j + 1], None))
-        else:
-            step(i)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_end)
-    part_ms = [hip.elapsed_ms(evs[2 * j], evs[2 * j + 1]) for j in range(len(timed_steps))]
-    hip.destroy(evs)
-
-    ms_step = total_ms / K
-    gbs = kv_bytes / (ms_step * 1e-3) / 1e9
+    r = time_decode(w, batch, args.q_len, dev, hip, K, args.warmup, opts, args.replicas)
+    print(f"measured {batch}: {r['ms_step'] * 1e3:.2f} us/step", file=sys.stderr, flush=True)
+    plan, ms_step, part_ms, part_avg = r["plan"], r["ms_step"], r["part_ms"], r["part_avg"]
+    gbs = r["kv_bytes"] / (ms_step * 1e-3) / 1e9
     seq_heads = w.num_seqs * w.num_heads * args.q_len
-    part_avg = float(np.mean(part_ms))
-    achieved = kv_bytes / (part_avg * 1e-3) / 1e9
-    kname = "pa_mfma_partition" if plan["kernel"] == "mfma" else "pa_valu_partition"
-    traffic = load_traffic(kname, batch, plan)
-    # Attention flops of the launch: QK and PV, 2 * head_dim each per attended
-    # (token, query position, query head); query i of q_len attends L - q_len + 1 + i
-    # tokens. The path is matrix-bound once flops per K/V byte pass the chip's
-    # ratio of the two peaks (bf16 / f16 operands on the matrix cores).
-    L = w.seq_lens.astype(np.float64)[:, None]
-    attended = np.maximum(0.0, L - args.q_len + 1 + np.arange(args.q_len)[None, :]).sum()
-    flops = 4.0 * w.head_dim * w.num_heads * attended
-    op_dtype = "bf16" if w.kv_dtype == "bf16" else ("f32" if w.kv_dtype == "f32" else "f16")
-    if plan["kernel"] != "mfma":
-        op_dtype = "f32"
-    mfma_peak = MFMA_PEAK_TFLOPS[op_dtype]
-    if flops / kv_bytes > mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9):
-        roofline = {"bound": "mfma" if op_dtype != "f32" else "alu", "kernel": kname,
-                    "achieved": round(flops / (part_avg * 1e-3) / 1e12, 2), "peak": mfma_peak,
-                    "unit": "TFLOP/s", "frac": round(flops / (part_avg * 1e-3) / 1e12 / mfma_peak, 4),
-                    "traffic": traffic}
-    else:
-        roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
     result = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -338,27 +368,47 @@ def main():
         "vs_baseline": None,
         "dtype": w.kv_dtype,
         "data": "synthetic",
-        "config": {"workload": W.CONFIG_TITLES[args.config] + (f", {w.kv_dtype} KV" if args.kv_dtype else ""),
-                   "name": batch,
+        "config": {"workload": _title(batch, w), "name": batch,
                    "num_seqs": w.num_seqs, "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "block_size": w.block_size, "q_dtype": w.q_dtype,
                    "kv_dtype": w.kv_dtype, "total_tokens": int(w.seq_lens.sum()),
-                   "max_seq_len": w.max_seq_len, "kv_bytes_per_step": kv_bytes, "replicas": R,
+                   "max_seq_len": w.max_seq_len, "kv_bytes_per_step": r["kv_bytes"], "replicas": r["replicas"],
                    "kernel": plan["kernel"], "schedule": plan["schedule"], "partition_tokens": plan["partition_tokens"],
                    "partitions_max": plan["max_partitions"], "grid_workgroups": plan["grid_workgroups"],
                    "waves_per_item": plan["waves_per_item"], "q_len": args.q_len, "q_seed": q_seed,
                    "seed": list(w.seed), "parallelism": "single GPU"},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "seq_head_per_s": round(seq_heads / (ms_step * 1e-3), 1),
-        "wall_ms_per_step": round(wall * 1e3 / K, 5),
+        "wall_ms_per_step": round(r["wall_ms"], 5),
         "partition_kernel_us": round(part_avg * 1e3, 2),
         "partition_kernel_us_p10_p50_p90": [round(float(x) * 1e3, 2) for x in np.percentile(part_ms, [10, 50, 90])],
         "partition_kernel_timed_launches": len(part_ms),
         "rest_of_step_us": round((ms_step - part_avg) * 1e3, 2),
-        "roofline": roofline,
+        "roofline": r["roofline"],
     }
+    # The other decode batches, each at full size in its default plan, in the same run.
+    others = args.configs
+    if others == "auto":
+        default_run = args.config == "c3" and not args.kv_dtype and args.q_len == 1 and not any(
+            (args.kernel != "auto", args.partition_tokens, args.schedule != "auto", args.waves_per_item))
+        others = "c1,c2,c3,c4,c5" if default_run else ""
+    rows = {}
+    for name in [x for x in others.split(",") if x and x != "none"]:
+        if name == batch:
+            rows[name] = config_row(name, w, args.q_len, r)
+            continue
+        wo, bo, _ = decode_batch(name, "", 1)
+        ro = time_decode(wo, bo, 1, dev, hip, max(K, 20), args.warmup, dict(kernel="auto", partition_tokens=0,
+                                                                              schedule="auto", waves_per_item=0))
+        rows[name] = config_row(name, wo, 1, ro)
+        print(f"measured {name}: {ro['ms_step'] * 1e3:.2f} us/step", file=sys.stderr, flush=True)
+        del wo
+    if rows:
+        result["configs"] = rows
     if not args.no_read_probe:
-        result["read_ceiling"] = read_ceiling(stream, dev, achieved if roofline["unit"] == "GB/s" else None)
+        stream = torch.cuda.current_stream(dev)
+        result["read_ceiling"] = read_ceiling(stream, dev, r["achieved_gbs"] if r["roofline"]["unit"] == "GB/s"
+                                              else None)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, args.q_len)
     print(json.dumps(result), flush=True)

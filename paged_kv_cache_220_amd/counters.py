@@ -32,8 +32,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["pa_internal.h", "pa_device.h", "pa_api.hip", "pa_mfma.hip"]
+VALU_KERNEL_SOURCES = ["pa_internal.h", "pa_device.h", "pa_api.hip", "pa_valu.hip"]
 COPY_KERNEL = "copyBuffer"
-PARTITION_KERNEL = "mfma_partition"   # the grid or the work-list form
+PARTITION_KERNEL = "_partition"   # matrix-core (grid or work-list form) or vector partition kernel
 REDUCE_KERNEL = "reduce_"   # the merge kernel in either form
 
 
@@ -88,13 +89,14 @@ def build_entry(fetch, write, copy_bytes, algorithmic_bytes):
         raise SystemExit("no copy-probe dispatch of the stated size in the counter runs")
     kname, pf = _pick(fetch, PARTITION_KERNEL)
     _, pw = _pick(write, PARTITION_KERNEL)
+    sources = VALU_KERNEL_SOURCES if "valu_partition" in kname else KERNEL_SOURCES
     mean = lambda v: sum(v) / len(v)
     fetch_scale = copy_bytes / 1024.0 / mean(cf)
     write_scale = copy_bytes / 1024.0 / mean(cw)
     traffic = (mean(pf) * fetch_scale + mean(pw) * write_scale) * 1024.0
     e = {
-        "kernel_source_files": KERNEL_SOURCES,
-        "kernel_source_sha256": source_digest(KERNEL_SOURCES),
+        "kernel_source_files": sources,
+        "kernel_source_sha256": source_digest(sources),
         "kernel": kname,
         "fetch_kib_per_dispatch": round(mean(pf), 1),
         "write_kib_per_dispatch": round(mean(pw), 1),
@@ -122,6 +124,7 @@ def main(argv=None):
     ap.add_argument("--write", required=True, help="counter CSV (or its directory) of the WRITE_SIZE run")
     ap.add_argument("--workload", default="c3")
     ap.add_argument("--kv-dtype", default="")
+    ap.add_argument("--q-len", type=int, default=1)
     ap.add_argument("--partition-tokens", type=int, required=True)
     ap.add_argument("--copy-mib", type=int, required=True)
     args = ap.parse_args(argv)
@@ -135,7 +138,9 @@ def main(argv=None):
 
     entry = build_entry(read_counter(args.fetch, "FETCH_SIZE"), read_counter(args.write, "WRITE_SIZE"),
                         args.copy_mib << 20, alg)
-    key = f"pa_mfma_partition:{args.workload}{'-' + args.kv_dtype if args.kv_dtype else ''}:{args.partition_tokens}"
+    batch = args.workload + (f"-{args.kv_dtype}" if args.kv_dtype else "") + (f"-q{args.q_len}" if args.q_len > 1 else "")
+    prefix = "pa_valu_partition" if "valu_partition" in entry["kernel"] else "pa_mfma_partition"
+    key = f"{prefix}:{batch}:{args.partition_tokens}"
     try:
         with open(TRAFFIC_FILE) as fh:
             t = json.load(fh)
