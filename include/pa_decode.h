@@ -52,6 +52,10 @@
  * seq_lens[s] in the last block, are never read. Several sequences may map
  * to the same physical block (shared prefixes).
  *
+ * Scales: scale and k_scale must be positive and finite, and so must their
+ * product with log2(e) (the kernels work in the log2 domain); v_scale finite.
+ * Otherwise the call returns PA_ERR_SHAPE.
+ *
  * Numeric range. Every kernel accumulates in float32 and needs the scores
  * scale * k_scale * (block scale) * q . K to be finite in float32. The
  * matrix-core kernel's fp8 and int4 paths multiply binary16 operands; they
@@ -83,7 +87,7 @@ extern "C" {
 typedef enum pa_status {
   PA_OK = 0,
   PA_ERR_NULL = 1,        /* a required pointer is NULL                              */
-  PA_ERR_SHAPE = 2,       /* non-positive size, num_heads % num_kv_heads != 0, ...   */
+  PA_ERR_SHAPE = 2,       /* non-positive size or scale, num_heads % num_kv_heads,   */
   PA_ERR_UNSUPPORTED = 3, /* head_dim / block_size / group / dtype combination       */
   PA_ERR_ALIGN = 4,       /* a data pointer is not 16-byte aligned                   */
   PA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than pa_decode_workspace_bytes */

@@ -48,6 +48,7 @@ int check_dims(const pa_dims_t* d, int32_t hkv) {
   if ((long long)d->max_seq_len > (long long)d->max_blocks_per_seq * d->block_size) return PA_ERR_SHAPE;
   if (d->partition_tokens % pa::kTileTokens != 0) return PA_ERR_SHAPE;
   if (!isfinite(d->k_scale) || !isfinite(d->v_scale)) return PA_ERR_SHAPE;
+  if (!(d->k_scale > 0.f)) return PA_ERR_SHAPE;   // scores scale by a positive factor
   if (d->q_len < 0) return PA_ERR_SHAPE;
   // per-block scales: both or neither; required for int4, allowed for fp8
   const bool fp8 = d->kv_dtype == PA_DTYPE_FP8_E5M2 || d->kv_dtype == PA_DTYPE_FP8_E4M3;
@@ -192,18 +193,28 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
   return PA_OK;
 }
 
+// Every host-side check of a decode call (pointers, sizes, plan, scale,
+// alignment); the entry points run it before any HIP call.
+int validate(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+             const int32_t* seq_lens, int32_t hkv, float scale, void* out, const pa_dims_t* dims, Plan* p) {
+  if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !out) return PA_ERR_NULL;
+  const int st = make_plan(dims, hkv, p);
+  if (st != PA_OK) return st;
+  if (!isfinite(scale) || !(scale > 0.f) || !isfinite(scale * dims->k_scale * 1.4426950408889634f))
+    return PA_ERR_SHAPE;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(block_tables, 4) || !aligned(seq_lens, 4))
+    return PA_ERR_ALIGN;
+  return PA_OK;
+}
+
 int run(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
         const int32_t* seq_lens, int32_t hkv, float scale, void* out, const pa_dims_t* dims,
         void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1,
         hipEvent_t ev2) {
-  if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !out) return PA_ERR_NULL;
   Plan p;
-  const int st = make_plan(dims, hkv, &p);
+  const int st = validate(q, k_cache, v_cache, block_tables, seq_lens, hkv, scale, out, dims, &p);
   if (st != PA_OK) return st;
-  if (!isfinite(scale)) return PA_ERR_SHAPE;
-  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
-      !aligned(block_tables, 4) || !aligned(seq_lens, 4))
-    return PA_ERR_ALIGN;
   if (p.ws_bytes > 0 && (workspace == nullptr || workspace_bytes < p.ws_bytes || !aligned(workspace, kAlign)))
     return PA_ERR_WORKSPACE;
 
@@ -354,9 +365,8 @@ int pa_decode_ws_timed(const void* q, const void* k_cache, const void* v_cache,
 int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
               const int32_t* seq_lens, int32_t num_kv_heads, float scale, void* out,
               const pa_dims_t* dims, void* stream) {
-  if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !out) return PA_ERR_NULL;
   Plan p;
-  const int st = make_plan(dims, num_kv_heads, &p);
+  const int st = validate(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale, out, dims, &p);
   if (st != PA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   void* ws = nullptr;
@@ -370,9 +380,8 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
 int pa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
                       const int32_t* seq_lens, int32_t num_kv_heads, float scale, void* out,
                       const pa_dims_t* dims, void* stream) {
-  if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !out) return PA_ERR_NULL;
   Plan p;
-  const int st = make_plan(dims, num_kv_heads, &p);
+  const int st = validate(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale, out, dims, &p);
   if (st != PA_OK) return st;
   if (p.ws_bytes > (size_t)PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_WORKSPACE;   // before any HIP call
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -51,6 +51,8 @@
 
 #include <hip/hip_ext.h>
 
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -403,7 +405,9 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
         qmax = max(qmax, (uint32_t)__shfl_xor((int)qmax, 32, 64));
         shift = 15 - __builtin_amdgcn_frexp_expf(bf16_bits_to_f32(qmax));   // max in [2^(e-1), 2^e)
       }
-      qss[cg] = M::kRescaleQ ? __builtin_amdgcn_ldexpf(a.score_scale, -shift) : a.score_scale;
+      // (held at the smallest normal float: a row of nothing but bf16 subnormals
+      // would otherwise scale its scores by 0)
+      qss[cg] = M::kRescaleQ ? fmaxf(__builtin_amdgcn_ldexpf(a.score_scale, -shift), 1.17549435e-38f) : a.score_scale;
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) qop[cg][ks] = M::q_operand(qraw[cg][ks], shift);
       if constexpr (KDT == kI4) {
@@ -526,11 +530,15 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   // PV receives 2^(s' - m) * vm = 2^(s - m) * vsc, and the running sum adds
   // 2^(s' - m) * 2^-ve = 2^(s - m): the state (m, l, o) keeps its meaning with
   // m the reference of both sums, and o / l is unchanged.
-  auto softmax = [&](const int cg, const f32x4 (&sg)[4], const int t0, op_t (&phi)[2], op_t (&plo)[2],
-                     const float (&ksc)[2], const float (&vsc)[2])
+  auto softmax = [&](auto edge, const int cg, const f32x4 (&sg)[4], const int t0, op_t (&phi)[2],
+                     op_t (&plo)[2], const float (&ksc)[2], const float (&vsc)[2])
       __attribute__((always_inline)) {
     const int nval = min(tok1, lim[cg]) - t0;   // this column's tokens in the tile (may be <= 0)
-    float sc[4][4];                             // [r][j]; tokens outside the window: -inf
+    // Plain scores (no int4 offset, no per-block scales) are product * ka with
+    // ka > 0; the others are one fma each, kept in sc ([r][j], -inf outside
+    // the window).
+    constexpr bool kPlainScores = KDT != kI4 && !BSCALE;
+    float sc[4][4];
     float tmax = -INFINITY;
     float ka[2], kb[2];                         // score = product * ka + kb, per block of the lane
     float vm[2];                                // V scale's mantissa (1 without per-block scales)
@@ -552,29 +560,33 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
         kb[x] = (float)ve[x];
       }
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if constexpr (KDT == kI4) sc[r][j] = fmaf(sg[j][r], ka[r >> 1] * (1.f / Mfma<kI4>::kKScale[j]), kb[r >> 1]);
-        else if constexpr (BSCALE) sc[r][j] = fmaf(sg[j][r], ka[r >> 1], kb[r >> 1]);
-        else sc[r][j] = sg[j][r] * ka[r >> 1];
-      }
-    }
     // Only a tile that reaches past the partition end or a query's window
-    // has tokens to select out; the test is the same for the whole wave.
-    if (t0 + kTile > full_lim) {
+    // has tokens to select out (the caller's wave-uniform test, taken once
+    // per tile as a compile-time branch so full tiles carry no selects).
+    const bool select = decltype(edge)::value && t0 + kTile > full_lim;
+    auto valid = [&](int r, int j) __attribute__((always_inline)) {
+      return 16 * ((c >> 1) + 2 * (r >> 1)) + 8 * (c & 1) + 4 * (r & 1) + j < nval;
+    };
+    if constexpr (kPlainScores) {
+      // one positive factor for the whole column: the largest score is that
+      // factor times the largest product, bit for bit (rounding is monotonic)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int tt = 16 * ((c >> 1) + 2 * (r >> 1)) + 8 * (c & 1) + 4 * (r & 1);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sc[r][j] = (tt + j < nval) ? sc[r][j] : -INFINITY;
+        for (int j = 0; j < 4; ++j) tmax = fmaxf(tmax, (select && !valid(r, j)) ? -INFINITY : sg[j][r]);
       }
-    }
+      tmax *= ka[0];
+    } else {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < 4; ++r) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) tmax = fmaxf(tmax, sc[r][j]);
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (KDT == kI4) sc[r][j] = fmaf(sg[j][r], ka[r >> 1] * (1.f / Mfma<kI4>::kKScale[j]), kb[r >> 1]);
+          else sc[r][j] = fmaf(sg[j][r], ka[r >> 1], kb[r >> 1]);
+          if (select) sc[r][j] = valid(r, j) ? sc[r][j] : -INFINITY;
+          tmax = fmaxf(tmax, sc[r][j]);
+        }
+      }
     }
     tmax = fmaxf(tmax, shfl_xor_f32(tmax, 16));
     tmax = fmaxf(tmax, shfl_xor_f32(tmax, 32));
@@ -591,7 +603,18 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     for (int r = 0; r < 4; ++r) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        p[r][j] = __builtin_amdgcn_exp2f(sc[r][j] - m_use);
+        // Plain scores: the exponent is one fma of the product (the max above
+        // used the rounded product), written out so every tile and every
+        // kernel variant takes the same arithmetic. Scaled scores already
+        // are one fma each.
+        float arg;
+        if constexpr (kPlainScores) {
+          arg = fmaf(sg[j][r], ka[r >> 1], -m_use);
+          if (select) arg = valid(r, j) ? arg : -INFINITY;
+        } else {
+          arg = sc[r][j] - m_use;
+        }
+        p[r][j] = __builtin_amdgcn_exp2f(arg);
         psum[r >> 1] += p[r][j];
       }
     }
@@ -631,9 +654,9 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   };
   // V values of token slots at or past the partition end are zeroed: their
   // weights are 0, but 0 * NaN would poison the sum.
-  auto mask_tail = [&](Tile& T, const int t0) __attribute__((always_inline)) {
+  auto mask_tail = [&](auto edge, Tile& T, const int t0) __attribute__((always_inline)) {
     const int nvalid = tok1 - t0;   // tokens of this tile inside the partition (may exceed 64)
-    if (nvalid < kTile) {
+    if (decltype(edge)::value && nvalid < kTile) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int seg = 16 * ((c >> 1) + 2 * hh) + 8 * (c & 1);
@@ -647,17 +670,17 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   // then softmax and O^T += V P^T. With V operands used as loaded (bf16) each
   // column group's PV follows its softmax, so only one group's P is live;
   // widened fp8 V operands are instead shared by all groups' MFMAs.
-  auto tile_step = [&](Tile& T, const int t0, auto&& after_qk, const float (&ksc)[2], const float (&vsc)[2])
-      __attribute__((always_inline)) {
+  auto tile_step = [&](auto edge, Tile& T, const int t0, auto&& after_qk, const float (&ksc)[2],
+                       const float (&vsc)[2]) __attribute__((always_inline)) {
     f32x4 sacc[NCG][4];
     qk(T, sacc);
     after_qk();
-    mask_tail(T, t0);
+    mask_tail(edge, T, t0);
     if constexpr (M::kBits == 16) {
 #pragma unroll
       for (int cg = 0; cg < NCG; ++cg) {
         op_t phi[2], plo[2];
-        softmax(cg, sacc[cg], t0, phi, plo, ksc, vsc);
+        softmax(edge, cg, sacc[cg], t0, phi, plo, ksc, vsc);
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
 #pragma unroll
@@ -671,7 +694,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     } else {
       op_t phi[NCG][2], plo[NCG][2];
 #pragma unroll
-      for (int cg = 0; cg < NCG; ++cg) softmax(cg, sacc[cg], t0, phi[cg], plo[cg], ksc, vsc);
+      for (int cg = 0; cg < NCG; ++cg) softmax(edge, cg, sacc[cg], t0, phi[cg], plo[cg], ksc, vsc);
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
 #pragma unroll
@@ -692,8 +715,8 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   // they are used (K a k-step at a time, V one 8-token row segment at a time)
   // and the other wave on the SIMD covers the LDS latency. Per column the
   // arithmetic and its order are those of tile_step.
-  auto share_tile = [&](const uint8_t* st, const int t0, const float (&ksc)[2], const float (&vsc)[2])
-      __attribute__((always_inline)) {
+  auto share_tile = [&](auto edge, const uint8_t* st, const int t0, const float (&ksc)[2],
+                        const float (&vsc)[2]) __attribute__((always_inline)) {
     const uint8_t* krow = st + kblk * kSlotBlk + c * kRowBytes + ktok * M::kBits / 8;
     f32x4 sacc[NCG][4];
 #pragma unroll
@@ -711,7 +734,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     }
     op_t phi[NCG][2], plo[NCG][2];
 #pragma unroll
-    for (int cg = 0; cg < NCG; ++cg) softmax(cg, sacc[cg], t0, phi[cg], plo[cg], ksc, vsc);
+    for (int cg = 0; cg < NCG; ++cg) softmax(edge, cg, sacc[cg], t0, phi[cg], plo[cg], ksc, vsc);
     const int nvalid = tok1 - t0;   // tokens of this tile inside the partition (may exceed 64)
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -720,7 +743,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         vload_t x = *reinterpret_cast<const vload_t*>(vrow + 16 * dt * kRowBytes);
-        if (nvalid < kTile) x = M::mask_v(x, nv);   // 0 * NaN would poison the sum
+        if (decltype(edge)::value && nvalid < kTile) x = M::mask_v(x, nv);   // 0 * NaN would poison the sum
         const op_t vop = M::v_operand(x);
 #pragma unroll
         for (int cg = 0; cg < NCG; ++cg) {
@@ -802,7 +825,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     if (ntiles > 0) {   // the same for every wave of the item (an empty sequence has none)
 #pragma unroll
       for (int i = 0; i < STAGES - 1; ++i) issue(min(i, ntiles - 1));
-      for (int i = 0; i < ntiles; ++i) {
+      auto step = [&](auto edge, const int i) __attribute__((always_inline)) {
         const int t0 = tok0 + i * kTile;
         // own copies of tile i: everything but those of the later tiles in flight
         const int ahead = min(STAGES - 2, ntiles - 1 - i);
@@ -827,8 +850,8 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
           }
           const uint8_t* st = &kv_lds[i % STAGES][0];
           if constexpr (NCG <= 2) {
-            share_tile(st, t0, ksc, vsc);
-            continue;
+            share_tile(edge, st, t0, ksc, vsc);
+            return;
           }
           const uint8_t* krow = st + kblk * kSlotBlk + c * kRowBytes + ktok * M::kBits / 8;
           Tile T;
@@ -845,9 +868,16 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
               T.vr[dt][hh] = *reinterpret_cast<const vload_t*>(st + (4 + (c >> 1) + 2 * hh) * kSlotBlk +
                                                                (16 * dt + n) * kRowBytes + 8 * (c & 1) * M::kBits / 8);
           }
-          tile_step(T, t0, []() __attribute__((always_inline)) {}, ksc, vsc);
+          tile_step(edge, T, t0, []() __attribute__((always_inline)) {}, ksc, vsc);
         }
-      }
+      };
+      // Tiles wholly inside the partition and every query's window first (no
+      // selects), then the rest: two loops, so full tiles carry no selection
+      // and each loop keeps its own register allocation.
+      const int nfull = max(0, min(ntiles, (full_lim - tok0) / kTile));
+      int i = 0;
+      for (; i < nfull; ++i) step(std::false_type{}, i);
+      for (; i < ntiles; ++i) step(std::true_type{}, i);
     }
   } else if constexpr (kLdsK) {
     // Staged K. A K tile is 4 block tiles of 128 rows x 16 tokens; it lands in
@@ -889,7 +919,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
       load_k_lds(icur);
       load_v_ids(T, icur);
       __builtin_amdgcn_sched_barrier(0);
-      for (int t0 = first; t0 < tok1; t0 += kStride) {
+      auto step = [&](auto edge, const int t0) __attribute__((always_inline)) {
         const bool more = t0 + kStride < tok1;
         scales_at(inext, kb_next, vb_next);   // the next tile's, a tile ahead of use
         float ksc[2], vsc[2];
@@ -907,14 +937,15 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
           for (int i = 0; i < 8; ++i)
             T.kr[ks][i] = *reinterpret_cast<const kload_t*>(krow + (32 * ks + 4 * i) * kRowBytes);
         }
-        tile_step(T, t0, [&]() __attribute__((always_inline)) {
+        auto next_k = [&]() __attribute__((always_inline)) {
           __builtin_amdgcn_sched_barrier(0);
           if (more) {
             ids_at(t0 + 2 * kStride, icur);
             load_k_lds(inext);
           }
           __builtin_amdgcn_sched_barrier(0);
-        }, ksc, vsc);
+        };
+        tile_step(edge, T, t0, next_k, ksc, vsc);
         __builtin_amdgcn_sched_barrier(0);
         if (more) load_v_ids(T, inext);
         __builtin_amdgcn_sched_barrier(0);
@@ -924,7 +955,10 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
           kb_cur[blk] = kb_next[blk];
           vb_cur[blk] = vb_next[blk];
         }
-      }
+      };
+      int t0 = first;   // full tiles first, then the ones that need selection
+      for (; t0 < tok1 && t0 + kTile <= full_lim; t0 += kStride) step(std::false_type{}, t0);
+      for (; t0 < tok1; t0 += kStride) step(std::true_type{}, t0);
     }
   } else {
     // Plain loop: K and V straight into registers, one tile in flight per
@@ -947,13 +981,16 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
       issue(first);
       make_q();
       __builtin_amdgcn_sched_barrier(0);
-      for (int t0 = first; t0 < tok1; t0 += kStride) {
+      auto step = [&](auto edge, const int t0) __attribute__((always_inline)) {
         constexpr float kOnes[2] = {1.f, 1.f};
-        tile_step(T, t0, []() __attribute__((always_inline)) {}, kOnes, kOnes);
+        tile_step(edge, T, t0, []() __attribute__((always_inline)) {}, kOnes, kOnes);
         __builtin_amdgcn_sched_barrier(0);
         if (t0 + kStride < tok1) issue(t0 + kStride);
         __builtin_amdgcn_sched_barrier(0);
-      }
+      };
+      int t0 = first;   // full tiles first, then the ones that need selection
+      for (; t0 < tok1 && t0 + kTile <= full_lim; t0 += kStride) step(std::false_type{}, t0);
+      for (; t0 < tok1; t0 += kStride) step(std::true_type{}, t0);
     }
   }
 

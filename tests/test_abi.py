@@ -70,6 +70,8 @@ def status_of(d, hkv=8):
     (dict(partition_tokens=100), 8, B.PA_ERR_SHAPE),
     (dict(max_seq_len=2048 * 16 + 1), 8, B.PA_ERR_SHAPE),
     (dict(k_scale=float("inf")), 8, B.PA_ERR_SHAPE),
+    (dict(k_scale=0.0), 8, B.PA_ERR_SHAPE),                     # scores need a positive factor
+    (dict(k_scale=-1.0), 8, B.PA_ERR_SHAPE),
     (dict(block_size=32), 8, B.PA_ERR_UNSUPPORTED),
     (dict(head_dim=96), 8, B.PA_ERR_UNSUPPORTED),
     (dict(num_heads=24), 8, B.PA_OK),                          # group 3: matrix-core kernel
@@ -434,3 +436,13 @@ def test_noalloc_scratch_size_matches_the_header():
     text = open(os.path.join(ROOT, "include", "pa_decode.h")).read()
     m = re.search(r"#define PA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == B.NOALLOC_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, float("nan"), float("inf"), 3e38])
+def test_non_positive_or_overflowing_scale_rejected_before_any_hip_call(lib, scale):
+    """scale must be positive and scale * k_scale * log2(e) finite; the check
+    precedes the allocation of pa_decode and the scratch lookup of pa_decode_noalloc."""
+    fake = ctypes.c_void_p(1 << 20)
+    d = dims(k_scale=2.0)
+    for fn in (lib.pa_decode, lib.pa_decode_noalloc):
+        assert fn(*([fake] * 5 + [8, ctypes.c_float(scale), fake, ctypes.byref(d), None])) == B.PA_ERR_SHAPE
