@@ -350,6 +350,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
 
   // NW waves share the item: without tile sharing wave w takes tiles w, w + NW, ...
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  __builtin_assume(wave >= 0 && wave < NW);   // lets the copy assignment below fold
   // first virtual head of this wave's query block
   const int v0 = kShare ? 16 * NCG * (qb * NW + wave) : 16 * kMaxColumnGroups * qb;
   const int lane = threadIdx.x & 63;
@@ -812,7 +813,9 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
       for (int y = 0; y < kPer; ++y) {
         const int x = y * NW + wave;          // copy x: cache kv, block blk, KiB pc of the block tile
         const int kv = x / (4 * kCpb), blk = (x / kCpb) % 4, pc = x % kCpb;
-        const int32_t id = blk == 0 ? ib[0] : blk == 1 ? ib[1] : blk == 2 ? ib[2] : ib[3];
+        int32_t id = ib[0];   // wave-uniform selects (mostly folded), no branches
+#pragma unroll
+        for (int b = 1; b < 4; ++b) id = blk == b ? ib[b] : id;
         const char* src = (kv ? vbase : kbase) + id * blk_bytes + pc * 1024 + lane * 16;
         __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(st + (4 * kv + blk) * kSlotBlk + pc * 1024),
                                          16, 0, STREAM ? 2 : 0);   // 2: non-temporal
