@@ -327,8 +327,6 @@ def main():
         sys.exit(3)
     B.load_library()
     dev = torch.device("cuda:0")
-    if args.op != "decode":
-        return bench_cache_op(args, dev)
     if args.copy_probe:
         n = args.copy_probe << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)
@@ -338,6 +336,8 @@ def main():
         torch.cuda.synchronize()
         print(f"copy probe: {n} bytes read and written per dispatch", file=sys.stderr, flush=True)
         del src, dst
+    if args.op != "decode":
+        return bench_cache_op(args, dev)
     hip = HipEvents()
     opts = dict(kernel=args.kernel, partition_tokens=args.partition_tokens, schedule=args.schedule,
                 waves_per_item=args.waves_per_item)

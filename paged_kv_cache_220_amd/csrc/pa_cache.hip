@@ -164,6 +164,26 @@ __global__ __launch_bounds__(64) void append_kernel(const AppendArgs a) {
     whole = __builtin_amdgcn_ballot_w64(!ok) == 0;
   }
   if (whole && slot != 0) return;                   // written by the block's first entry
+  // Runs (not int4): entries that continue the previous entry's sequence at
+  // the next position of the same block are written by the wavefront of the
+  // run's first entry, which writes the run's tokens row after row; so each
+  // row's bytes of the run are stored back to back by one wavefront and reach
+  // the L2 together (otherwise the partial last block of every sequence in a
+  // bulk append is written two bytes per row by separate wavefronts, and L2
+  // writes some of its sectors back more than once). Other runs in the same
+  // block hold other slots: their bytes are disjoint.
+  int run = 1;                                      // entries of this entry's run from it on
+  if constexpr (KV != kI4) {
+    if (!whole) {
+      const bool pred = slot > 0 && __builtin_amdgcn_readlane(wseq, kHalo - 1) == s &&
+                        __builtin_amdgcn_readlane(wpos, kHalo - 1) == pos - 1;
+      if (pred) return;                             // written by the run's first entry
+      const int k = lane - kHalo;                   // this lane's entry is i + k
+      const bool next = k >= 1 && k < kBlockSize - slot && wseq == s && wpos == pos + k;
+      const uint64_t m = __builtin_amdgcn_ballot_w64(next) >> (kHalo + 1);   // bit j: entry i + 1 + j
+      run = 1 + __builtin_ctzll(~m);                // consecutive successors inside the block
+    }
+  }
   int32_t id = a.tables[(int64_t)s * a.max_blocks + pos / kBlockSize];
   id = min(max(id, 0), a.num_blocks - 1);
   // code of value / scale, the scale being k_scale times the block's own
@@ -183,6 +203,28 @@ __global__ __launch_bounds__(64) void append_kernel(const AppendArgs a) {
       }
       store_row<KV>(a.k_cache, tile + (int64_t)d * kBlockSize, ck);
       store_row<KV>(a.v_cache, tile + (int64_t)d * kBlockSize, cv);
+    }
+    return;
+  }
+  if (run > 1) {
+    // four tokens at a time (their loads in flight together), a row's stores back to back
+    for (int d = lane; d < a.head_dim; d += 64) {
+      for (int t0 = 0; t0 < run; t0 += 4) {
+        float kx[4], vx[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int tt = min(t0 + t, run - 1);   // past the run: reload its last token, not stored
+          kx[t] = load_in<IN>(a.k_new, src + tt * head_stride + d);
+          vx[t] = load_in<IN>(a.v_new, src + tt * head_stride + d);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if (t0 + t < run) {
+            store_kv<KV>(a.k_cache, tile + (int64_t)d * kBlockSize + slot + t0 + t, kx[t], ks);
+            store_kv<KV>(a.v_cache, tile + (int64_t)d * kBlockSize + slot + t0 + t, vx[t], vs);
+          }
+        }
+      }
     }
     return;
   }

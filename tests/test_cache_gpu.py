@@ -310,3 +310,56 @@ def test_append_bulk_byte_exact(in_dtype, kv_dtype, scale, D):
     torch.cuda.synchronize()
     assert _same(_from_dev(kd, kv_dtype), k_ref, kv_dtype)
     assert _same(_from_dev(vd, kv_dtype), v_ref, kv_dtype)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "e5m2", "f32", "int4"])
+def test_append_runs_in_any_list_order(kv_dtype):
+    """Entries written as runs (consecutive positions inside one block, the
+    run's first entry writing all of them) in lists that break runs every way:
+    a block's positions split over distant parts of the list, runs in reverse
+    order, two sequences interleaved, padding entries inside runs. Byte-exact
+    against the oracle, which takes the entries one by one."""
+    rng = np.random.default_rng([31, len(kv_dtype)])
+    S, Hkv, D = 4, 2, 128
+    lens = [5, 0, 30, 17]
+    new = [40, 37, 19, 15]
+    nblk = [(L + m + 15) // 16 for L, m in zip(lens, new)]
+    pool = sum(nblk) + 3
+    perm = rng.permutation(pool).astype(np.int32)
+    tables = np.zeros((S, max(nblk)), np.int32)
+    off = 0
+    for s_, nb in enumerate(nblk):
+        tables[s_, :nb] = perm[off:off + nb]
+        off += nb
+    w = W.random_edge_workload(77, S=S, H=2 * Hkv, Hkv=Hkv, D=D, seq_lens=lens, kv_dtype=kv_dtype, extra_pool=pool)
+    k_cache, v_cache = w.k_cache[:pool].copy(), w.v_cache[:pool].copy()
+    runs = [[(s_, p) for p in range(lens[s_], lens[s_] + new[s_])] for s_ in range(S)]
+    entries = []
+    a, b = runs[0], runs[1]
+    entries += a[:7] + [(3, -1)] + a[7:20]            # padding inside a run
+    entries += b[:10][::-1]                           # a run in reverse order
+    entries += [e for pair in zip(b[10:25], runs[2][:15]) for e in pair]   # two sequences interleaved
+    entries += a[20:] + runs[3][8:] + b[25:] + runs[2][15:]
+    entries += runs[3][:8][::2] + [(1, -3)] + runs[3][:8][1::2]            # one block's positions split
+    token_seq = np.array([e[0] for e in entries], np.int32)
+    token_pos = np.array([e[1] for e in entries], np.int32)
+    assert sorted(e for e in entries if e[1] >= 0) == sorted(e for r in runs for e in r)
+    n = len(entries)
+    kn = _special_rows((n, Hkv, D), "f32", kv_dtype, rng)
+    vn = _special_rows((n, Hkv, D), "f32", kv_dtype, rng)
+    ks = vs = None
+    if kv_dtype == "int4":
+        ks = np.exp2(rng.uniform(-3, -1, (pool, Hkv))).astype(np.float32)
+        vs = np.exp2(rng.uniform(-3, -1, (pool, Hkv))).astype(np.float32)
+    scale = 1.0 if kv_dtype in ("bf16", "f32") else 0.5
+    k_ref, v_ref = O.paged_append(kn, vn, k_cache, v_cache, tables, token_seq, token_pos, "f32", kv_dtype,
+                                  k_scale=scale, v_scale=scale, k_block_scales=ks, v_block_scales=vs)
+    kd, vd = _to_dev(k_cache, kv_dtype), _to_dev(v_cache, kv_dtype)
+    sc = lambda x: None if x is None else torch.from_numpy(x).cuda()
+    log(f"case append runs in any order {kv_dtype} n={n}")
+    B.pa_cache_append(_to_dev(kn, "f32"), _to_dev(vn, "f32"), kd, vd, torch.from_numpy(tables).cuda(),
+                      torch.from_numpy(token_seq).cuda(), torch.from_numpy(token_pos).cuda(),
+                      k_scale=scale, v_scale=scale, k_block_scales=sc(ks), v_block_scales=sc(vs))
+    torch.cuda.synchronize()
+    assert _same(_from_dev(kd, kv_dtype), k_ref, kv_dtype)
+    assert _same(_from_dev(vd, kv_dtype), v_ref, kv_dtype)
