@@ -452,7 +452,33 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   }
 
   const int first = tok0 + (kShare ? 0 : wave) * kTile;
-  constexpr int kStride = (kShare ? 1 : NW) * kTile;
+  // Tiles of the partition, and how many of them lie wholly inside the
+  // partition and inside every query's window (they need no selection; the
+  // others are the partition's last tiles). The full tiles are visited in an
+  // order rotated by a per-sequence offset: sequences that share prefix blocks
+  // (the same physical blocks at the same logical positions) then reach them
+  // at different times, so the tiles the caches serve and the tiles that come
+  // from HBM are mixed throughout the launch instead of every item reading the
+  // shared prefix first. All KV heads of a sequence keep one order (a block's
+  // KV heads lie side by side in memory), and the offset depends only on the
+  // sequence and partition, so every kernel variant and schedule visits the
+  // same order.
+  const int ntiles_all = (tok1 - tok0 + kTile - 1) / kTile;
+  const int nfull_all = max(0, min(ntiles_all, (full_lim - tok0) / kTile));
+  const uint32_t item_hash = ((uint32_t)(s * a.max_parts + part)) * 2654435761u;
+  // (four bf16 column groups split over two waves keep the plain order: the
+  // rotation's registers would spill there, and no other variant is held to
+  // their bits)
+  constexpr bool kRotate = !(kPlain && NCG == 4 && NW > 1);
+  const int rot = kRotate && nfull_all > 0 ? (int)((item_hash >> 16) % (uint32_t)nfull_all) : 0;
+  auto tstart = [&](const int k) __attribute__((always_inline)) {   // start token of tile k in visiting order
+    int j = k;
+    if (k < nfull_all) {
+      j = k + rot;
+      if (j >= nfull_all) j -= nfull_all;
+    }
+    return tok0 + j * kTile;
+  };
 
   // K slots in LDS (one per wave) for the kernels that stage K tiles there:
   // fp8 (whole-row copies instead of 4-byte pieces) and two column groups
@@ -807,7 +833,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     const bool active = v0 < GV;              // wave-uniform: this wave's query block exists
     auto issue = [&](int i) __attribute__((always_inline)) {
       int32_t ib[4];
-      ids_at(tok0 + i * kTile, ib);
+      ids_at(tstart(i), ib);
       uint8_t* st = &kv_lds[i % STAGES][0];
 #pragma unroll
       for (int y = 0; y < kPer; ++y) {
@@ -829,7 +855,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
 #pragma unroll
       for (int i = 0; i < STAGES - 1; ++i) issue(min(i, ntiles - 1));
       auto step = [&](auto edge, const int i) __attribute__((always_inline)) {
-        const int t0 = tok0 + i * kTile;
+        const int t0 = tstart(i);
         // own copies of tile i: everything but those of the later tiles in flight
         const int ahead = min(STAGES - 2, ntiles - 1 - i);
         if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * kPer));
@@ -877,9 +903,8 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
       // Tiles wholly inside the partition and every query's window first (no
       // selects), then the rest: two loops, so full tiles carry no selection
       // and each loop keeps its own register allocation.
-      const int nfull = max(0, min(ntiles, (full_lim - tok0) / kTile));
       int i = 0;
-      for (; i < nfull; ++i) step(std::false_type{}, i);
+      for (; i < nfull_all; ++i) step(std::false_type{}, i);
       for (; i < ntiles; ++i) step(std::true_type{}, i);
     }
   } else if constexpr (kLdsK) {
@@ -916,14 +941,15 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
       Tile T;
       int32_t icur[4], inext[4];
       float kb_cur[4], vb_cur[4], kb_next[4], vb_next[4];
-      ids_at(first, icur);
-      ids_at(first + kStride, inext);
+      ids_at(tstart(wave), icur);
+      ids_at(tstart(wave + NW), inext);
       scales_at(icur, kb_cur, vb_cur);
       load_k_lds(icur);
       load_v_ids(T, icur);
       __builtin_amdgcn_sched_barrier(0);
-      auto step = [&](auto edge, const int t0) __attribute__((always_inline)) {
-        const bool more = t0 + kStride < tok1;
+      auto step = [&](auto edge, const int k) __attribute__((always_inline)) {
+        const int t0 = tstart(k);
+        const bool more = k + NW < ntiles_all;
         scales_at(inext, kb_next, vb_next);   // the next tile's, a tile ahead of use
         float ksc[2], vsc[2];
         lane_scales(kb_cur, ksc);
@@ -943,7 +969,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
         auto next_k = [&]() __attribute__((always_inline)) {
           __builtin_amdgcn_sched_barrier(0);
           if (more) {
-            ids_at(t0 + 2 * kStride, icur);
+            ids_at(tstart(k + 2 * NW), icur);
             load_k_lds(inext);
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -959,9 +985,9 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
           vb_cur[blk] = vb_next[blk];
         }
       };
-      int t0 = first;   // full tiles first, then the ones that need selection
-      for (; t0 < tok1 && t0 + kTile <= full_lim; t0 += kStride) step(std::false_type{}, t0);
-      for (; t0 < tok1; t0 += kStride) step(std::true_type{}, t0);
+      int k = wave;   // full tiles first, then the ones that need selection
+      for (; k < nfull_all; k += NW) step(std::false_type{}, k);
+      for (; k < ntiles_all; k += NW) step(std::true_type{}, k);
     }
   } else {
     // Plain loop: K and V straight into registers, one tile in flight per
@@ -975,25 +1001,25 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     };
     int32_t ib[4] = {0, 0, 0, 0};
     Tile T;
-    auto issue = [&](int t) __attribute__((always_inline)) {
+    auto issue = [&](int k) __attribute__((always_inline)) {   // tile k (its ids in ib), then the ids of k + NW
       load_tile(T, pick(ib, kblk), pick(ib, c >> 1), pick(ib, (c >> 1) + 2));
-      if (t + kStride < tok1) ids_at(t + kStride, ib);
+      if (k + NW < ntiles_all) ids_at(tstart(k + NW), ib);
     };
     if (first < tok1) {   // a wave without tiles needs no q operands
-      ids_at(first, ib);
-      issue(first);
+      ids_at(tstart(wave), ib);
+      issue(wave);
       make_q();
       __builtin_amdgcn_sched_barrier(0);
-      auto step = [&](auto edge, const int t0) __attribute__((always_inline)) {
+      auto step = [&](auto edge, const int k) __attribute__((always_inline)) {
         constexpr float kOnes[2] = {1.f, 1.f};
-        tile_step(edge, T, t0, []() __attribute__((always_inline)) {}, kOnes, kOnes);
+        tile_step(edge, T, tstart(k), []() __attribute__((always_inline)) {}, kOnes, kOnes);
         __builtin_amdgcn_sched_barrier(0);
-        if (t0 + kStride < tok1) issue(t0 + kStride);
+        if (k + NW < ntiles_all) issue(k + NW);
         __builtin_amdgcn_sched_barrier(0);
       };
-      int t0 = first;   // full tiles first, then the ones that need selection
-      for (; t0 < tok1 && t0 + kTile <= full_lim; t0 += kStride) step(std::false_type{}, t0);
-      for (; t0 < tok1; t0 += kStride) step(std::true_type{}, t0);
+      int k = wave;   // full tiles first, then the ones that need selection
+      for (; k < nfull_all; k += NW) step(std::false_type{}, k);
+      for (; k < ntiles_all; k += NW) step(std::true_type{}, k);
     }
   }
 
