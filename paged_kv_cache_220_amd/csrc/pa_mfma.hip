@@ -77,6 +77,9 @@ constexpr int kD = 128;       // head_dim handled by this kernel
 constexpr int kWaitVmcnt0 = (0x7 << 4) | (0xF << 8);
 // The same operand waiting for vmcnt <= n (n < 64).
 constexpr int vmcnt_wait(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+// Word 3 of a raw buffer resource on gfx9-family chips (32-bit data format,
+// no swizzle, no index stride): offsets are plain bytes from the base.
+constexpr int kRawBufferWord3 = 0x00020000;
 constexpr int kTile = 64;     // tokens per tile
 constexpr int kKSteps = kD / 32;
 
@@ -495,6 +498,9 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     kload_t kr[kKSteps][8];
     vload_t vr[8][2];
   };
+  // Vector-memory instructions of one tile's V load (one per vr element).
+  constexpr int kVLoadInsts = 8 * 2;
+  static_assert(sizeof(Tile::vr) == kVLoadInsts * sizeof(vload_t), "one load per V register group");
   auto ld = [&](auto* ptr) __attribute__((always_inline)) {
     if constexpr (STREAM) return __builtin_nontemporal_load(ptr);
     else return *ptr;
@@ -919,19 +925,36 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     //
     // Pipeline: K of the next tile is issued right after this tile's QK (its
     // slot is free again) and V of the next tile right after PV (into the V
-    // registers PV has released). The four block ids of a tile are the same
-    // for the whole wave; they are fetched two tiles ahead.
+    // registers PV has released). The wait before reading a K tile from LDS
+    // leaves that tile's V loads (issued after its K copies) in flight, so V
+    // arrives under QK and the softmax. The four block ids of a tile are the
+    // same for the whole wave; they are fetched two tiles ahead.
+    //
+    // The copies are buffer loads with one resource per block tile (base =
+    // the tile, size = its bytes), not global ones: the compiler counts those
+    // in issue order with the V loads and waits for V before PV with the K
+    // copies of the next tile still in flight, while a global-to-LDS load in
+    // flight makes it wait for every outstanding load. It does not order LDS
+    // reads after these copies by itself, hence the explicit wait.
     uint8_t* kslot = &k_lds[wave][0];
     const uint8_t* krow = kslot + kblk * kSlotBlk + c * kRowBytes + ktok * M::kBits / 8;   // + row bytes * (32 ks + 4 i)
-    auto load_k_lds = [&](const int32_t (&ib)[4]) __attribute__((always_inline)) {
+    // With copy false the resources hold no bytes: the loads touch no memory
+    // (out of range) and only keep the loads per tile the same on every path,
+    // which lets the compiler count exactly in its waits for V.
+    auto load_k_lds = [&](const int32_t (&ib)[4], const bool copy) __attribute__((always_inline)) {
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk) {
-        const char* src = kbase + ib[blk] * blk_bytes + lane * 16;
+        // (ids and sizes are wave-uniform; readfirstlane keeps the resource in
+        // scalar registers)
+        const int32_t id = __builtin_amdgcn_readfirstlane(ib[blk]);
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<char*>(kbase + id * blk_bytes), 0, __builtin_amdgcn_readfirstlane(copy ? kTileBlk : 0),
+            kRawBufferWord3);
 #pragma unroll
         for (int part = 0; part < kTileBlk / 1024; ++part)
-          __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src + part * 1024),
-                                           (lds_ptr_t)(kslot + blk * kSlotBlk + part * 1024), 16, 0,
-                                           STREAM ? 2 : 0);   // 2: non-temporal
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(kslot + blk * kSlotBlk + part * 1024), 16,
+                                                   lane * 16 + part * 1024, 0, 0,
+                                                   STREAM ? 2 : 0);   // 2: non-temporal
       }
     };
     auto load_v_ids = [&](Tile& T, const int32_t (&ib)[4]) __attribute__((always_inline)) {
@@ -944,7 +967,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
       ids_at(tstart(wave), icur);
       ids_at(tstart(wave + NW), inext);
       scales_at(icur, kb_cur, vb_cur);
-      load_k_lds(icur);
+      load_k_lds(icur, true);
       load_v_ids(T, icur);
       __builtin_amdgcn_sched_barrier(0);
       auto step = [&](auto edge, const int k) __attribute__((always_inline)) {
@@ -954,11 +977,10 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
         float ksc[2], vsc[2];
         lane_scales(kb_cur, ksc);
         lane_scales(vb_cur, vsc);
-        // The K copy into LDS is a vector-memory operation: wait for every
-        // outstanding one (vmcnt 0) before reading the slot. The compiler's own
-        // wait insertion does not cover LDS written this way in every
-        // instantiation, so the wait is explicit.
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        // The K copies into LDS are vector-memory operations, and the only
+        // ones issued after them are this tile's V loads: waiting until at
+        // most those are outstanding completes the copies.
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait(kVLoadInsts));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks < kKSteps; ++ks) {
@@ -968,15 +990,18 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
         }
         auto next_k = [&]() __attribute__((always_inline)) {
           __builtin_amdgcn_sched_barrier(0);
-          if (more) {
-            ids_at(tstart(k + 2 * NW), icur);
-            load_k_lds(inext);
-          }
+          if (more) ids_at(tstart(k + 2 * NW), icur);
+          load_k_lds(inext, more);
           __builtin_amdgcn_sched_barrier(0);
         };
         tile_step(edge, T, t0, next_k, ksc, vsc);
         __builtin_amdgcn_sched_barrier(0);
-        if (more) load_v_ids(T, inext);
+        // After the last tile the loads read block 0 (in range, unused), so
+        // that every path through the loop issues the same loads.
+        int32_t vids[4];
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) vids[blk] = more ? inext[blk] : 0;
+        load_v_ids(T, vids);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) {
@@ -988,6 +1013,9 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
       int k = wave;   // full tiles first, then the ones that need selection
       for (; k < nfull_all; k += NW) step(std::false_type{}, k);
       for (; k < ntiles_all; k += NW) step(std::true_type{}, k);
+      // The last tile's empty copies target this wave's slot, which the
+      // epilogue may reuse: let them finish.
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     }
   } else {
     // Plain loop: K and V straight into registers, one tile in flight per
@@ -1127,10 +1155,12 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
 }
 
 // One column group fits two waves per SIMD (<= 256 registers per lane), so
-// one wave's compute overlaps the other's loads; more groups take one wave.
+// one wave's compute overlaps the other's loads, and three with an 8-bit or
+// 4-bit cache (<= 168 registers); more groups take one wave.
 #define PA_MFMA_KERNEL_ATTRS                                          \
   __global__ __launch_bounds__(64 * NW)                               \
-  __attribute__((amdgpu_waves_per_eu((NCG == 1 || (STAGES > 0 && NCG == 2)) ? 2 : 1, 8)))
+  __attribute__((amdgpu_waves_per_eu(                                 \
+      (NCG == 1 && KDT != kBF16) ? 3 : (NCG == 1 || (STAGES > 0 && NCG == 2)) ? 2 : 1, 8)))
 
 // Grid schedule: one workgroup per (KV head, sequence, partition) of the dense grid.
 template <int KDT, int NCG, int NW, bool STREAM, bool BSCALE, int STAGES>
