@@ -8,6 +8,13 @@
 // the online-softmax state (running max m, running sum l, rescaled o) of the
 // PagedAttention kernel pseudocode on the vLLM page in registers.
 //
+// For small groups (G x head_dim / 4 <= 32) blocks are fetched ahead: the
+// partition's physical block ids are read one per lane (64 at a time) and
+// handed out with readlane, and the K and V tiles of block j + kDepth - 1 are
+// issued, into a ring of raw registers, before block j is computed. A short
+// sequence then costs about one memory round trip per kDepth blocks instead
+// of three per block (id, then K, then V).
+//
 // Per 16-token block (tile [head_dim][16], tokens fastest):
 //   QK: lane = (token t = lane % 16, row group c = lane / 16); the lane reads
 //       rows d = 4i + c (one 128-byte line per wave instruction), multiplies
@@ -23,65 +30,76 @@
 // This kernel covers every supported shape and dtype; the matrix-core kernel
 // replaces it for the grouped bf16 / fp8 shapes.
 
+#include <utility>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
 namespace pa {
 namespace {
 
-template <int KDT> struct Row16;
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>): slot
+// numbers known at compile time, so the register ring is never indexed at run time.
+template <int N, typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
+}
 
-template <> struct Row16<kF32> {
-  static __device__ __forceinline__ void load(const float* row, float (&v)[16]) {
-    const float4* p = reinterpret_cast<const float4*>(row);
+// A V row of 16 tokens is sizeof(element) x 16 bytes: that many 16-byte
+// pieces, loaded raw and widened at use.
+template <int KDT> struct Row16 {
+  static constexpr int kPieces = (int)sizeof(typename Storage<KDT>::type);
+  typedef uint4 raw_t[kPieces];
+  static __device__ __forceinline__ void load(const void* row, raw_t& x) {
+    const uint4* p = static_cast<const uint4*>(row);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float4 x = p[i];
-      v[4 * i + 0] = x.x; v[4 * i + 1] = x.y; v[4 * i + 2] = x.z; v[4 * i + 3] = x.w;
-    }
+    for (int i = 0; i < kPieces; ++i) x[i] = p[i];
   }
+  static __device__ __forceinline__ void widen(const raw_t& x, float (&v)[16]);
 };
 
-template <> struct Row16<kBF16> {
-  static __device__ __forceinline__ void load(const uint16_t* row, float (&v)[16]) {
-    const uint4* p = reinterpret_cast<const uint4*>(row);
+template <> __device__ __forceinline__ void Row16<kF32>::widen(const raw_t& x, float (&v)[16]) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint4 x = p[i];
-      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[8 * i + 2 * j + 0] = __uint_as_float(w[j] << 16);
-        v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
-      }
-    }
+  for (int i = 0; i < 4; ++i) {
+    v[4 * i + 0] = __uint_as_float(x[i].x); v[4 * i + 1] = __uint_as_float(x[i].y);
+    v[4 * i + 2] = __uint_as_float(x[i].z); v[4 * i + 3] = __uint_as_float(x[i].w);
   }
-};
+}
 
-template <> struct Row16<kE5M2> {
-  static __device__ __forceinline__ void load(const uint8_t* row, float (&v)[16]) {
-    const uint4 x = *reinterpret_cast<const uint4*>(row);
-    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+template <> __device__ __forceinline__ void Row16<kBF16>::widen(const raw_t& x, float (&v)[16]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t w[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-#pragma unroll
-      for (int b = 0; b < 4; ++b) v[4 * j + b] = e5m2_to_f32(w[j] >> (8 * b));
+      v[8 * i + 2 * j + 0] = __uint_as_float(w[j] << 16);
+      v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
     }
   }
-};
+}
 
-template <> struct Row16<kE4M3> {
-  static __device__ __forceinline__ void load(const uint8_t* row, float (&v)[16]) {
-    const uint4 x = *reinterpret_cast<const uint4*>(row);
-    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+template <> __device__ __forceinline__ void Row16<kE5M2>::widen(const raw_t& x, float (&v)[16]) {
+  const uint32_t w[4] = {x[0].x, x[0].y, x[0].z, x[0].w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[j], false);   // bytes 0, 1
-      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[j], true);    // bytes 2, 3
-      v[4 * j + 0] = lo[0]; v[4 * j + 1] = lo[1]; v[4 * j + 2] = hi[0]; v[4 * j + 3] = hi[1];
-    }
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) v[4 * j + b] = e5m2_to_f32(w[j] >> (8 * b));
   }
-};
+}
+
+template <> __device__ __forceinline__ void Row16<kE4M3>::widen(const raw_t& x, float (&v)[16]) {
+  const uint32_t w[4] = {x[0].x, x[0].y, x[0].z, x[0].w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[j], false);   // bytes 0, 1
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[j], true);    // bytes 2, 3
+    v[4 * j + 0] = lo[0]; v[4 * j + 1] = lo[1]; v[4 * j + 2] = hi[0]; v[4 * j + 3] = hi[1];
+  }
+}
 
 template <int QDT, int KDT, int D, int G>
 __global__ __launch_bounds__(64) void valu_partition_kernel(const Args a) {
@@ -124,21 +142,66 @@ __global__ __launch_bounds__(64) void valu_partition_kernel(const Args a) {
   const KT* vc = static_cast<const KT*>(a.v) + (int64_t)kvh * D * BS;
   const int32_t* table = a.tables + (int64_t)s * a.max_blocks;
 
-  for (int blk = tok0 / BS; blk * BS < tok1; ++blk) {
-    const int64_t phys = clamp_block(a, table[blk]);
-    const KT* kb = kc + phys * a.block_stride;
-    const KT* vb = vc + phys * a.block_stride;
-    const int nvalid = min(BS, tok1 - blk * BS);
+  // Ring of raw K/V registers, kDepth blocks deep, for small groups (q of the
+  // lane's D/4 rows for all G heads then fits in registers as well: the QK
+  // loop is unrolled and reads the ring at fixed indices). Larger groups keep
+  // one block at a time, its id read at the step and K and V loaded inside
+  // it, as the ring would cost their occupancy.
+  typedef typename Row16<KDT>::raw_t vraw_t;
+  constexpr bool kRing = G * D / 4 <= 32;
+  constexpr int kSlotRegs = D / 4 + DPL * 4 * Row16<KDT>::kPieces;
+  constexpr int kDepth = !kRing ? 1 : (kSlotRegs <= 32 ? 4 : 2);
+  KT kraw[kRing ? kDepth : 1][kRing ? D / 4 : 1];
+  vraw_t vraw[kRing ? kDepth : 1][kRing ? DPL : 1];
+  int64_t phys_of[kDepth];
+
+  const int b0 = tok0 / BS;                        // tok0 is a multiple of the block size
+  const int nblk = (tok1 - tok0 + BS - 1) / BS;    // 0 for an empty sequence
+  int ids = 0;                                     // physical id of block (64-block chunk) + lane
+  auto issue = [&](const int j, const int slot) __attribute__((always_inline)) {
+    if constexpr (!kRing) {
+      phys_of[slot] = clamp_block(a, table[b0 + j]);   // wave-uniform: a scalar load
+      return;
+    }
+    if ((j & 63) == 0) {
+      const int jj = j + lane;
+      ids = jj < nblk ? (int)clamp_block(a, table[b0 + jj]) : 0;
+    }
+    phys_of[slot] = __builtin_amdgcn_readlane(ids, j & 63);
+    {
+      const KT* kb = kc + phys_of[slot] * a.block_stride;
+      const KT* vb = vc + phys_of[slot] * a.block_stride;
+#pragma unroll
+      for (int i = 0; i < D / 4; ++i) kraw[slot][i] = kb[(4 * i + c) * BS + t];
+#pragma unroll
+      for (int jr = 0; jr < DPL; ++jr) Row16<KDT>::load(vb + (lane + 64 * jr) * BS, vraw[slot][jr]);
+    }
+  };
+
+  auto compute = [&](const int j, const int slot) __attribute__((always_inline)) {
+    const int nvalid = min(BS, tok1 - (b0 + j) * BS);
+    const KT* kb = kc + phys_of[slot] * a.block_stride;
+    const KT* vb = vc + phys_of[slot] * a.block_stride;
 
     float acc[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) acc[h] = 0.f;
-#pragma unroll 8
-    for (int i = 0; i < D / 4; ++i) {
-      const int d = 4 * i + c;
-      const float kv = to_f32<KDT>(kb[d * BS + t]);
+    if constexpr (kRing) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) acc[h] = fmaf(q_s[d][h], kv, acc[h]);
+      for (int i = 0; i < D / 4; ++i) {
+        const int d = 4 * i + c;
+        const float kv = to_f32<KDT>(kraw[slot][i]);
+#pragma unroll
+        for (int h = 0; h < G; ++h) acc[h] = fmaf(q_s[d][h], kv, acc[h]);
+      }
+    } else {
+#pragma unroll 8
+      for (int i = 0; i < D / 4; ++i) {
+        const int d = 4 * i + c;
+        const float kv = to_f32<KDT>(kb[d * BS + t]);
+#pragma unroll
+        for (int h = 0; h < G; ++h) acc[h] = fmaf(q_s[d][h], kv, acc[h]);
+      }
     }
 
     const bool valid = t < nvalid;
@@ -165,10 +228,15 @@ __global__ __launch_bounds__(64) void valu_partition_kernel(const Args a) {
     __syncthreads();
 
 #pragma unroll
-    for (int j = 0; j < DPL; ++j) {
-      const int d = lane + 64 * j;
+    for (int jr = 0; jr < DPL; ++jr) {
       float vv[16];
-      Row16<KDT>::load(vb + d * BS, vv);
+      if constexpr (kRing) {
+        Row16<KDT>::widen(vraw[slot][jr], vv);
+      } else {
+        vraw_t x;
+        Row16<KDT>::load(vb + (lane + 64 * jr) * BS, x);
+        Row16<KDT>::widen(x, vv);
+      }
 #pragma unroll
       for (int tt = 0; tt < BS; ++tt) vv[tt] = tt < nvalid ? vv[tt] : 0.f;
 #pragma unroll
@@ -176,10 +244,31 @@ __global__ __launch_bounds__(64) void valu_partition_kernel(const Args a) {
         float pv = 0.f;
 #pragma unroll
         for (int tt = 0; tt < BS; ++tt) pv = fmaf(p_s[h][tt], vv[tt], pv);
-        o[h][j] = o[h][j] * alpha[h] + pv;
+        o[h][jr] = o[h][jr] * alpha[h] + pv;
       }
     }
     __syncthreads();
+  };
+
+  // Block j + kDepth - 1 goes into the slot block j - 1 has released.
+  static_for<kDepth - 1>([&](auto J) __attribute__((always_inline)) {
+    if (J() < nblk) issue(J(), J());
+  });
+  if constexpr (kRing) {
+    for (int jb = 0; jb < nblk; jb += kDepth) {
+      static_for<kDepth>([&](auto SL) __attribute__((always_inline)) {
+        const int j = jb + SL();
+        if (j < nblk) {
+          if (j + kDepth - 1 < nblk) issue(j + kDepth - 1, (SL() + kDepth - 1) % kDepth);
+          compute(j, SL());
+        }
+      });
+    }
+  } else {
+    for (int j = 0; j < nblk; ++j) {
+      issue(j, 0);
+      compute(j, 0);
+    }
   }
 
   if (nparts == 1) {
