@@ -367,6 +367,13 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   // tile in between, so that q's latency and the tile's overlap.
   constexpr bool kLdsK = !kShare && (M::kBits < 16 || NCG == 2);
   constexpr bool kPlain = !kShare && !kLdsK;
+  // P enters PV as hi + lo (about 16 significant bits per weight) with one
+  // column group, i.e. decode; with more groups (several query positions),
+  // where the matrix cores and the vector ALU bound the kernel, as hi alone
+  // (bf16: 8 bits, binary16: 11), which halves the PV products. The error of
+  // an output is then at most 2^-9 (2^-12) of sum_i p_i |v_i|, the attention
+  // over |V|.
+  constexpr bool kTwoPartP = NCG == 1;
   op_t qop[NCG][kKSteps];
   int lim[NCG];                // tokens the column's query may attend: t < lim
   float qsum[NCG];             // int4: sum_d q[d] of the column
@@ -673,6 +680,9 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
         for (int k = 0; k < 8; ++k) {
           const int i = Mfma<kI4>::kVTok[k];
           pv[k] = p[2 * hh + (i >> 2)][i & 3] * (Mfma<kI4>::kVHigh[k] ? vs16 : vm[hh]);
+          // with hi alone, PV receives binary16(pv): sum that (the operand
+          // conversion of an exact binary16 value then changes nothing)
+          if constexpr (!kTwoPartP) pv[k] = static_cast<float>(static_cast<_Float16>(pv[k]));
           asm("" : "+v"(pv[k]));
           if (Mfma<kI4>::kVHigh[k]) pv_hi += pv[k];
           else pv_lo += pv[k];
@@ -720,7 +730,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
           for (int hh = 0; hh < 2; ++hh) {
             const op_t vop = M::v_operand(T.vr[dt][hh]);
             oacc[cg][dt] = M::mma(vop, phi[hh], oacc[cg][dt]);
-            oacc[cg][dt] = M::mma(vop, plo[hh], oacc[cg][dt]);
+            if constexpr (kTwoPartP) oacc[cg][dt] = M::mma(vop, plo[hh], oacc[cg][dt]);
           }
         }
       }
@@ -736,7 +746,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
 #pragma unroll
           for (int cg = 0; cg < NCG; ++cg) {
             oacc[cg][dt] = M::mma(vop, phi[cg][hh], oacc[cg][dt]);
-            oacc[cg][dt] = M::mma(vop, plo[cg][hh], oacc[cg][dt]);
+            if constexpr (kTwoPartP) oacc[cg][dt] = M::mma(vop, plo[cg][hh], oacc[cg][dt]);
           }
         }
       }
@@ -781,7 +791,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
 #pragma unroll
         for (int cg = 0; cg < NCG; ++cg) {
           oacc[cg][dt] = M::mma(vop, phi[cg][hh], oacc[cg][dt]);
-          oacc[cg][dt] = M::mma(vop, plo[cg][hh], oacc[cg][dt]);
+          if constexpr (kTwoPartP) oacc[cg][dt] = M::mma(vop, plo[cg][hh], oacc[cg][dt]);
         }
       }
     }

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import check, log, upload
+from gpu_helpers import abs_attention_multi, check, log, upload
 from oracle import pa_oracle as O
 from paged_kv_cache_220_amd import binding as B
 from paged_kv_cache_220_amd import workloads as W
@@ -37,6 +37,7 @@ def test_multi_query_parity(name, kw, ql, ptok):
     q = W.to_storage(rng.standard_normal((w.num_seqs, ql, w.num_heads, w.head_dim), dtype=np.float32), "bf16")
     ref = O.paged_attention_multi(q, w.k_cache, w.v_cache, w.block_tables, w.seq_lens, w.num_kv_heads, w.scale,
                                   "bf16", w.kv_dtype)
+    a = abs_attention_multi(q, w)
     qd = _dev(q, "bf16")
     out = torch.empty_like(qd)
     log(f"case multi-query {name}{kw} q_len={ql} P={ptok}")
@@ -45,7 +46,7 @@ def test_multi_query_parity(name, kw, ql, ptok):
                 max_seq_len=w.max_seq_len)
     torch.cuda.synchronize()
     got = out.float().cpu().numpy().astype(np.float64)
-    check(got, ref, w, f"multi-query {name} q_len={ql} P={ptok}")
+    check(got, ref, w, f"multi-query {name} q_len={ql} P={ptok}", a=a)
 
 
 @pytest.mark.parametrize("ql", [2, 4])
@@ -55,6 +56,7 @@ def test_multi_query_two_waves_per_item(ql):
     q = W.to_storage(rng.standard_normal((w.num_seqs, ql, w.num_heads, w.head_dim), dtype=np.float32), "bf16")
     ref = O.paged_attention_multi(q, w.k_cache, w.v_cache, w.block_tables, w.seq_lens, w.num_kv_heads, w.scale,
                                   "bf16", w.kv_dtype)
+    a = abs_attention_multi(q, w)
     qd = _dev(q, "bf16")
     for ptok in (0, 256):
         out = torch.empty_like(qd)
@@ -64,7 +66,7 @@ def test_multi_query_two_waves_per_item(ql):
                     float(w.scale), out, partition_tokens=ptok, max_seq_len=w.max_seq_len, kernel="mfma",
                     waves_per_item=2)
         torch.cuda.synchronize()
-        check(out.float().cpu().numpy().astype(np.float64), ref, w, f"multi-query 2 waves q_len={ql} P={ptok}")
+        check(out.float().cpu().numpy().astype(np.float64), ref, w, f"multi-query 2 waves q_len={ql} P={ptok}", a=a)
 
 
 def test_query_window_longer_than_sequence():
@@ -74,6 +76,7 @@ def test_query_window_longer_than_sequence():
     rng = np.random.default_rng(8)
     q = W.to_storage(rng.standard_normal((4, ql, 16, 128), dtype=np.float32), "bf16")
     ref = O.paged_attention_multi(q, w.k_cache, w.v_cache, w.block_tables, w.seq_lens, 2, w.scale, "bf16", "bf16")
+    a = abs_attention_multi(q, w, num_kv_heads=2)
     for ptok in (0, 64):
         qd = _dev(q, "bf16")
         out = torch.full_like(qd, float("nan"))
@@ -83,7 +86,7 @@ def test_query_window_longer_than_sequence():
         torch.cuda.synchronize()
         got = out.float().cpu().numpy().astype(np.float64)
         assert np.all(got[0, :3] == 0) and np.all(got[1, :1] == 0) and np.all(got[3] == 0)
-        check(got, ref, w, f"short window P={ptok}")
+        check(got, ref, w, f"short window P={ptok}", a=a)
 
 
 def _multi_ref(w, q):
@@ -109,6 +112,7 @@ def test_query_blocks(name, kw, ql):
     rng = np.random.default_rng([ql, 91])
     q = W.to_storage(rng.standard_normal((w.num_seqs, ql, w.num_heads, w.head_dim), dtype=np.float32), "bf16")
     ref = _multi_ref(w, q)
+    a = abs_attention_multi(q, w)
     qd = _dev(q, "bf16")
     kd, vd = _dev(w.k_cache, w.kv_dtype), _dev(w.v_cache, w.kv_dtype)
     td, ld = torch.from_numpy(w.block_tables).cuda(), torch.from_numpy(w.seq_lens).cuda()
@@ -118,7 +122,8 @@ def test_query_blocks(name, kw, ql):
         B.pa_decode(qd, kd, vd, td, ld, w.num_kv_heads, float(w.scale), out, partition_tokens=ptok,
                     max_seq_len=w.max_seq_len, kernel="mfma", schedule=sched, waves_per_item=nw)
         torch.cuda.synchronize()
-        check(out.float().cpu().numpy().astype(np.float64), ref, w, f"query blocks {name} q_len={ql} P={ptok} {sched}")
+        check(out.float().cpu().numpy().astype(np.float64), ref, w, f"query blocks {name} q_len={ql} P={ptok} {sched}",
+              a=a)
 
 
 def test_query_blocks_one_kv_head():
@@ -128,6 +133,7 @@ def test_query_blocks_one_kv_head():
     rng = np.random.default_rng(62)
     q = W.to_storage(rng.standard_normal((3, ql, 64, 128), dtype=np.float32), "bf16")
     ref = _multi_ref(w, q)
+    a = abs_attention_multi(q, w)
     qd = _dev(q, "bf16")
     for ptok in (0, 128):
         out = torch.full_like(qd, float("nan"))
@@ -135,7 +141,7 @@ def test_query_blocks_one_kv_head():
                     torch.from_numpy(w.seq_lens).cuda(), 1, float(w.scale), out, partition_tokens=ptok,
                     max_seq_len=w.max_seq_len)
         torch.cuda.synchronize()
-        check(out.float().cpu().numpy().astype(np.float64), ref, w, f"one KV head, group 64, P={ptok}")
+        check(out.float().cpu().numpy().astype(np.float64), ref, w, f"one KV head, group 64, P={ptok}", a=a)
 
 
 def test_prefill_chunk():
@@ -145,6 +151,7 @@ def test_prefill_chunk():
     rng = np.random.default_rng(63)
     q = W.to_storage(rng.standard_normal((1, ql, w.num_heads, w.head_dim), dtype=np.float32), "bf16")
     ref = _multi_ref(w, q)
+    a = abs_attention_multi(q, w)
     qd = _dev(q, "bf16")
     out = torch.full_like(qd, float("nan"))
     log(f"case prefill chunk q_len={ql} L={int(w.seq_lens[0])}")
@@ -152,7 +159,7 @@ def test_prefill_chunk():
                 torch.from_numpy(w.seq_lens).cuda(), w.num_kv_heads, float(w.scale), out,
                 max_seq_len=int(w.seq_lens[0]))
     torch.cuda.synchronize()
-    check(out.float().cpu().numpy().astype(np.float64), ref, w, "prefill chunk")
+    check(out.float().cpu().numpy().astype(np.float64), ref, w, "prefill chunk", a=a)
 
 
 @pytest.mark.parametrize("ql", [2, 4, 8, 12])
@@ -165,6 +172,7 @@ def test_multi_query_int4(ql):
                                                   w.seq_lens[s:s + 1], w.num_kv_heads, w.scale, "bf16", "int4",
                                                   k_block_scales=w.k_block_scales, v_block_scales=w.v_block_scales)
                           for s in range(w.num_seqs)])
+    a = abs_attention_multi(q, w)
     qd = _dev(q, "bf16")
     sc = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
     kd = torch.from_numpy(np.ascontiguousarray(w.k_cache)).cuda()
@@ -176,7 +184,7 @@ def test_multi_query_int4(ql):
                     w.num_kv_heads, float(w.scale), out, partition_tokens=ptok, max_seq_len=w.max_seq_len,
                     k_block_scales=sc(w.k_block_scales), v_block_scales=sc(w.v_block_scales))
         torch.cuda.synchronize()
-        check(out.float().cpu().numpy().astype(np.float64), ref, w, f"multi-query int4 q_len={ql} P={ptok}")
+        check(out.float().cpu().numpy().astype(np.float64), ref, w, f"multi-query int4 q_len={ql} P={ptok}", a=a)
 
 
 SHARE = [
@@ -209,6 +217,7 @@ def test_tile_sharing(kv, scaled, ql):
                                                   k_block_scales=w.k_block_scales,
                                                   v_block_scales=w.v_block_scales)
                           for s in range(w.num_seqs)])
+    a = abs_attention_multi(q, w)
     dev = upload(w)
     qd = _dev(q, "bf16")
     outs = {}
@@ -222,7 +231,7 @@ def test_tile_sharing(kv, scaled, ql):
                     k_block_scales=dev["k_block_scales"], v_block_scales=dev["v_block_scales"])
         torch.cuda.synchronize()
         got = out.float().cpu().numpy().astype(np.float64)
-        check(got, ref, w, f"tile sharing {kv} q_len={ql} P={ptok} {sched} waves={nw}")
+        check(got, ref, w, f"tile sharing {kv} q_len={ql} P={ptok} {sched} waves={nw}", a=a)
         outs[(ptok, nw)] = out.view(torch.int16).cpu().numpy()
     for nw in (2, 4, 8):
         assert np.array_equal(outs[(128, nw)], outs[(128, 1)]), f"{nw} waves sharing tiles differ from one block per item"
@@ -242,6 +251,7 @@ def test_tile_sharing_poisoned(kv):
                                                   k_block_scales=w.k_block_scales,
                                                   v_block_scales=w.v_block_scales)
                           for s in range(w.num_seqs)])
+    a = abs_attention_multi(q, w)
     dev = upload(w)
     qd = _dev(q, "bf16")
     for ptok, nw in ((0, 0), (64, 2), (128, 4)):
@@ -251,7 +261,8 @@ def test_tile_sharing_poisoned(kv):
                     partition_tokens=ptok, max_seq_len=w.max_seq_len, kernel="mfma", waves_per_item=nw,
                     k_block_scales=dev["k_block_scales"], v_block_scales=dev["v_block_scales"])
         torch.cuda.synchronize()
-        check(out.float().cpu().numpy().astype(np.float64), ref, w, f"tile sharing poisoned {kv} P={ptok} waves={nw}")
+        check(out.float().cpu().numpy().astype(np.float64), ref, w, f"tile sharing poisoned {kv} P={ptok} waves={nw}",
+              a=a)
 
 
 SHARE_SHAPES = [
@@ -268,6 +279,7 @@ def test_tile_sharing_shapes(H, Hkv, ql, lens):
     rng = np.random.default_rng([ql, 81])
     q = W.to_storage(rng.standard_normal((w.num_seqs, ql, w.num_heads, w.head_dim), dtype=np.float32), "bf16")
     ref = _multi_ref(w, q)
+    a = abs_attention_multi(q, w)
     qd = _dev(q, "bf16")
     kd, vd = _dev(w.k_cache, "bf16"), _dev(w.v_cache, "bf16")
     td, ld = torch.from_numpy(w.block_tables).cuda(), torch.from_numpy(w.seq_lens).cuda()
@@ -278,6 +290,50 @@ def test_tile_sharing_shapes(H, Hkv, ql, lens):
                     max_seq_len=w.max_seq_len, kernel="mfma", waves_per_item=nw)
         torch.cuda.synchronize()
         got = out.float().cpu().numpy().astype(np.float64)
-        check(got, ref, w, f"tile sharing H={H} Hkv={Hkv} q_len={ql} P={ptok} waves={nw}")
+        check(got, ref, w, f"tile sharing H={H} Hkv={Hkv} q_len={ql} P={ptok} waves={nw}", a=a)
         if 0 in lens:
             assert np.all(got[lens.index(0)] == 0)
+
+
+HEAVY_LENS = [9000, 8200, 6000, 4101]
+
+
+@pytest.mark.parametrize("ql", [4, 16])
+def test_every_block_counted_once(ql):
+    """Long sequences where one block holds V = 32 and q is tiny (weights all but
+    uniform): the output then sits near 32 x 16 / n, and a kernel that skips the
+    block, or takes it twice, misses by about that much, far beyond the gate.
+    The heavy block is the first one, one in the middle of a partition, the
+    first of the second 4096-token partition, and the last, partly filled one;
+    4 positions run two column groups per wave, 16 share tiles between waves.
+    (Elsewhere the gate with several positions, 2^-8 of the attention over |V|,
+    is loose enough on sequences of several thousand tokens to let one
+    ordinary block go unnoticed.)"""
+    w = W.random_edge_workload(90 + ql, S=len(HEAVY_LENS), H=64, Hkv=8, D=128, seq_lens=HEAVY_LENS)
+    heavy = [0, 100, 256, (HEAVY_LENS[3] - 1) // 16]
+    for s, b in enumerate(heavy):
+        w.v_cache[int(w.block_tables[s, b])] = W.to_storage(np.full(w.v_cache.shape[1:], 32.0, np.float32), "bf16")
+    rng = np.random.default_rng([ql, 93])
+    qf = rng.standard_normal((w.num_seqs, ql, w.num_heads, w.head_dim), dtype=np.float32) * np.float32(2.0 ** -20)
+    q = W.to_storage(qf, "bf16")
+    ref = _multi_ref(w, q)
+    a = abs_attention_multi(q, w)
+    # tokens of each heavy block inside its sequence (the last one is partial)
+    ntok = [min(16, HEAVY_LENS[s] - 16 * b) for s, b in enumerate(heavy)]
+    assert ntok[3] == 5
+    # the last query of each sequence attends all of it: missing the heavy block
+    # there moves every element by about 32 x ntok / L, several times the gate
+    gate = 2.0 ** -7 * np.abs(ref) + 2.0 ** -8 * a + 1e-4
+    for s in range(w.num_seqs):
+        assert gate[s, -1].max() < 0.25 * 32.0 * ntok[s] / HEAVY_LENS[s], f"sequence {s}: gate too loose"
+    qd = _dev(q, "bf16")
+    kd, vd = _dev(w.k_cache, "bf16"), _dev(w.v_cache, "bf16")
+    td, ld = torch.from_numpy(w.block_tables).cuda(), torch.from_numpy(w.seq_lens).cuda()
+    for ptok, nw in ((0, 0), (4096, 0), (512, 2)):
+        out = torch.full_like(qd, float("nan"))
+        log(f"case heavy block q_len={ql} P={ptok} waves={nw}")
+        B.pa_decode(qd, kd, vd, td, ld, w.num_kv_heads, float(w.scale), out, partition_tokens=ptok,
+                    max_seq_len=w.max_seq_len, kernel="mfma", waves_per_item=nw)
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy().astype(np.float64)
+        check(got, ref, w, f"heavy block q_len={ql} P={ptok} waves={nw}", a=a)

@@ -15,7 +15,10 @@ scaled values the error scales with them, so each output row is held to
   |err| <= 2^-7 |ref| + 1e-4 * u   and   |err| <= 1e-2 * u,
 where u is the largest |scaled V value| among the tokens the row attends (the
 output is a convex combination of those rows). For N(0,1) data u is about
-4.5, so the second bar is the task's 5e-2.
+4.5, so the second bar is the task's 5e-2. With several query positions the
+kernels feed each weight to PV as one binary16 value (11 significant bits),
+which may move an output by up to 2^-12 u; those rows take 2^-10 u in place
+of 1e-4 u.
 """
 
 import numpy as np
@@ -51,7 +54,7 @@ def _row_units(w, q_len=1):
     return u if q_len > 1 else u[:, 0]
 
 
-def check_scaled(got, ref, u, label):
+def check_scaled(got, ref, u, label, u_coef=1e-4):
     assert got.shape == ref.shape
     assert not np.isnan(got).any(), f"{label}: NaN in output"
     assert np.isfinite(got).all(), f"{label}: non-finite output"
@@ -59,8 +62,8 @@ def check_scaled(got, ref, u, label):
     worst = float((err / np.maximum(u, 1e-300)).max())
     log(f"{label}: max|err|/u = {worst:.3e}")
     assert np.all(err <= 1e-2 * u), f"{label}: max|err|/u {worst} > 1e-2"
-    bad = err > 2.0 ** -7 * np.abs(ref) + 1e-4 * u
-    assert not bad.any(), f"{label}: {int(bad.sum())} elements beyond 2^-7|ref| + 1e-4 u"
+    bad = err > 2.0 ** -7 * np.abs(ref) + u_coef * u
+    assert not bad.any(), f"{label}: {int(bad.sum())} elements beyond 2^-7|ref| + {u_coef:.3g} u"
 
 
 def _with_scales(w, kind, rng):
@@ -136,4 +139,4 @@ def test_multi_query_operand_range(kv, ql, qpow, scales):
                     k_block_scales=dev["k_block_scales"], v_block_scales=dev["v_block_scales"])
         torch.cuda.synchronize()
         got = out.float().cpu().numpy().astype(np.float64)
-        check_scaled(got, ref, u, f"multi-query {kv} q_len={ql} q*2^{qpow} {scales} P={ptok}")
+        check_scaled(got, ref, u, f"multi-query {kv} q_len={ql} q*2^{qpow} {scales} P={ptok}", u_coef=2.0 ** -10)
