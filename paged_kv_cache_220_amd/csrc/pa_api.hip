@@ -90,16 +90,17 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
   }
   p->max_len = d->max_seq_len > 0 ? d->max_seq_len : d->max_blocks_per_seq * d->block_size;
   // Query blocks (up to 64 (query position, head) pairs each). With more than
-  // one, the matrix-core kernel by default gives an item 4 or 8 waves of 32
-  // pairs each, and the waves share every K/V tile; waves_per_item = 1 keeps
-  // one block of 64 per item.
+  // one, the matrix-core kernel by default gives an item 2, 4 or (past 4096
+  // tokens) 8 waves of 32 pairs each, and the waves share every K/V tile;
+  // waves_per_item = 1 keeps one block of 64 per item.
   const int gv = p->group * p->q_len;   // (query position, head) pairs per KV head
   const int ncg = gv <= 16 ? 1 : gv <= 32 ? 2 : 4;
   const int blocks64 = (gv + 16 * pa::kMaxColumnGroups - 1) / (16 * pa::kMaxColumnGroups);
   const bool mfma = p->kernel == PA_KERNEL_MFMA;
   int share_nw = 0;   // waves per item when they share tiles
   if (mfma && blocks64 > 1 && d->waves_per_item != 1) {
-    share_nw = d->waves_per_item > 0 ? d->waves_per_item : pa::mfma_share_default_waves(p->group, p->q_len);
+    share_nw = d->waves_per_item > 0 ? d->waves_per_item
+                                        : pa::mfma_share_default_waves(p->group, p->q_len, p->max_len);
     if (!pa::mfma_share_tiles(p->group, p->q_len, share_nw) || share_nw > pa::kShareMaxWaves)
       return PA_ERR_UNSUPPORTED;
   }

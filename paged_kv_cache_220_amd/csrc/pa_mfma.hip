@@ -1209,9 +1209,16 @@ int mfma_item_blocks(int group, int q_len, int nw) {
   return (gv + 16 * kMaxColumnGroups - 1) / (16 * kMaxColumnGroups);
 }
 
-int mfma_share_default_waves(int group, int q_len) {
+// Default waves per item when they share tiles: 2 for up to 64 pairs of a KV
+// head, else 4 (two workgroups of two LDS stages per CU), except past 4096
+// tokens, where 8 (one workgroup of four stages per CU: half the items, so
+// half the K/V re-reads) came out about 1 % ahead (32 positions over 32K
+// tokens; 64 positions even). On shorter sequences 8 waves measured 2-14 %
+// slower: a few tiles per item never fill the deeper pipeline.
+int mfma_share_default_waves(int group, int q_len, long long max_len) {
   const int blocks = (group * q_len + 16 * kShareGroups - 1) / (16 * kShareGroups);
-  return blocks <= 2 ? 2 : blocks <= 4 || kShareMaxWaves == 4 ? 4 : 8;
+  if (blocks <= 2) return 2;
+  return blocks > 4 && max_len > 4096 && kShareMaxWaves == 8 ? 8 : 4;
 }
 
 // Waves per item: 1 to 4 with one column group; 1 or 2 with two or four

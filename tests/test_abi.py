@@ -159,14 +159,19 @@ def test_plan_schedule_choice():
     assert pq["partition_tokens"] == 256                                 # 512 items x 4 waves: 2048
     pq1 = B.plan(dims(num_seqs=4, max_seq_len=4096, q_len=16, waves_per_item=1), 8)
     assert pq1["waves_per_item"] == 1 and pq1["grid_workgroups"] == 4 * 8 * 2 * pq1["max_partitions"]
-    # 64 heads, one KV head, 3 positions: 192 pairs -> 6 wave blocks, one 8-wave item
+    # 64 heads, one KV head, 3 positions: 192 pairs -> 6 wave blocks, two 4-wave items
     pm = B.plan(dims(num_seqs=2, max_seq_len=2048, q_len=3), 1)
-    assert pm["waves_per_item"] == 8 and pm["grid_workgroups"] == 2 * 1 * 1 * pm["max_partitions"]
+    assert pm["waves_per_item"] == 4 and pm["grid_workgroups"] == 2 * 1 * 2 * pm["max_partitions"]
+    pm8 = B.plan(dims(num_seqs=2, max_seq_len=2048, q_len=3, waves_per_item=8), 1)
+    assert pm8["waves_per_item"] == 8 and pm8["grid_workgroups"] == 2 * 1 * 1 * pm8["max_partitions"]
     pm2 = B.plan(dims(num_seqs=2, max_seq_len=2048, q_len=3, waves_per_item=2), 1)
     assert pm2["waves_per_item"] == 2 and pm2["grid_workgroups"] == 2 * 1 * 3 * pm2["max_partitions"]
-    # prefill chunk: 8 heads x 64 positions = 16 wave blocks -> 2 items of 8 waves per KV head
+    # 32 positions over long sequences (256 pairs, past 4096 tokens): one item of 8 waves
+    pl = B.plan(dims(num_seqs=16, max_seq_len=32768, q_len=32), 8)
+    assert pl["waves_per_item"] == 8 and pl["grid_workgroups"] == 16 * 8 * 1 * pl["max_partitions"]
+    # prefill chunk: 8 heads x 64 positions = 16 wave blocks -> 4 items of 4 waves per KV head
     pp = B.plan(dims(num_seqs=128, max_seq_len=512, max_blocks_per_seq=32, q_len=64), 8)
-    assert pp["waves_per_item"] == 8 and pp["grid_workgroups"] == 128 * 8 * 2 and pp["max_partitions"] == 1
+    assert pp["waves_per_item"] == 4 and pp["grid_workgroups"] == 128 * 8 * 4 and pp["max_partitions"] == 1
     p = B.plan(dims(num_seqs=256, max_seq_len=32657), 8)
     assert p["schedule"] == "queue" and p["partition_tokens"] == 4096 and p["waves_per_item"] == 4
     g = B.plan(dims(num_seqs=256, max_seq_len=32657, schedule=1), 8)
