@@ -374,6 +374,16 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   // an output is then at most 2^-9 (2^-12) of sum_i p_i |v_i|, the attention
   // over |V|.
   constexpr bool kTwoPartP = NCG == 1;
+  // bf16 tile sharing reads its K operands from LDS with gfx950's
+  // transposing read (ds_read_b64_tr_b16), which hands each lane one token's
+  // values of four rows, so no register transpose follows. The read fixes
+  // which tokens can share an instruction's rows: rows 4q..4q+3 are four
+  // consecutive tokens. The tokens of the QK results are then those of the
+  // other kernels with the roles of result register r and instruction j
+  // exchanged (score (r, j) of lane group c is token 16 ((c >> 1) + 2 (j >> 1))
+  // + 8 (c & 1) + 4 (j & 1) + r), which leaves the V operands as they are and
+  // only reorders P.
+  constexpr bool kTrK = kShare && KDT == kBF16 && !BSCALE;
   op_t qop[NCG][kKSteps];
   int lim[NCG];                // tokens the column's query may attend: t < lim
   float qsum[NCG];             // int4: sum_d q[d] of the column
@@ -605,6 +615,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     // per tile as a compile-time branch so full tiles carry no selects).
     const bool select = decltype(edge)::value && t0 + kTile > full_lim;
     auto valid = [&](int r, int j) __attribute__((always_inline)) {
+      if constexpr (kTrK) return 16 * ((c >> 1) + 2 * (j >> 1)) + 8 * (c & 1) + 4 * (j & 1) + r < nval;
       return 16 * ((c >> 1) + 2 * (r >> 1)) + 8 * (c & 1) + 4 * (r & 1) + j < nval;
     };
     if constexpr (kPlainScores) {
@@ -639,10 +650,13 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     m_run[cg] = m_new;
     float psum[2] = {0.f, 0.f};                 // per block of the lane
     float p[4][4];
+    // The sums take the tokens in one order in every kernel: with the
+    // exchanged roles of r and j (kTrK) the loops run over (j, r).
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int a = 0; a < 4; ++a) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int b = 0; b < 4; ++b) {
+        const int r = kTrK ? b : a, j = kTrK ? a : b;
         // Plain scores: the exponent is one fma of the product (the max above
         // used the rounded product), written out so every tile and every
         // kernel variant takes the same arithmetic. Scaled scores already
@@ -655,7 +669,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
           arg = sc[r][j] - m_use;
         }
         p[r][j] = __builtin_amdgcn_exp2f(arg);
-        psum[r >> 1] += p[r][j];
+        psum[a >> 1] += p[r][j];
       }
     }
     if constexpr (BSCALE)
@@ -687,6 +701,10 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
           if (Mfma<kI4>::kVHigh[k]) pv_hi += pv[k];
           else pv_lo += pv[k];
         }
+      } else if constexpr (kTrK) {
+        // slots 0-3 are rows r = 0..3 of instruction 2hh, 4-7 those of 2hh + 1
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pv[i] = p[i & 3][2 * hh + (i >> 2)] * vm[hh];
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) pv[i] = p[2 * hh + (i >> 2)][i & 3] * vm[hh];
@@ -760,19 +778,47 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   // arithmetic and its order are those of tile_step.
   auto share_tile = [&](auto edge, const uint8_t* st, const int t0, const float (&ksc)[2],
                         const float (&vsc)[2]) __attribute__((always_inline)) {
-    const uint8_t* krow = st + kblk * kSlotBlk + c * kRowBytes + ktok * M::kBits / 8;
     f32x4 sacc[NCG][4];
+    if constexpr (kTrK) {
+      // Operand of instruction j, k-step ks for lane (n, c): rows 32 ks + 4 i
+      // + c (i = 0..7, the order q's operand uses) of the token of row n. In
+      // the transposing read a lane gets slot (its lane % 4) of the 4-element
+      // pieces that lanes (its lane / 4) + 4 k (k = 0..3) of its 16-lane group
+      // load. So lane n loads row 32 ks + 4 (n / 4) + c (+ 16 for i = 4..7) at
+      // the 4 tokens of row group q = n % 4 (block (q >> 1) + 2 (j >> 1),
+      // from token 8 (q & 1) + 4 (j & 1)), and receives rows 32 ks + 4 k + c
+      // of its own row's token.
+      typedef short s16x4 __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) {
-      kload_t kr[8];
+      for (int ks = 0; ks < kKSteps; ++ks) {
 #pragma unroll
-      for (int r = 0; r < 8; ++r) kr[r] = *reinterpret_cast<const kload_t*>(krow + (32 * ks + 4 * r) * kRowBytes);
+        for (int j = 0; j < 4; ++j) {
+          const int q = n & 3;
+          const uint8_t* kp = st + ((q >> 1) + 2 * (j >> 1)) * kSlotBlk + (32 * ks + 4 * (n >> 2) + c) * kRowBytes +
+                              (8 * (q & 1) + 4 * (j & 1)) * 2;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)kp);
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(kp + 16 * kRowBytes));
+          const op_t kop = __builtin_bit_cast(op_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const op_t kop = M::k_operand(kr, j);
+          for (int cg = 0; cg < NCG; ++cg)
+            sacc[cg][j] = M::mma(kop, qop[cg][ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[cg][j]);
+        }
+      }
+    } else {
+      const uint8_t* krow = st + kblk * kSlotBlk + c * kRowBytes + ktok * M::kBits / 8;
 #pragma unroll
-        for (int cg = 0; cg < NCG; ++cg)
-          sacc[cg][j] = M::mma(kop, qop[cg][ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[cg][j]);
+      for (int ks = 0; ks < kKSteps; ++ks) {
+        kload_t kr[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) kr[r] = *reinterpret_cast<const kload_t*>(krow + (32 * ks + 4 * r) * kRowBytes);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const op_t kop = M::k_operand(kr, j);
+#pragma unroll
+          for (int cg = 0; cg < NCG; ++cg)
+            sacc[cg][j] = M::mma(kop, qop[cg][ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[cg][j]);
+        }
       }
     }
     op_t phi[NCG][2], plo[NCG][2];
