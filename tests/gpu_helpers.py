@@ -105,12 +105,17 @@ def check(got, ref, w, label="", a=None):
     catches kernels that drop blocks or mis-scale long sequences, whose
     outputs are small enough to slip under the absolute bar.
 
-    With several query positions the kernels feed each weight to PV as one
-    16-bit value (8 significant bits with a bf16 cache): pass `a`, the
-    attention over |V| (`abs_attention_multi`), and the gate becomes
-    2^-7 |ref| + 2^-8 a + 1e-4, twice the rounding bound 2^-9 a.
+    With several query positions, and in decode with an fp8 cache, the
+    kernels feed each weight to PV as one 16-bit value (8 significant bits
+    with a bf16 cache, 11 with fp8 and int4): pass `a`, the attention over |V|
+    (`abs_attention_multi`), and the gate becomes 2^-7 |ref| + k a + 1e-4 with
+    k = 2^-8 (bf16 cache) or 2^-10 (the others), twice and four times the
+    rounding bounds 2^-9 a and 2^-12 a. For fp8 decode outputs (one query row
+    per sequence) `a` is taken from w.q when not given.
     """
     assert got.shape == ref.shape
+    if a is None and w.kv_dtype in ("e5m2", "e4m3") and got.ndim == 3 and w.q.shape == got.shape:
+        a = abs_attention_multi(w.q[:, None], w, q_dtype=w.q_dtype)[:, 0]
     assert not np.isnan(got).any(), f"{label}: NaN in output"
     err = np.abs(got - ref)
     tol = ABS_TOL[w.kv_dtype]
@@ -122,6 +127,6 @@ def check(got, ref, w, label="", a=None):
         gate = 2.0 ** -7 * np.abs(ref) + 1e-4
         if a is not None:
             assert a.shape == ref.shape
-            gate = gate + 2.0 ** -8 * a
+            gate = gate + (2.0 ** -8 if w.kv_dtype == "bf16" else 2.0 ** -10) * a
         bad = err > gate
         assert not bad.any(), f"{label}: {int(bad.sum())} elements beyond the relative gate (worst {worst})"
