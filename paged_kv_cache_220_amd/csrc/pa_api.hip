@@ -109,10 +109,11 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
   // HBM latency at full bandwidth takes about as many waves as the chip holds
   // at once: 2048 with bf16 / fp32 tiles (32 KiB, two waves per SIMD) and 3072
   // with fp8 and int4 tiles (16 / 8 KiB; those kernels stage K in LDS and run
-  // three waves per SIMD, fp8 with per-block scales two). Partitions are made as long as
-  // possible (up to 4096 tokens: start-up and merge traffic are amortised) and
-  // the waves come from splitting each item over 1 to 4 waves; partitions
-  // are shortened only when even 4 waves per item would not reach the target.
+  // three waves per SIMD, fp8 with per-block scales two). Partitions are
+  // made as long as possible (up to 4096 tokens, 8192 with tile sharing:
+  // start-up and merge traffic are amortised) and the waves come from
+  // splitting each item over 1 to 4 waves; partitions are shortened only when
+  // even 4 waves per item would not reach the target.
   const long long units = (long long)d->num_seqs * hkv * (p->kernel == PA_KERNEL_MFMA ? p->q_blocks : 1);
   // three waves per SIMD: fp8 without per-block scales and int4 (with them).
   // The tile-sharing kernels run two waves per SIMD (2048 on the chip).
@@ -123,7 +124,11 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
   auto items_for = [&](long long P) { return units * ((p->max_len + P - 1) / P); };
   int P = d->partition_tokens;
   if (P == 0) {
-    long long cap = 4096;
+    // Tile-sharing items run up to 8192 tokens: with every item resident at
+    // once, half the partitions halve the merge traffic of their (larger)
+    // states and the per-item start-up (measured 3-4 % per call at 16 to 64
+    // positions over 32K tokens); decode stays at 4096.
+    long long cap = share_nw > 0 ? 8192 : 4096;
     while (cap / 2 >= p->max_len && cap > pa::kTileTokens) cap /= 2;   // no longer than the longest sequence needs
     P = (int)cap;
     while (P > 256 && items_for(P) * max_item_waves < target_waves) P /= 2;
