@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace pa {
 
 // Storage-type tags (match pa_dtype_t).
@@ -42,6 +44,17 @@ template <> __device__ __forceinline__ void store_out<kF32>(void* out, int64_t i
 }
 template <> __device__ __forceinline__ void store_out<kBF16>(void* out, int64_t idx, float x) {
   static_cast<uint16_t*>(out)[idx] = f32_to_bf16_bits(x);
+}
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>): indices
+// known at compile time (register rings and LDS stages never indexed at run time).
+template <int N, typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
 }
 
 __device__ __forceinline__ float shfl_xor_f32(float x, int mask) {

@@ -510,7 +510,20 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   constexpr int kSlotBlk = kTileBlk + 64;
   __shared__ __attribute__((aligned(16))) uint8_t k_lds[kLdsK ? NW : 1][kLdsK ? 4 * kSlotBlk : 16];
   // Tile sharing: stage x holds the K tile (4 block slots) then the V tile.
-  __shared__ __attribute__((aligned(16))) uint8_t kv_lds[kShare ? STAGES : 1][kShare ? 8 * kSlotBlk : 16];
+  // One array per stage: distinct objects, which the compiler knows apart
+  // (below).
+  constexpr int kStageBytes = kShare ? 8 * kSlotBlk : 16;
+  __shared__ __attribute__((aligned(16))) uint8_t kv_lds0[kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t kv_lds1[STAGES > 1 ? kStageBytes : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t kv_lds2[STAGES > 2 ? kStageBytes : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t kv_lds3[STAGES > 3 ? kStageBytes : 16];
+  auto stage = [&](auto S) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int x = decltype(S)::value;
+    if constexpr (x == 0) return kv_lds0;
+    else if constexpr (x == 1) return kv_lds1;
+    else if constexpr (x == 2) return kv_lds2;
+    else return kv_lds3;
+  };
   // One tile's K and V registers.
   struct Tile {
     kload_t kr[kKSteps][8];
@@ -772,6 +785,17 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     }
   };
 
+  // Stage reads address the stage as its array plus this lane's offset plus a
+  // constant. The empty asm keeps the lane's offset one value, so that the
+  // compiler does not spread its terms over a chain of address steps: the
+  // stage reads are then traced to their stage array (the trace has a depth
+  // limit), and the compiler holds a read only for the copies into that
+  // stage.
+  auto lane_offset = [](int x) __attribute__((always_inline)) {
+    asm("" : "+v"(x));
+    return x;
+  };
+
   // One tile of the tile-sharing kernels with at most two column groups per
   // wave (two waves per SIMD): operands are read from the LDS stage `st` as
   // they are used (K a k-step at a time, V one 8-token row segment at a time)
@@ -791,15 +815,15 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
       // of its own row's token.
       typedef short s16x4 __attribute__((ext_vector_type(4)));
       typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
+      const int q = n & 3;
+      const int klane = lane_offset((q >> 1) * kSlotBlk + (4 * (n >> 2) + c) * kRowBytes + 8 * (q & 1) * 2);
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int q = n & 3;
-          const uint8_t* kp = st + ((q >> 1) + 2 * (j >> 1)) * kSlotBlk + (32 * ks + 4 * (n >> 2) + c) * kRowBytes +
-                              (8 * (q & 1) + 4 * (j & 1)) * 2;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)kp);
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(kp + 16 * kRowBytes));
+          const int kc = 2 * (j >> 1) * kSlotBlk + 32 * ks * kRowBytes + 4 * (j & 1) * 2;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(st + (klane + kc)));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(st + (klane + (kc + 16 * kRowBytes))));
           const op_t kop = __builtin_bit_cast(op_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
           for (int cg = 0; cg < NCG; ++cg)
@@ -807,12 +831,13 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
         }
       }
     } else {
-      const uint8_t* krow = st + kblk * kSlotBlk + c * kRowBytes + ktok * M::kBits / 8;
+      const int klane = lane_offset(kblk * kSlotBlk + c * kRowBytes + ktok * M::kBits / 8);
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) {
         kload_t kr[8];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) kr[r] = *reinterpret_cast<const kload_t*>(krow + (32 * ks + 4 * r) * kRowBytes);
+        for (int r = 0; r < 8; ++r)
+          kr[r] = *reinterpret_cast<const kload_t*>(st + (klane + (32 * ks + 4 * r) * kRowBytes));
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const op_t kop = M::k_operand(kr, j);
@@ -826,13 +851,14 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
 #pragma unroll
     for (int cg = 0; cg < NCG; ++cg) softmax(edge, cg, sacc[cg], t0, phi[cg], plo[cg], ksc, vsc);
     const int nvalid = tok1 - t0;   // tokens of this tile inside the partition (may exceed 64)
+    const int vlane = lane_offset((c >> 1) * kSlotBlk + n * kRowBytes + 8 * (c & 1) * M::kBits / 8);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      const uint8_t* vrow = st + (4 + (c >> 1) + 2 * hh) * kSlotBlk + n * kRowBytes + 8 * (c & 1) * M::kBits / 8;
       const int nv = min(8, max(0, nvalid - (16 * ((c >> 1) + 2 * hh) + 8 * (c & 1))));
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        vload_t x = *reinterpret_cast<const vload_t*>(vrow + 16 * dt * kRowBytes);
+        const int vc = (4 + 2 * hh) * kSlotBlk + 16 * dt * kRowBytes;
+        vload_t x = *reinterpret_cast<const vload_t*>(st + (vlane + vc));
         if (decltype(edge)::value && nvalid < kTile) x = M::mask_v(x, nv);   // 0 * NaN would poison the sum
         const op_t vop = M::v_operand(x);
 #pragma unroll
@@ -880,13 +906,20 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
 
   if constexpr (kShare) {
     // Tile sharing. A tile's K and V (4 block tiles each) land in one LDS
-    // stage through direct global-to-LDS copies of 1 KiB (16 bytes per lane),
-    // dealt round robin to the NW waves, STAGES - 1 tiles ahead of use. Before
-    // tile i each wave waits for its own copies of it; the workgroup barrier
-    // that follows covers the other waves' copies, and also tells that every
-    // wave is done with the stage of tile i - 1, which then takes tile
+    // stage through buffer-to-LDS copies of 1 KiB (16 bytes per lane), dealt
+    // round robin to the NW waves, STAGES - 1 tiles ahead of use. Before tile
+    // i each wave waits for its own copies of it; the workgroup barrier that
+    // follows covers the other waves' copies, and also tells that every wave
+    // is done with the stage of tile i - 1, which then takes tile
     // i + STAGES - 1. Each wave reads its K pieces and V rows from the stage
     // and runs the tile for its own query block.
+    //
+    // Tile i uses stage i % STAGES, and the loop holds one copy of the tile
+    // step per stage, so every copy and every LDS read names its stage at
+    // compile time. The compiler then tells the stage being read from the one
+    // being filled and lets the next tile's copies run under this tile's
+    // compute; with a stage index known only at run time it holds each tile's
+    // first LDS read until every copy in flight has landed.
     constexpr int kCpb = kTileBlk / 1024;     // copies per block tile
     constexpr int kCopies = 8 * kCpb;         // K and V of 4 blocks
     constexpr int kPer = kCopies / NW;        // copies per wave per tile
@@ -894,10 +927,10 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     static_assert(STAGES >= 2 && STAGES <= 4, "two to four stages");
     const int ntiles = (tok1 - tok0 + kTile - 1) / kTile;
     const bool active = v0 < GV;              // wave-uniform: this wave's query block exists
-    auto issue = [&](int i) __attribute__((always_inline)) {
+    auto issue = [&](auto S, int i) __attribute__((always_inline)) {   // tile i into stage S
       int32_t ib[4];
       ids_at(tstart(i), ib);
-      uint8_t* st = &kv_lds[i % STAGES][0];
+      uint8_t* st = stage(S);
 #pragma unroll
       for (int y = 0; y < kPer; ++y) {
         const int x = y * NW + wave;          // copy x: cache kv, block blk, KiB pc of the block tile
@@ -905,19 +938,22 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
         int32_t id = ib[0];   // wave-uniform selects (mostly folded), no branches
 #pragma unroll
         for (int b = 1; b < 4; ++b) id = blk == b ? ib[b] : id;
-        const char* src = (kv ? vbase : kbase) + id * blk_bytes + pc * 1024 + lane * 16;
-        __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(st + (4 * kv + blk) * kSlotBlk + pc * 1024),
-                                         16, 0, STREAM ? 2 : 0);   // 2: non-temporal
+        id = __builtin_amdgcn_readfirstlane(id);
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<char*>((kv ? vbase : kbase) + id * blk_bytes), 0, kTileBlk, kRawBufferWord3);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(st + (4 * kv + blk) * kSlotBlk + pc * 1024), 16,
+                                                 lane * 16 + pc * 1024, 0, 0, STREAM ? 2 : 0);   // 2: non-temporal
       }
     };
     // Prologue: tiles 0 .. STAGES - 2. A partition with fewer tiles copies its
-    // last tile again (into the same stage, with the same bytes), so that the
-    // number of copies after the q loads is fixed; the loop's waits then count
-    // the extra copies as later ones and stay on the safe side.
+    // last tile again (into a stage no tile uses), so that the number of
+    // copies after the q loads is fixed; the loop's waits then count the
+    // extra copies as later ones and stay on the safe side.
     if (ntiles > 0) {   // the same for every wave of the item (an empty sequence has none)
-#pragma unroll
-      for (int i = 0; i < STAGES - 1; ++i) issue(min(i, ntiles - 1));
-      auto step = [&](auto edge, const int i) __attribute__((always_inline)) {
+      static_for<STAGES - 1>([&](auto S) __attribute__((always_inline)) { issue(S, min(S(), ntiles - 1)); });
+      // tile i, which sits in stage S = i % STAGES
+      auto step = [&](auto edge, auto S, const int i) __attribute__((always_inline)) {
+        constexpr int kS = decltype(S)::value;
         const int t0 = tstart(i);
         // own copies of tile i: everything but those of the later tiles in flight
         const int ahead = min(STAGES - 2, ntiles - 1 - i);
@@ -927,7 +963,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        if (i + STAGES - 1 < ntiles) issue(i + STAGES - 1);
+        if (i + STAGES - 1 < ntiles) issue(std::integral_constant<int, (kS + STAGES - 1) % STAGES>{}, i + STAGES - 1);
         __builtin_amdgcn_sched_barrier(0);
         if (active) {
           float kb[4], vb[4], ksc[2], vsc[2];
@@ -940,35 +976,59 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
           } else {
             ksc[0] = ksc[1] = vsc[0] = vsc[1] = 1.f;
           }
-          const uint8_t* st = &kv_lds[i % STAGES][0];
+          const uint8_t* st = stage(S);
           if constexpr (NCG <= 2) {
             share_tile(edge, st, t0, ksc, vsc);
             return;
           }
-          const uint8_t* krow = st + kblk * kSlotBlk + c * kRowBytes + ktok * M::kBits / 8;
+          const int klane = lane_offset(kblk * kSlotBlk + c * kRowBytes + ktok * M::kBits / 8);
+          const int vlane = lane_offset((c >> 1) * kSlotBlk + n * kRowBytes + 8 * (c & 1) * M::kBits / 8);
           Tile T;
 #pragma unroll
           for (int ks = 0; ks < kKSteps; ++ks) {
 #pragma unroll
             for (int r = 0; r < 8; ++r)
-              T.kr[ks][r] = *reinterpret_cast<const kload_t*>(krow + (32 * ks + 4 * r) * kRowBytes);
+              T.kr[ks][r] = *reinterpret_cast<const kload_t*>(st + (klane + (32 * ks + 4 * r) * kRowBytes));
           }
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt)
-              T.vr[dt][hh] = *reinterpret_cast<const vload_t*>(st + (4 + (c >> 1) + 2 * hh) * kSlotBlk +
-                                                               (16 * dt + n) * kRowBytes + 8 * (c & 1) * M::kBits / 8);
+              T.vr[dt][hh] = *reinterpret_cast<const vload_t*>(st + (vlane + ((4 + 2 * hh) * kSlotBlk + 16 * dt * kRowBytes)));
           }
           tile_step(edge, T, t0, []() __attribute__((always_inline)) {}, ksc, vsc);
         }
       };
       // Tiles wholly inside the partition and every query's window first (no
       // selects), then the rest: two loops, so full tiles carry no selection
-      // and each loop keeps its own register allocation.
+      // and each loop keeps its own register allocation. A loop that may
+      // start in the middle of a round of stages first runs the steps up to
+      // the round's end; each pass of the loop then runs one step per stage
+      // in stage order. (The steps of different stages stay apart in the
+      // code: were they merged, the merged reads would address either stage
+      // and wait for every copy in flight.)
       int i = 0;
-      for (; i < nfull_all; ++i) step(std::false_type{}, i);
-      for (; i < ntiles; ++i) step(std::true_type{}, i);
+      auto run = [&](auto edge, auto aligned, const int end) __attribute__((always_inline)) {
+        if constexpr (!decltype(aligned)::value) {
+          static_for<STAGES - 1>([&](auto S) __attribute__((always_inline)) {
+            constexpr int kS = decltype(S)::value + 1;
+            if (i < end && i % STAGES == kS) {
+              step(edge, std::integral_constant<int, kS>{}, i);
+              ++i;
+            }
+          });
+        }
+        while (i < end) {
+          static_for<STAGES>([&](auto S) __attribute__((always_inline)) {
+            if (i < end) {
+              step(edge, S, i);
+              ++i;
+            }
+          });
+        }
+      };
+      run(std::false_type{}, std::true_type{}, nfull_all);
+      run(std::true_type{}, std::false_type{}, ntiles);
     }
   } else if constexpr (kLdsK) {
     // Staged K. A K tile is 4 block tiles of 128 rows x 16 tokens; it lands in
@@ -1309,15 +1369,15 @@ void launch_scaled(const Args& a, int group, dim3 grid, bool queue, hipStream_t 
   else launch_one<KDT, NCG, NW, ST, false, STG>(a, group, grid, queue, stream, tm);
 }
 
-// LDS stages of the tile-sharing kernels. Four column groups per wave: one
-// wave per SIMD, a CU holds four waves; four stages, except for bf16 with two
-// waves, where two stages of 33 KiB let two workgroups share a CU's LDS. Two
-// groups per wave: two waves per SIMD, eight per CU; a workgroup of fewer than
-// eight waves shares the CU, so bf16 takes two stages there.
+// LDS stages of the tile-sharing kernels: two of 33 KiB. The copies of the
+// next tile land in one stage while the compute reads the other (the compiler
+// tells them apart and does not hold the reads for those copies), and the
+// barrier before each tile both covers its copies and frees the other stage.
+// More stages were measured slower: their LDS takes occupancy and the
+// prefetch depth does not pay for it once the copies overlap the compute.
 template <int KDT, int NW>
 constexpr int share_stages() {
-  if constexpr (kShareGroups == 2) return (KDT == kBF16 && NW < 8) ? 2 : 4;
-  else return (KDT == kBF16 && NW == 2) ? 2 : 4;
+  return 2;
 }
 
 template <int KDT>

@@ -30,24 +30,12 @@
 // This kernel covers every supported shape and dtype; the matrix-core kernel
 // replaces it for the grouped bf16 / fp8 shapes.
 
-#include <utility>
 
 #include "pa_device.h"
 #include "pa_internal.h"
 
 namespace pa {
 namespace {
-
-// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>): slot
-// numbers known at compile time, so the register ring is never indexed at run time.
-template <int N, typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
-}
 
 // A V row of 16 tokens is sizeof(element) x 16 bytes: that many 16-byte
 // pieces, loaded raw and widened at use.
