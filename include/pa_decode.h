@@ -173,7 +173,9 @@ typedef struct pa_dims {
                                   q_len > 64:
                                   2, 4 or 8 waves take 32 (query position, head)
                                   pairs each and share every K/V tile through LDS
-                                  (default: 4 for up to 128 pairs, else 8); 1 gives
+                                  (default: 2 for up to 64 pairs, else 4; 8 with a
+                                  bf16 cache past 4096 tokens and more than 128
+                                  pairs); 1 gives
                                   one block of 64 pairs per item, each block reading
                                   the tiles itself.                                  */
   const float* k_block_scales; /* device, [num_blocks][num_kv_heads] float32: the K

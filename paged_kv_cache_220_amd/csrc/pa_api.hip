@@ -100,7 +100,7 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
   int share_nw = 0;   // waves per item when they share tiles
   if (mfma && blocks64 > 1 && d->waves_per_item != 1) {
     share_nw = d->waves_per_item > 0 ? d->waves_per_item
-                                        : pa::mfma_share_default_waves(p->group, p->q_len, p->max_len);
+                                        : pa::mfma_share_default_waves(p->group, p->q_len, p->max_len, d->kv_dtype);
     if (!pa::mfma_share_tiles(p->group, p->q_len, share_nw) || share_nw > pa::kShareMaxWaves)
       return PA_ERR_UNSUPPORTED;
   }

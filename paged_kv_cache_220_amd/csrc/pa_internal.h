@@ -64,7 +64,7 @@ bool mfma_share_tiles(int group, int q_len, int nw);
 // Work items per (sequence, KV head) of the matrix-core kernel (Args::q_blocks).
 int mfma_item_blocks(int group, int q_len, int nw);
 // Waves per item the planner takes for tile sharing.
-int mfma_share_default_waves(int group, int q_len, long long max_len);
+int mfma_share_default_waves(int group, int q_len, long long max_len, int kv_dtype);
 
 constexpr int kBlockSize = 16;     // tokens per physical block handled by the kernels
 constexpr int kTileTokens = 64;    // partition lengths are multiples of this

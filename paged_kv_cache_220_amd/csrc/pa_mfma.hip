@@ -1317,15 +1317,18 @@ int mfma_item_blocks(int group, int q_len, int nw) {
 }
 
 // Default waves per item when they share tiles: 2 for up to 64 pairs of a KV
-// head, else 4 (two workgroups of two LDS stages per CU), except past 4096
-// tokens, where 8 (one workgroup of four stages per CU: half the items, so
-// half the K/V re-reads) came out about 1 % ahead (32 positions over 32K
-// tokens; 64 positions even). On shorter sequences 8 waves measured 2-14 %
-// slower: a few tiles per item never fill the deeper pipeline.
-int mfma_share_default_waves(int group, int q_len, long long max_len) {
+// head, else 4 (two workgroups per CU), except with a bf16 cache past 4096
+// tokens, where 8 (one workgroup per CU: half the items, so half the K/V
+// re-reads) measured 5 % ahead at 32 positions over 32K tokens and 1.5 % at
+// 64. On shorter sequences 8 waves measured 2-14 % slower (a few tiles per
+// item never fill the pipeline), and with fp8 and int4 caches, whose tiles
+// are half or a quarter the bytes, 4 waves tied or won (long-context batch,
+// 32 positions: e5m2 even, e4m3 and int4 1.5 % ahead; shared-prefix batch, 32
+// and 64 positions: 5.5 % ahead).
+int mfma_share_default_waves(int group, int q_len, long long max_len, int kv_dtype) {
   const int blocks = (group * q_len + 16 * kShareGroups - 1) / (16 * kShareGroups);
   if (blocks <= 2) return 2;
-  return blocks > 4 && max_len > 4096 && kShareMaxWaves == 8 ? 8 : 4;
+  return blocks > 4 && max_len > 4096 && kv_dtype == kBF16 && kShareMaxWaves == 8 ? 8 : 4;
 }
 
 // Waves per item: 1 to 4 with one column group; 1 or 2 with two or four

@@ -169,6 +169,10 @@ def test_plan_schedule_choice():
     # 32 positions over long sequences (256 pairs, past 4096 tokens): one item of 8 waves
     pl = B.plan(dims(num_seqs=16, max_seq_len=32768, q_len=32), 8)
     assert pl["waves_per_item"] == 8 and pl["grid_workgroups"] == 16 * 8 * 1 * pl["max_partitions"]
+    # the same with an fp8 or int4 cache: two items of 4 waves (half or a quarter the tile bytes)
+    for kvd in (B.PA_DTYPE_FP8_E5M2, B.PA_DTYPE_FP8_E4M3):
+        pf8 = B.plan(dims(num_seqs=16, max_seq_len=32768, q_len=32, kv_dtype=kvd), 8)
+        assert pf8["waves_per_item"] == 4 and pf8["grid_workgroups"] == 16 * 8 * 2 * pf8["max_partitions"]
     # prefill chunk: 8 heads x 64 positions = 16 wave blocks -> 4 items of 4 waves per KV head
     pp = B.plan(dims(num_seqs=128, max_seq_len=512, max_blocks_per_seq=32, q_len=64), 8)
     assert pp["waves_per_item"] == 4 and pp["grid_workgroups"] == 128 * 8 * 4 and pp["max_partitions"] == 1
