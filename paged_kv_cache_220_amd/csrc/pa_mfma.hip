@@ -1030,6 +1030,11 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
       run(std::false_type{}, std::true_type{}, nfull_all);
       run(std::true_type{}, std::false_type{}, ntiles);
     }
+    // every wave is past its last stage read: the stages take the outputs of
+    // single-partition bf16 items below
+    if constexpr (M::kBits == 16) {
+      if (nparts == 1) __builtin_amdgcn_s_barrier();
+    }
   } else if constexpr (kLdsK) {
     // Staged K. A K tile is 4 block tiles of 128 rows x 16 tokens; it lands in
     // this wave's LDS slot through direct global-to-LDS loads of whole rows
@@ -1246,6 +1251,27 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   for (int cg = 0; cg < NCG; ++cg) {
     const int v = v0 + 16 * cg + n;
     if (v >= GV) continue;
+    if constexpr (kShare && NCG == 2 && M::kBits == 16) {
+      if (nparts == 1) {
+        // bf16 tile sharing, one partition: the outputs go out through this
+        // wave's 8 KiB of a stage (rows of 256 B per pair; 16-byte chunk k of
+        // pair p at chunk k ^ (p & 15), so the 16 pairs of a write hit distinct
+        // banks), and each lane then stores 16 contiguous bytes, each
+        // instruction four whole rows, instead of 8 bytes of 16 rows
+        uint8_t* ob = (wave < 4 ? kv_lds0 : kv_lds1) + (wave & 3) * 8192;
+        const int p = 16 * cg + n;
+        const float inv = l_tot[cg] > 0.f ? a.v_scale / l_tot[cg] : 0.f;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          u32x2 w;
+          w[0] = uint32_t(f32_to_bf16_bits(oacc[cg][dt][0] * inv)) | (uint32_t(f32_to_bf16_bits(oacc[cg][dt][1] * inv)) << 16);
+          w[1] = uint32_t(f32_to_bf16_bits(oacc[cg][dt][2] * inv)) | (uint32_t(f32_to_bf16_bits(oacc[cg][dt][3] * inv)) << 16);
+          const int k = 2 * dt + (c >> 1);
+          *reinterpret_cast<u32x2*>(ob + p * 256 + ((k ^ (p & 15)) << 4) + ((c & 1) << 3)) = w;
+        }
+        continue;
+      }
+    }
     if (nparts == 1) {
       const int qi = v / group;
       const int h = v - qi * group;
@@ -1266,6 +1292,25 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
       if (c == 0) {
         a.part_m[slot * GV + v] = m_run[cg];
         a.part_l[slot * GV + v] = l_tot[cg];
+      }
+    }
+  }
+  if constexpr (kShare && NCG == 2 && M::kBits == 16) {
+    static_assert(4 * 8192 <= kStageBytes, "four waves' outputs fit a stage");
+    if (nparts == 1) {
+      const uint8_t* ob = (wave < 4 ? kv_lds0 : kv_lds1) + (wave & 3) * 8192;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const int p = 4 * kk + (lane >> 4), j = lane & 15;
+        const uint4 x = *reinterpret_cast<const uint4*>(ob + p * 256 + ((j ^ (p & 15)) << 4));
+        const int v = v0 + p;
+        if (v < GV) {
+          const int qi = v / group;
+          const int h = v - qi * group;
+          uint16_t* out = static_cast<uint16_t*>(a.out) +
+                          (((int64_t)s * QL + qi) * a.num_heads + (int64_t)kvh * group + h) * kD;
+          *reinterpret_cast<uint4*>(out + 8 * j) = x;
+        }
       }
     }
   }
