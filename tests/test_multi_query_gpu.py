@@ -191,6 +191,7 @@ SHARE = [
     # kv dtype, per-block scales, query positions: 8 heads x q_len pairs in blocks of 64
     ("bf16", False, 16),    # two blocks: by default one item of two waves
     ("bf16", False, 24),    # three blocks: four waves, one idle; or two items of two waves
+    ("bf16", False, 13),    # 104 pairs: the last wave's 32 pairs are 8 real ones and 24 past the end
     ("e5m2", False, 16),
     ("e4m3", True, 20),
     ("int4", True, 24),
