@@ -19,8 +19,8 @@
 // group c takes rows 32*kstep + 4*i + c. For bf16 those are 64-bit loads
 // straight from HBM, and every load instruction covers whole 128-byte lines.
 // For fp8 the 4-token pieces are only 4 bytes, so the K tile is first copied
-// into LDS as whole rows by direct global-to-LDS loads, and the pieces are
-// read from there.
+// into LDS as whole rows by buffer-to-LDS copies, and the pieces are read
+// from there.
 //
 // A tile is 64 tokens = 4 physical blocks. MFMA row (quartet) q = 4c + r of
 // the QK step holds block (c >> 1) + 2 * (r >> 1), tokens 8 * (c & 1) +
@@ -875,7 +875,6 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   // the constant address space, so they become scalar loads even where the
   // compiler cannot tell that the loop's LDS copies leave that memory alone.
   typedef __attribute__((address_space(3))) void* lds_ptr_t;
-  typedef __attribute__((address_space(1))) void* gbl_ptr_t;
   typedef const __attribute__((address_space(4))) int32_t* cint_ptr_t;
   typedef const __attribute__((address_space(4))) float* cflt_ptr_t;
   const cint_ptr_t ctable = (cint_ptr_t)table;
@@ -1037,7 +1036,7 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     }
   } else if constexpr (kLdsK) {
     // Staged K. A K tile is 4 block tiles of 128 rows x 16 tokens; it lands in
-    // this wave's LDS slot through direct global-to-LDS loads of whole rows
+    // this wave's LDS slot through buffer-to-LDS copies of whole rows
     // (16 bytes per lane, each instruction reading 1 KiB contiguous), and QK
     // reads each lane's 4-token pieces back from LDS. (For fp8, loading those
     // 4-byte pieces straight from HBM touches half of every 128-byte line per
@@ -1056,8 +1055,9 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
     // the tile, size = its bytes), not global ones: the compiler counts those
     // in issue order with the V loads and waits for V before PV with the K
     // copies of the next tile still in flight, while a global-to-LDS load in
-    // flight makes it wait for every outstanding load. It does not order LDS
-    // reads after these copies by itself, hence the explicit wait.
+    // flight makes it wait for every outstanding load. The explicit wait
+    // before the K reads does not depend on the compiler tracing those reads
+    // to the slot array (its own waits after such copies do).
     uint8_t* kslot = &k_lds[wave][0];
     const uint8_t* krow = kslot + kblk * kSlotBlk + c * kRowBytes + ktok * M::kBits / 8;   // + row bytes * (32 ks + 4 i)
     // With copy false the resources hold no bytes: the loads touch no memory
