@@ -107,18 +107,19 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
   p->q_blocks = mfma ? pa::mfma_item_blocks(p->group, p->q_len, share_nw > 0 ? share_nw : 1) : 1;
   // Every wave keeps about one 64-token tile of K and V in flight. Covering
   // HBM latency at full bandwidth takes about as many waves as the chip holds
-  // at once: 2048 with bf16 / fp32 tiles (32 KiB, two waves per SIMD) and 3072
-  // with fp8 and int4 tiles (16 / 8 KiB; those kernels stage K in LDS and run
-  // three waves per SIMD, fp8 with per-block scales two). Partitions are
+  // at once: 2048 (two waves per SIMD), and 3072 with int4 tiles (8 KiB; that
+  // kernel stages K in LDS and runs three waves per SIMD). The fp8 kernel can
+  // hold three as well, but with its K copies and V loads overlapping the
+  // compute two waves per SIMD measured 1-2 % faster (fp8 batches of 32K and
+  // of shared-prefix sequences). Partitions are
   // made as long as possible (up to 4096 tokens, 8192 with tile sharing:
   // start-up and merge traffic are amortised) and the waves come from
   // splitting each item over 1 to 4 waves; partitions are shortened only when
   // even 4 waves per item would not reach the target.
   const long long units = (long long)d->num_seqs * hkv * (p->kernel == PA_KERNEL_MFMA ? p->q_blocks : 1);
-  // three waves per SIMD: fp8 without per-block scales and int4 (with them).
-  // The tile-sharing kernels run two waves per SIMD (2048 on the chip).
-  const bool fp8 = d->kv_dtype == PA_DTYPE_FP8_E5M2 || d->kv_dtype == PA_DTYPE_FP8_E4M3;
-  const bool three_waves = (fp8 && d->k_block_scales == nullptr) || d->kv_dtype == PA_DTYPE_INT4;
+  // three waves per SIMD: int4. The tile-sharing kernels run two waves per
+  // SIMD (2048 on the chip).
+  const bool three_waves = d->kv_dtype == PA_DTYPE_INT4;
   const long long target_waves = share_nw > 0 ? 2048 : three_waves ? 3072 : 2048;
   const int max_item_waves = share_nw > 0 ? share_nw : 4;
   auto items_for = [&](long long P) { return units * ((p->max_len + P - 1) / P); };
@@ -175,8 +176,8 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
   } else {
     const long long tiles = (std::min<long long>(P, p->max_len) + pa::kTileTokens - 1) / pa::kTileTokens;
     // the most waves (1 to 4) for which the grid fits the target and every
-    // wave keeps at least 4 tiles: 3 fills the three waves per SIMD of the fp8
-    // and int4 kernels when the grid is a third of them
+    // wave keeps at least 4 tiles: 3 fills the three waves per SIMD of the
+    // int4 kernel when the grid is a third of them
     int nw = 1;
     for (int w = 2; w <= 4; ++w)
       if (p->grid * w <= target_waves && tiles >= 4LL * w && pa::mfma_waves_supported(p->group, p->q_len, w)) nw = w;

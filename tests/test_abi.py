@@ -134,9 +134,12 @@ def test_plan_long_context():
     items = 16 * 8 * 8 * 8
     assert p["workspace_bytes"] >= items * (128 + 2) * 4
     assert p["waves_per_item"] == 2                                      # 1024 items x 2 = 2048 waves
-    # fp8 runs 3 waves per SIMD (3072 resident): 1024 items x 3 waves fill them; 4 would not fit at once
+    # fp8: 1024 items x 2 waves, as bf16; int4 runs 3 waves per SIMD (3072 resident): 1024 items x 3
     pf = B.plan(dims(num_seqs=128, max_blocks_per_seq=256, kv_dtype=B.PA_DTYPE_FP8_E5M2), 8)
-    assert pf["partition_tokens"] == 4096 and pf["grid_workgroups"] == 8 * 128 and pf["waves_per_item"] == 3
+    assert pf["partition_tokens"] == 4096 and pf["grid_workgroups"] == 8 * 128 and pf["waves_per_item"] == 2
+    pi = B.plan(dims(num_seqs=128, max_blocks_per_seq=256, kv_dtype=B.PA_DTYPE_INT4, k_block_scales=4096,
+                     v_block_scales=8192), 8)
+    assert pi["partition_tokens"] == 4096 and pi["grid_workgroups"] == 8 * 128 and pi["waves_per_item"] == 3
     # one sequence: partitions shrink until 4 waves per item would reach 2048 waves
     p1 = B.plan(dims(num_seqs=1), 8)
     assert p1["partition_tokens"] == 512 and p1["grid_workgroups"] == 512 and p1["waves_per_item"] == 2
