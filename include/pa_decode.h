@@ -70,14 +70,14 @@
  *     the softmax weights fed to the matrix cores (kept in [0, 2)), and a power
  *     of two, added to the score in the log2 domain, so the running maximum
  *     follows weight x scale and no fed weight overflows or loses precision.
- * Softmax weights in the P.V product. Decode (q_len = 1) with a bf16 or int4
- * cache feeds each weight as a rounded 16-bit value plus its rounding
- * residual: about 16 significant bits with bf16 operands, 22 with binary16
- * ones. Calls with more than 16 (query position, head) pairs per KV head
- * (several query positions per sequence) and decode with an fp8 cache feed the
- * rounded value alone: 8 significant bits (bf16 cache) or 11 (fp8, int4), which
- * moves an output by at most 2^-9 (2^-12) of sum_i p_i |v_i|, well inside the stated
- * bars (2e-2 for bf16 I/O, 5e-2 for fp8 KV).
+ * Softmax weights in the P.V product. Decode (q_len = 1) with a bf16 cache
+ * feeds each weight as a rounded bf16 value plus its rounding residual (about
+ * 16 significant bits). Calls with more than 16 (query position, head) pairs
+ * per KV head (several query positions per sequence) and decode with an fp8
+ * or int4 cache feed the rounded value alone: 8 significant bits (bf16 cache)
+ * or 11 (binary16: fp8, int4), which moves an output by at most 2^-9 (2^-12)
+ * of sum_i p_i |v_i|, well inside the stated bars (2e-2 for bf16 I/O, 5e-2
+ * for fp8 KV).
  */
 #ifndef PA_DECODE_H
 #define PA_DECODE_H

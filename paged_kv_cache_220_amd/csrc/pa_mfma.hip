@@ -368,13 +368,14 @@ __device__ __forceinline__ void partition_item(const Args& a, int group, int s, 
   constexpr bool kLdsK = !kShare && (M::kBits < 16 || NCG == 2);
   constexpr bool kPlain = !kShare && !kLdsK;
   // P enters PV as hi + lo (about 16 significant bits per weight) in bf16
-  // and int4 decode (one column group). With several query positions, where
-  // the matrix cores and the vector ALU bound the kernel, and in fp8 decode,
-  // where the shorter tile step lets the next V loads go out sooner, it
-  // enters as hi alone (bf16: 8 bits, binary16: 11), which halves the PV
-  // products. The error of an output is then at most 2^-9 (2^-12) of
-  // sum_i p_i |v_i|, the attention over |V|.
-  constexpr bool kTwoPartP = NCG == 1 && M::kBits != 8;
+  // decode (one column group). With several query positions, where the
+  // matrix cores and the vector ALU bound the kernel, and in fp8 and int4
+  // decode, where the shorter tile step lets the next loads go out sooner
+  // (int4: its tile step is compute-bound), it enters as hi alone (bf16: 8
+  // bits, binary16: 11), which halves the PV products. The error of an
+  // output is then at most 2^-9 (2^-12) of sum_i p_i |v_i|, the attention
+  // over |V|.
+  constexpr bool kTwoPartP = NCG == 1 && M::kBits == 16;
   // bf16 tile sharing reads its K operands from LDS with gfx950's
   // transposing read (ds_read_b64_tr_b16), which hands each lane one token's
   // values of four rows, so no register transpose follows. The read fixes

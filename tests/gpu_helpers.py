@@ -105,16 +105,16 @@ def check(got, ref, w, label="", a=None):
     catches kernels that drop blocks or mis-scale long sequences, whose
     outputs are small enough to slip under the absolute bar.
 
-    With several query positions, and in decode with an fp8 cache, the
-    kernels feed each weight to PV as one 16-bit value (8 significant bits
+    With several query positions, and in decode with an fp8 or int4 cache,
+    the kernels feed each weight to PV as one 16-bit value (8 significant bits
     with a bf16 cache, 11 with fp8 and int4): pass `a`, the attention over |V|
     (`abs_attention_multi`), and the gate becomes 2^-7 |ref| + k a + 1e-4 with
     k = 2^-8 (bf16 cache) or 2^-10 (the others), twice and four times the
-    rounding bounds 2^-9 a and 2^-12 a. For fp8 decode outputs (one query row
-    per sequence) `a` is taken from w.q when not given.
+    rounding bounds 2^-9 a and 2^-12 a. For fp8 and int4 decode outputs (one
+    query row per sequence) `a` is taken from w.q when not given.
     """
     assert got.shape == ref.shape
-    if a is None and w.kv_dtype in ("e5m2", "e4m3") and got.ndim == 3 and w.q.shape == got.shape:
+    if a is None and w.kv_dtype in ("e5m2", "e4m3", "int4") and got.ndim == 3 and w.q.shape == got.shape:
         a = abs_attention_multi(w.q[:, None], w, q_dtype=w.q_dtype)[:, 0]
     assert not np.isnan(got).any(), f"{label}: NaN in output"
     err = np.abs(got - ref)

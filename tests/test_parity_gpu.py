@@ -358,21 +358,26 @@ def test_int4_full_size():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("kv_dtype", ["e5m2", "e4m3"])
-def test_fp8_every_block_counted_once(kv_dtype):
-    """fp8 decode feeds each weight to PV as one binary16 value, so its outputs
-    are held to 2^-7 |ref| + 2^-10 a + 1e-4 (a: the attention over |V|); on
-    sequences of several thousand tokens that lets one ordinary skipped block
-    pass. Here one block per sequence holds V = 32 under near-uniform weights
-    (q x 2^-20): the first block, one mid-partition, the first of the second
-    4096-token partition, and the last, partly filled one. Skipping or
-    repeating it moves the output by about 32 x its tokens / L, several times
-    the gate."""
+@pytest.mark.parametrize("kv_dtype", ["e5m2", "e4m3", "int4"])
+def test_one_part_decode_every_block_counted_once(kv_dtype):
+    """fp8 and int4 decode feed each weight to PV as one binary16 value, so
+    their outputs are held to 2^-7 |ref| + 2^-10 a + 1e-4 (a: the attention
+    over |V|); on sequences of several thousand tokens that lets one ordinary
+    skipped block pass. Here one block per sequence holds V = 32 under
+    near-uniform weights (q x 2^-20): the first block, one mid-partition, the
+    first of the second 4096-token partition, and the last, partly filled one
+    (int4: codes 4 at block scale 8). Skipping or repeating it moves the output
+    by about 32 x its tokens / L, several times the gate."""
     lens = [9000, 8200, 6000, 4101]
     w = W.random_edge_workload(97, S=len(lens), H=64, Hkv=8, D=128, seq_lens=lens, kv_dtype=kv_dtype)
     heavy = [0, 100, 256, (lens[3] - 1) // 16]
     for s, b in enumerate(heavy):
-        w.v_cache[int(w.block_tables[s, b])] = W.to_storage(np.full(w.v_cache.shape[1:], 32.0, np.float32), kv_dtype)
+        blk = int(w.block_tables[s, b])
+        if kv_dtype == "int4":
+            w.v_cache[blk] = O.int4_pack(np.full(w.v_cache.shape[1:3] + (16,), 4, np.int8))
+            w.v_block_scales[blk] = 8.0
+        else:
+            w.v_cache[blk] = W.to_storage(np.full(w.v_cache.shape[1:], 32.0, np.float32), kv_dtype)
     qf = (w.q.astype(np.uint32) << 16).view(np.float32) * np.float32(2.0 ** -20)
     w.q = W.to_storage(qf, "bf16")
     ref = oracle_full(w)
@@ -383,6 +388,6 @@ def test_fp8_every_block_counted_once(kv_dtype):
         assert gate[s].max() < 0.25 * 32.0 * ntok[s] / lens[s], f"sequence {s}: gate too loose"
     dev = upload(w)
     for ptok, nw, sched in ((0, 0, "auto"), (4096, 0, "grid"), (512, 2, "grid"), (1024, 3, "queue")):
-        log(f"case fp8 heavy block {kv_dtype} P={ptok} waves={nw} {sched}")
+        log(f"case one-part heavy block {kv_dtype} P={ptok} waves={nw} {sched}")
         got = run_gpu(w, dev, kernel="mfma", partition_tokens=ptok, waves_per_item=nw, schedule=sched)
-        check(got, ref, w, f"fp8 heavy block {kv_dtype} P={ptok} waves={nw} {sched}", a=a)
+        check(got, ref, w, f"one-part heavy block {kv_dtype} P={ptok} waves={nw} {sched}", a=a)

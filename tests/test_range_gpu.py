@@ -15,10 +15,9 @@ scaled values the error scales with them, so each output row is held to
   |err| <= 2^-7 |ref| + 1e-4 * u   and   |err| <= 1e-2 * u,
 where u is the largest |scaled V value| among the tokens the row attends (the
 output is a convex combination of those rows). For N(0,1) data u is about
-4.5, so the second bar is the task's 5e-2. With several query positions, and
-in decode with an fp8 cache, the kernels feed each weight to PV as one
-binary16 value (11 significant bits), which may move an output by up to
-2^-12 u; those rows take 2^-10 u in place of 1e-4 u.
+4.5, so the second bar is the task's 5e-2. With these caches the kernels
+feed each weight to PV as one binary16 value (11 significant bits), which may
+move an output by up to 2^-12 u; the rows take 2^-10 u in place of 1e-4 u.
 """
 
 import numpy as np
@@ -109,7 +108,7 @@ def test_decode_operand_range(kv, qpow, scales):
         log(f"case range {kv} q*2^{qpow} scales={scales} P={ptok} waves={nw} {sched}")
         got = run_gpu(w, dev, kernel="mfma", partition_tokens=ptok, waves_per_item=nw, schedule=sched)
         check_scaled(got, ref, u, f"{kv} q*2^{qpow} {scales} P={ptok} waves={nw} {sched}",
-                     u_coef=2.0 ** -10 if kv in ("e5m2", "e4m3") else 1e-4)
+                     u_coef=2.0 ** -10)
 
 
 MQ = [(kv, ql, qp, sk) for kv in ("e5m2", "int4") for ql in (4, 8, 16)
