@@ -177,10 +177,16 @@ int make_plan(const pa_dims_t* d, int32_t hkv, Plan* p) {
     const long long tiles = (std::min<long long>(P, p->max_len) + pa::kTileTokens - 1) / pa::kTileTokens;
     // the most waves (1 to 4) for which the grid fits the target and every
     // wave keeps at least 4 tiles: 3 fills the three waves per SIMD of the
-    // int4 kernel when the grid is a third of them
+    // int4 kernel when the grid is a third of them. With fp8 and whole
+    // sequences as items (one partition) a wave keeps at least 8: on the chat
+    // batch (at most 8 tiles) one wave per item ran 6-7 % faster than two,
+    // where bf16 ties and int4 prefers two.
+    const bool fp8 = d->kv_dtype == PA_DTYPE_FP8_E5M2 || d->kv_dtype == PA_DTYPE_FP8_E4M3;
+    const long long min_tiles = fp8 && p->max_parts == 1 ? 8 : 4;
     int nw = 1;
     for (int w = 2; w <= 4; ++w)
-      if (p->grid * w <= target_waves && tiles >= 4LL * w && pa::mfma_waves_supported(p->group, p->q_len, w)) nw = w;
+      if (p->grid * w <= target_waves && tiles >= min_tiles * w && pa::mfma_waves_supported(p->group, p->q_len, w))
+        nw = w;
     p->waves_per_item = nw;
   }
   size_t off = 0;

@@ -147,6 +147,9 @@ def test_plan_long_context():
     pc = B.plan(dims(num_seqs=128, max_blocks_per_seq=32, max_seq_len=507), 8)
     assert pc["partition_tokens"] == 512 and pc["max_partitions"] == 1 and pc["workspace_bytes"] == 0
     assert pc["waves_per_item"] == 2                                     # 8 tiles: 4 per wave
+    # the same with an fp8 cache: whole-sequence items keep 8 tiles per wave, so one wave
+    pc8 = B.plan(dims(num_seqs=128, max_blocks_per_seq=32, max_seq_len=507, kv_dtype=B.PA_DTYPE_FP8_E4M3), 8)
+    assert pc8["partition_tokens"] == 512 and pc8["max_partitions"] == 1 and pc8["waves_per_item"] == 1
     p2 = B.plan(dims(partition_tokens=1024, max_seq_len=4096), 8)
     assert p2["max_partitions"] == 4 and p2["partition_tokens"] == 1024
 
