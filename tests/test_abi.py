@@ -150,6 +150,13 @@ def test_plan_long_context():
     # the same with an fp8 cache: whole-sequence items keep 8 tiles per wave, so one wave
     pc8 = B.plan(dims(num_seqs=128, max_blocks_per_seq=32, max_seq_len=507, kv_dtype=B.PA_DTYPE_FP8_E4M3), 8)
     assert pc8["partition_tokens"] == 512 and pc8["max_partitions"] == 1 and pc8["waves_per_item"] == 1
+    # ... but one long fp8 sequence, cut into 8-tile partitions by the wave target, keeps two waves per item
+    p18 = B.plan(dims(num_seqs=1, kv_dtype=B.PA_DTYPE_FP8_E5M2), 8)
+    assert p18["partition_tokens"] == 512 and p18["max_partitions"] == 64 and p18["waves_per_item"] == 2
+    # and int4 on the chat batch keeps two (it preferred them)
+    pc4 = B.plan(dims(num_seqs=128, max_blocks_per_seq=32, max_seq_len=507, kv_dtype=B.PA_DTYPE_INT4,
+                      k_block_scales=4096, v_block_scales=8192), 8)
+    assert pc4["max_partitions"] == 1 and pc4["waves_per_item"] == 2
     p2 = B.plan(dims(partition_tokens=1024, max_seq_len=4096), 8)
     assert p2["max_partitions"] == 4 and p2["partition_tokens"] == 1024
 
